@@ -1,0 +1,259 @@
+/*
+ * spec_verify.h -- C ABI of the speculative-decoding verify step on one
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The verify step of speculative decoding runs the target model once over a
+ * flattened draft tree and keeps the longest draft path the target accepts:
+ *
+ *   spec_tree_build_mask   parents -> packed ancestor masks, depth, positions
+ *   spec_kv_append         tree rows' K/V -> cache slots [L_b, L_b + N_b)
+ *   spec_tree_attn_verify  tree attention: prefix + ancestors only
+ *   spec_accept_sample     lossless acceptance walk + final token
+ *   spec_kv_commit         compact the accepted path's K/V, roll back the rest
+ *
+ * Pages this interface restates (title, section):
+ *   [TREE]  "投机推理算法的常见优化手段" (cnblogs) -- generating and verifying
+ *           the draft tree: flattening, the tree mask (printed 6x6 matrix),
+ *           the forward call with tree mask, position ids and KV cache, and
+ *           verifying every token of every level.
+ *   [MATH]  "【模型后训练与深度推理】9 推理加速：推测解码与级联推理" (CSDN),
+ *           sections 7.1-7.2: accept with probability min(1, p/q), resample
+ *           from norm(max(0, p - q)), emitted length counts the final token.
+ *   [SD]    guijiagi.com speculative-decoding post: rejection-sampling rule
+ *           (stop at the first rejection), batching with divergent progress,
+ *           KV rollback by freeing paged blocks, variable-length candidates.
+ *   [SURV]  "万字综述 10+ 种 LLM 投机采样推理加速方案", sections 5.2 (tree
+ *           based parallel decoding), 6.2 (Cartesian trees), 4.3/8.1
+ *           (temperature 0 = argmax; keep the longest matching prefix).
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - Batch of B requests; request b owns tree rows [row_offsets[b],
+ *    row_offsets[b+1]) of every per-row array (N_b = that count, root first,
+ *    1 <= N_b <= max_rows <= SPEC_MAX_TREE_ROWS).  Rows are flattened in any
+ *    topological order: local row 0 is the root and parent[i] < i.
+ *  - L_b = prefix_len[b] tokens of KV are already cached for request b.
+ *  - All pointers named *_d are device memory, *_h host memory.  The caller
+ *    owns every buffer; the library never allocates or frees, and keeps no
+ *    pointer after a call returns.  Scratch comes from caller workspaces
+ *    sized by the *_workspace_bytes queries.
+ *  - Every call validates its arguments on the host first.  Invalid
+ *    arguments return a status != SPEC_OK and launch nothing; the detail is
+ *    in spec_last_error() (thread-local).  Valid calls enqueue kernels on
+ *    `stream` and return SPEC_OK without waiting.  Errors found on the device
+ *    (a bad parent array held in device memory) are reported through the
+ *    documented output fields, never by a fault.
+ *  - The library is thread-safe and holds no mutable global state apart from
+ *    the thread-local error string.
+ */
+#ifndef SPEC_VERIFY_H
+#define SPEC_VERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SPEC_ABI_VERSION 1
+#define SPEC_MAX_TREE_ROWS 256   /* rows per request incl. the root: <= 4 mask words */
+#define SPEC_KV_BLOCK 16         /* paged KV block size (tokens) */
+
+typedef enum {
+  SPEC_OK = 0,
+  SPEC_ERR_NULL = 1,         /* a required pointer is NULL */
+  SPEC_ERR_SHAPE = 2,        /* sizes, strides or alignment out of range */
+  SPEC_ERR_TREE = 3,         /* host-visible tree metadata inconsistent */
+  SPEC_ERR_CAPACITY = 4,     /* cache or output too small for the rows */
+  SPEC_ERR_DTYPE = 5,        /* unsupported element type combination */
+  SPEC_ERR_HIP = 6,          /* a HIP launch failed */
+  SPEC_ERR_UNSUPPORTED = 7,  /* valid request this build does not handle */
+  SPEC_ERR_WORKSPACE = 8     /* workspace NULL or smaller than required */
+} spec_status;
+
+typedef enum { SPEC_BF16 = 0, SPEC_F32 = 1 } spec_dtype;
+typedef enum { SPEC_KV_CONTIGUOUS = 0, SPEC_KV_PAGED = 1 } spec_kv_layout;
+
+/* Ragged batch metadata.  Both copies must hold the same values: the host
+ * copy sizes grids and is validated, the device copy is read by kernels. */
+typedef struct {
+  int32_t batch;                  /* B >= 1 */
+  int32_t max_rows;               /* >= every N_b, <= SPEC_MAX_TREE_ROWS;
+                                     mask words per row W = ceil(max_rows/64) */
+  const int32_t *row_offsets_h;   /* [B+1], row_offsets[0] = 0, strictly increasing */
+  const int32_t *row_offsets_d;
+  const int32_t *prefix_len_h;    /* [B], L_b >= 0 */
+  const int32_t *prefix_len_d;
+} spec_batch;
+
+/* KV cache of one attention layer (caller-owned).
+ *  contiguous: k, v are [B][Hkv][capacity][D]; request b's token t of head h
+ *              at ((b*Hkv + h)*capacity + t)*D.
+ *  paged:      k, v are [num_blocks][Hkv][16][D]; token t of request b lives
+ *              in physical block block_table[b*max_blocks_per_seq + t/16],
+ *              slot t%16.  Block ids are trusted (device memory). */
+typedef struct {
+  spec_kv_layout layout;
+  spec_dtype dtype;               /* element type of k and v */
+  int32_t num_kv_heads;           /* Hkv >= 1 */
+  int32_t head_dim;               /* D: 64 or 128 */
+  void *k;
+  void *v;
+  int32_t capacity;               /* contiguous: token slots per (request, head) */
+  int32_t block_size;             /* paged: must be SPEC_KV_BLOCK */
+  const int32_t *block_table_d;   /* paged: [B][max_blocks_per_seq] */
+  int32_t max_blocks_per_seq;     /* paged */
+} spec_kv;
+
+/* ---------------------------------------------------------------------------
+ * spec_tree_build_mask -- [TREE] tree-mask section.
+ *
+ * For every row i of request b: mask word w, bit j (j = 64*w + bit) is 1 iff
+ * local row j is i itself or an ancestor of i (row = attending token, column
+ * = attended token, diagonal set, as in the printed matrix).  depth_d[i] =
+ * number of strict ancestors; position_d[i] = L_b + depth_i (the tree
+ * position id).  The parent array is checked on the device: parent[0] must
+ * be -1 and 0 <= parent[i] < i.  err_row_d[b] = -1 when request b is valid,
+ * else the smallest invalid local row; its mask rows are then all zero and
+ * its depth/position entries -1.
+ *
+ *   parents_d   int32 [R]   local parent index, -1 at each root
+ *   mask_d      uint64 [R][W], W = ceil(max_rows/64)           (output)
+ *   depth_d     int32 [R]   optional (NULL)                     (output)
+ *   position_d  int32 [R]   optional (NULL)                     (output)
+ *   err_row_d   int32 [B]                                       (output)
+ */
+spec_status spec_tree_build_mask(const spec_batch *batch, const int32_t *parents_d,
+                                 uint64_t *mask_d, int32_t *depth_d, int32_t *position_d,
+                                 int32_t *err_row_d, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * spec_kv_append -- [SURV] 5.2 / [TREE]: during verification the tree's K/V
+ * rows occupy cache slots L_b .. L_b + N_b - 1 (row i at slot L_b + i).
+ *
+ *   k_new_d, v_new_d   [R][Hkv][D] of kv->dtype
+ * Contiguous caches need capacity >= L_b + N_b; paged caches need
+ * max_blocks_per_seq >= ceil((L_b + N_b)/16) with those blocks mapped.
+ */
+spec_status spec_kv_append(const spec_batch *batch, const spec_kv *kv,
+                           const void *k_new_d, const void *v_new_d, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * spec_tree_attn_verify -- [TREE] forward with tree mask; [SURV] 5.2.
+ *
+ * out[i][h] = softmax_j(q[i][h] . k_j * softmax_scale) v_j over the keys row
+ * i may see: every cached prefix token t < L_b of its request, and tree rows
+ * j with mask bit (i, j) set (their K/V at slot L_b + j, see spec_kv_append).
+ * Query head h reads KV head h / (Hq / Hkv) (grouped-query attention).
+ *
+ *   q_d        [R][Hq][D], same dtype as the cache
+ *   mask_d     uint64 [R][W] from spec_tree_build_mask
+ *   out_d      [R][Hq][D] of out_dtype (bf16 or f32)
+ *   workspace  >= spec_tree_attn_workspace_bytes(batch, kv, Hq) bytes
+ *              (split-KV partial results; contents need no initialisation)
+ * bf16 caches run on the MFMA path (fp32 accumulation, fp32 online softmax);
+ * f32 caches run on a plain fp32 vector path.
+ */
+size_t spec_tree_attn_workspace_bytes(const spec_batch *batch, const spec_kv *kv,
+                                      int32_t num_q_heads);
+spec_status spec_tree_attn_verify(const spec_batch *batch, const spec_kv *kv,
+                                  const void *q_d, int32_t num_q_heads,
+                                  const uint64_t *mask_d, float softmax_scale,
+                                  void *out_d, spec_dtype out_dtype,
+                                  void *workspace_d, size_t workspace_bytes,
+                                  hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * spec_accept_sample -- [MATH] 7.1-7.2, [SD] rejection sampling, [TREE]
+ * level-by-level tree verification, [SURV] 4.3/8.1 greedy verification.
+ *
+ * Row u's target logits p_u give the distribution of u's children; row u's
+ * draft logits q_u the distribution u's children were drafted from (only
+ * rows that have children are read).  With T = temperature > 0,
+ * P_u = softmax(p_u/T), Q_u = softmax(q_u/T).  For each request, starting at
+ * the root: the children c of the current node u are tried in ascending row
+ * order; child c (token x = tokens[c], coin r) is accepted iff
+ * r * Q_u(x) < R(x), where R starts as P_u and after each rejected sibling
+ * becomes max(0, R - Q_u) / sum(max(0, R - Q_u)) (kept, with a flag, when
+ * that sum is 0).  An accepted child becomes the new node.  The walk stops
+ * at a leaf (emitting one token drawn from P_leaf) or when every child of u
+ * is rejected (emitting one token drawn from the current R).  Draws use the
+ * inverse CDF in vocabulary order: the smallest t whose cumulative weight
+ * exceeds r * (total weight).  T = 0 is greedy: g = argmax p_u (lowest index
+ * on ties), move to the lowest-numbered child whose token is g, else emit g.
+ *
+ * Coins are Philox4x64-10 (Salmon et al., SC'11) with key (seed, 0) and
+ * counter (step, b, local row, purpose): purpose 0 = accept coin of draft row
+ * c, purpose 1 = draw at the node where the walk stops;
+ * r = (word0 >> 11) * 2^-53.
+ *
+ *   parents_d            int32 [R] local parents (as for the mask)
+ *   tokens_d             int32 [R] draft token of each row (roots ignored)
+ *   p_logits_d           f32 [R][logits_ld], first `vocab` columns used
+ *   q_logits_d           f32 [R][logits_ld] (may be NULL when T == 0)
+ *   logits_ld            row stride in elements, >= vocab, multiple of 4;
+ *                        both logits pointers 16-byte aligned
+ *   path_stride          entries per request in path/tokens outputs, >= 1
+ * Outputs (spec_accept_out):
+ *   accept_len_d  [B]  a_b = accepted draft tokens
+ *   path_d        [B][path_stride]  accepted local rows, root first (a_b + 1
+ *                      entries), then -1
+ *   tokens_d      [B][path_stride]  the a_b accepted draft tokens followed by
+ *                      the final (corrected or bonus) token, then -1
+ *   accept_mask_d [R]  1 on rows of the accepted path (root included), else 0 (optional)
+ *   child_p_d     [R]  P_parent(c)(token c); NaN at roots (optional).  At T = 0:
+ *                      1 if token c is the parent's argmax, else 0.
+ *   child_q_d     [R]  Q_parent(c)(token c); NaN at roots; untouched at T = 0 (optional)
+ *   flags_d       [B]  SPEC_FLAG_* bits (optional)
+ * workspace >= spec_accept_workspace_bytes(batch, vocab) bytes (no init needed).
+ */
+#define SPEC_FLAG_ZERO_RESIDUAL 1   /* a residual had zero mass; R kept unchanged */
+#define SPEC_FLAG_PATH_TRUNCATED 2  /* path longer than path_stride; walk cut short */
+#define SPEC_FLAG_BAD_TREE 4        /* parent array invalid on the device; nothing emitted */
+
+typedef struct {
+  int32_t *accept_len_d;
+  int32_t *path_d;
+  int32_t *tokens_d;
+  uint8_t *accept_mask_d;
+  float *child_p_d;
+  float *child_q_d;
+  int32_t *flags_d;
+} spec_accept_out;
+
+size_t spec_accept_workspace_bytes(const spec_batch *batch, int32_t vocab);
+spec_status spec_accept_sample(const spec_batch *batch, const int32_t *parents_d,
+                               const int32_t *tokens_d, const float *p_logits_d,
+                               const float *q_logits_d, int64_t logits_ld, int32_t vocab,
+                               float temperature, uint64_t seed, uint64_t step,
+                               int32_t path_stride, const spec_accept_out *out,
+                               void *workspace_d, size_t workspace_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * spec_kv_commit -- [SD] KV-cache management: keep accepted tokens' K/V,
+ * roll back the rejected ones (paged: free their blocks).
+ *
+ * For each request: slot L_b + k receives the K/V row at slot L_b + path[k],
+ * k = 0 .. a_b (in place, all heads); new_len_d[b] = L_b + a_b + 1.  With
+ * paged caches and freed_blocks_d != NULL, row b of freed_blocks_d
+ * ([B][max_blocks_per_seq]) lists the physical blocks of logical blocks
+ * ceil(new_len/16) .. ceil((L_b + N_b)/16) - 1, then -1.  A request whose
+ * accept_len/path are inconsistent (a_b outside [0, N_b), path[0] != 0, or a
+ * path entry not strictly increasing / out of range) is left untouched and
+ * gets new_len_d[b] = -1.
+ */
+spec_status spec_kv_commit(const spec_batch *batch, const spec_kv *kv,
+                           const int32_t *accept_len_d, const int32_t *path_d,
+                           int32_t path_stride, int32_t *new_len_d,
+                           int32_t *freed_blocks_d, hipStream_t stream);
+
+const char *spec_status_string(spec_status status);
+const char *spec_last_error(void);
+int spec_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SPEC_VERIFY_H */

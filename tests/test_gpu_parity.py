@@ -1,0 +1,193 @@
+"""GPU parity: the HIP library against the oracle on seeded workloads.
+
+Reduced sizes span several 64-key tiles, several key splits and ragged tails;
+full sizes are the five stated workloads, checked on sampled requests for
+attention and on every request for acceptance.  Tolerances: masks, commits,
+paths and tokens bit-exact (near-threshold sampling decisions are reported,
+not failed); attention max |d| <= 1e-2 for bf16 inputs (1e-4 for fp32);
+child probabilities within 1e-5 relative.
+"""
+import numpy as np
+import pytest
+import torch
+
+pytestmark = pytest.mark.gpu
+
+from parity import (check_accept, check_attention, check_commit, check_mask, log, make,  # noqa: E402
+                    run_step)
+
+SMALL = {
+    "toy": dict(),
+    "chain8-small": dict(L=300, V=5000),
+    "chain8-d64": dict(L=333, V=4000, D=64, Hq=8, Hkv=8),
+    "medusa-small": dict(L=200, V=3000, Hq=4, Hkv=4),
+    "medusa-256rows": dict(L=150, V=2000, Hq=2, Hkv=2, tree=("cartesian", (5, 5, 9))),
+    "specinfer-small": dict(B=3, L=700, Hq=16, Hkv=2, V=6000),
+    "dynamic-small": dict(B=6, L=("uniform", 30, 700), V=5000),
+    "dynamic-contig": dict(B=5, L=("uniform", 0, 300), V=4004, kv_layout="contig"),
+    "specinfer-empty-prefix": dict(B=2, L=0, Hq=8, Hkv=2, V=2048),
+}
+BASE = {"toy": "toy", "chain8-small": "chain8", "chain8-d64": "chain8", "medusa-small": "medusa",
+        "medusa-256rows": "medusa", "specinfer-small": "specinfer", "dynamic-small": "dynamic",
+        "dynamic-contig": "dynamic", "specinfer-empty-prefix": "specinfer"}
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import tree_attention_verification_02_amd as T
+    assert torch.cuda.is_available()
+    return T
+
+
+@pytest.mark.parametrize("case", list(SMALL))
+def test_small_sampling(lib, case):
+    w = make(BASE[case], **SMALL[case])
+    snap = w.k_cache.clone()
+    vs = run_step(w, temperature=1.0, seed=0, step=0)
+    check_mask(w, vs)
+    worst = check_attention(w, vs)
+    log(f"[parity] {case}: attention max|d| = {worst:.3e}")
+    check_accept(w, vs, 1.0, 0, 0)
+    check_commit(w, vs)
+    # the library never writes below a request's prefix length
+    if w.kv_layout == "contig":
+        for b in range(w.B):
+            L = int(w.prefix_len[b])
+            assert torch.equal(w.k_cache[b, :, :L], snap[b, :, :L])
+
+
+@pytest.mark.parametrize("case", ["chain8-small", "medusa-small", "dynamic-small", "toy"])
+def test_small_greedy(lib, case):
+    w = make(BASE[case], **SMALL[case])
+    vs = run_step(w, temperature=0.0)
+    check_accept(w, vs, 0.0, 0, 0)
+    check_commit(w, vs)
+
+
+@pytest.mark.parametrize("case,T,seed,step", [("dynamic-small", 0.7, 5, 3),
+                                              ("medusa-small", 1.6, 1, 9)])
+def test_small_other_temperatures(lib, case, T, seed, step):
+    w = make(BASE[case], **SMALL[case])
+    vs = run_step(w, temperature=T, seed=seed, step=step)
+    check_accept(w, vs, T, seed, step)
+
+
+def test_fp32_output_of_bf16_path(lib):
+    w = make("specinfer", **SMALL["specinfer-small"])
+    vs = run_step(w, out_dtype=torch.float32)
+    worst = check_attention(w, vs, tol=5e-3)
+    log(f"[parity] fp32-out bf16 path max|d| = {worst:.3e}")
+
+
+def test_deterministic(lib):
+    w = make("dynamic", **SMALL["dynamic-small"])
+    a = run_step(w, commit=False)
+    out1 = a.attn_out.clone()
+    acc1 = [t.clone() for t in (a.acc.accept_len, a.acc.path, a.acc.tokens, a.acc.child_p)]
+    a.run(commit=False)
+    torch.cuda.synchronize()
+    assert torch.equal(out1, a.attn_out)
+    for x, y in zip(acc1, (a.acc.accept_len, a.acc.path, a.acc.tokens, a.acc.child_p)):
+        assert torch.equal(x, y)
+
+
+def test_device_side_tree_validation(lib):
+    import tree_attention_verification_02_amd._lib as L
+    w = make("dynamic", **SMALL["dynamic-small"])
+    from tree_attention_verification_02_amd.pipeline import VerifyStep
+    vs = VerifyStep(w)
+    bad = vs.parents.clone()
+    o = int(w.row_offsets[2])
+    bad[o + 3] = 7                     # parent not before the row
+    bad[int(w.row_offsets[4])] = 0     # root without -1
+    vs.parents = bad
+    vs.build_mask()
+    vs.accept()
+    torch.cuda.synchronize()
+    err = vs.err_row.cpu().numpy()
+    assert err[2] == 3 and err[4] == 0
+    assert (err[[0, 1, 3, 5]] == -1).all()
+    m = vs.mask.cpu().numpy()
+    assert (m[o:int(w.row_offsets[3])] == 0).all()
+    flags = vs.acc.flags.cpu().numpy()
+    alen = vs.acc.accept_len.cpu().numpy()
+    assert flags[2] == L.SPEC_FLAG_BAD_TREE and alen[2] == -1
+    assert flags[4] == L.SPEC_FLAG_BAD_TREE and alen[4] == -1
+
+
+def test_path_truncation_flag(lib):
+    import tree_attention_verification_02_amd._lib as L
+    w = make("chain8", L=64, V=512, Hq=2, Hkv=2, q_sigma=0.0)   # q = p: every draft accepted
+    vs = run_step(w, path_stride=4, commit=False)
+    assert int(vs.acc.flags[0]) == L.SPEC_FLAG_PATH_TRUNCATED
+    assert int(vs.acc.accept_len[0]) == 3
+    assert vs.acc.path[0].tolist() == [0, 1, 2, 3]
+    assert vs.acc.tokens[0].tolist()[3] == -1
+
+
+def test_commit_adversarial_paths(lib):
+    """In-place compaction with overlapping source/destination slots."""
+    w = make("medusa", **SMALL["medusa-small"])
+    from tree_attention_verification_02_amd.pipeline import VerifyStep
+    import tree_attention_verification_02_amd._lib as L
+    vs = VerifyStep(w, path_stride=8)
+    vs.append()
+    # hand-made accepted paths: root->1->(child of 1)->... in the Cartesian tree
+    from oracle import tree as OT
+    kids = OT.children(w.parents)
+    p = [0, 2, kids[2][4], kids[kids[2][4]][6]]
+    vs.acc.accept_len[0] = len(p) - 1
+    vs.acc.path[0, :] = -1
+    vs.acc.path[0, :len(p)] = torch.tensor(p, dtype=torch.int32)
+    vs.commit()
+    torch.cuda.synchronize()
+    check_commit(w, vs)
+    # a chain-prefix path is the identity
+    w2 = make("chain8", L=100, V=512, Hq=2, Hkv=2)
+    vs2 = VerifyStep(w2, path_stride=9)
+    vs2.append()
+    before = w2.k_cache.clone()
+    vs2.acc.accept_len[0] = 4
+    vs2.acc.path[0, :] = torch.tensor([0, 1, 2, 3, 4, -1, -1, -1, -1], dtype=torch.int32)
+    vs2.commit()
+    torch.cuda.synchronize()
+    assert torch.equal(before, w2.k_cache)
+    # an inconsistent path is refused with new_len = -1 and no write
+    vs2.acc.path[0, :5] = torch.tensor([0, 2, 1, 3, 4], dtype=torch.int32)
+    vs2.commit()
+    torch.cuda.synchronize()
+    assert int(vs2.new_len[0]) == -1
+    assert torch.equal(before, w2.k_cache)
+    del L
+
+
+FULL = ["toy", "chain8", "medusa", "specinfer", "dynamic"]
+SAMPLE_REQ = {"toy": None, "chain8": None, "medusa": None, "specinfer": [0, 5],
+              "dynamic": "pick"}
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size(lib, name):
+    w = make(name)
+    vs = run_step(w, temperature=1.0, seed=0, step=0)
+    check_mask(w, vs)
+    req = SAMPLE_REQ[name]
+    if req == "pick":
+        n = np.diff(w.row_offsets)
+        req = sorted({int(np.argmin(w.prefix_len)), int(np.argmax(w.prefix_len)),
+                      int(np.argmax(n)), 17})
+    worst = check_attention(w, vs, requests=req)
+    log(f"[parity] full {name}: attention max|d| = {worst:.3e} on requests {req}")
+    check_accept(w, vs, 1.0, 0, 0)
+    check_commit(w, vs, requests=req, heads=[0, w.Hkv - 1])
+    alen = vs.acc.accept_len.cpu().numpy()
+    log(f"[parity] full {name}: mean accepted drafts {alen.mean():.3f}")
+
+
+@pytest.mark.parametrize("name", ["specinfer", "dynamic"])
+def test_full_size_greedy_and_seed1(lib, name):
+    w = make(name)
+    vs = run_step(w, temperature=0.0, commit=False)
+    check_accept(w, vs, 0.0, 0, 0)
+    vs = run_step(w, temperature=1.0, seed=1, step=0, commit=False)
+    check_accept(w, vs, 1.0, 1, 0)

@@ -1,0 +1,57 @@
+// Host-side launchers of the verify-step kernels (called by the C ABI layer
+// after it has validated every argument).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "common.hpp"
+
+namespace spec {
+
+struct LaunchCtx {
+  int B;
+  const int32_t* row_offsets_d;
+  const int32_t* prefix_len_d;
+  hipStream_t stream;
+};
+
+// Split-KV plan of the bf16 tree-attention kernel: every (request, KV head,
+// row block, key split) is one workgroup.
+struct AttnPlan {
+  int rows_per_block;   // query rows (tree rows x group heads) per workgroup
+  int split_keys;       // keys per split (multiple of the key tile)
+  int64_t items;        // total workgroups
+  int64_t partial_items;// workgroups whose request needs more than one split
+  int64_t units;        // (request, KV head, row block) triples
+};
+
+hipError_t launch_build_mask(const LaunchCtx& cx, const int32_t* parents, uint64_t* mask, int words,
+                             int32_t* depth, int32_t* pos, int32_t* err_row);
+hipError_t launch_kv_append(const LaunchCtx& cx, int R, const KvAddr& addr, int esize,
+                            const void* k_new, const void* v_new, void* k_cache, void* v_cache);
+hipError_t launch_kv_commit(const LaunchCtx& cx, const KvAddr& addr, int esize,
+                            const int32_t* accept_len, const int32_t* path, int path_stride,
+                            void* k_cache, void* v_cache, int32_t* new_len, int32_t* freed);
+
+// Attention.
+AttnPlan plan_attention(int B, const int32_t* row_offsets_h, const int32_t* prefix_len_h, int hq,
+                        int hkv);
+size_t attention_workspace_bytes(const AttnPlan& plan, int d);
+hipError_t launch_attention_bf16(const LaunchCtx& cx, const AttnPlan& plan, const KvAddr& addr,
+                                 int hq, const void* q, const uint64_t* mask, int words,
+                                 float scale, const void* k_cache, const void* v_cache, void* out,
+                                 int out_f32, void* workspace);
+hipError_t launch_attention_f32(const LaunchCtx& cx, int R, const KvAddr& addr, int hq,
+                                const float* q, const uint64_t* mask, int words, float scale,
+                                const float* k_cache, const float* v_cache, void* out, int out_f32);
+
+// Acceptance.
+size_t accept_workspace_bytes(int R, int B);
+hipError_t launch_accept(const LaunchCtx& cx, int R, const int32_t* parents, const int32_t* tokens,
+                         const float* p_logits, const float* q_logits, int64_t ld, int vocab,
+                         float temperature, uint64_t seed, uint64_t step, int path_stride,
+                         int32_t* accept_len, int32_t* path, int32_t* tokens_out,
+                         uint8_t* accept_mask, float* child_p, float* child_q, int32_t* flags,
+                         void* workspace);
+
+}  // namespace spec

@@ -1,0 +1,85 @@
+"""One verify step over a workload: allocate device buffers, call the library.
+
+``VerifyStep`` owns the output and workspace tensors (torch allocations: the
+library itself never allocates) and runs the five C entry points in order on
+one stream: build mask -> append tree K/V -> tree attention -> acceptance ->
+commit.  It only marshals; every step runs in libspecverify.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import torch
+
+from . import _lib as L
+
+
+class VerifyStep:
+    def __init__(self, w, path_stride=None, out_dtype=None, temperature=None, seed=None, step=None):
+        """``w`` is any object with the workload fields (see workloads.gen.Workload)."""
+        dev = w.q.device
+        self.w = w
+        self.batch = L.Batch(w.row_offsets, w.prefix_len, dev)
+        self.parents = torch.from_numpy(np.asarray(w.parents, np.int32)).to(dev)
+        self.tokens = torch.from_numpy(np.asarray(w.tokens, np.int32)).to(dev)
+        R, B = self.batch.R, self.batch.B
+        self.kv = L.Kv(w.k_cache, w.v_cache, w.Hkv, w.D,
+                       layout="paged" if w.kv_layout == "paged" else "contig",
+                       capacity=getattr(w, "capacity", 0), block_table=w.block_table)
+        self.mask = torch.empty((R, self.batch.words), dtype=torch.int64, device=dev)
+        self.depth = torch.empty(R, dtype=torch.int32, device=dev)
+        self.position = torch.empty(R, dtype=torch.int32, device=dev)
+        self.err_row = torch.empty(B, dtype=torch.int32, device=dev)
+        odt = out_dtype or (torch.float32 if w.dtype == "f32" else torch.bfloat16)
+        self.attn_out = torch.empty((R, w.Hq, w.D), dtype=odt, device=dev)
+        self.attn_ws = torch.empty(L.spec_tree_attn_workspace_bytes(self.batch, self.kv, w.Hq),
+                                   dtype=torch.uint8, device=dev)
+        self.scale = 1.0 / math.sqrt(w.D)
+        S = path_stride or self.batch.c.max_rows
+        self.acc = L.AcceptOut(
+            accept_len=torch.empty(B, dtype=torch.int32, device=dev),
+            path=torch.empty((B, S), dtype=torch.int32, device=dev),
+            tokens=torch.empty((B, S), dtype=torch.int32, device=dev),
+            accept_mask=torch.empty(R, dtype=torch.uint8, device=dev),
+            child_p=torch.empty(R, dtype=torch.float32, device=dev),
+            child_q=torch.empty(R, dtype=torch.float32, device=dev),
+            flags=torch.empty(B, dtype=torch.int32, device=dev))
+        self.acc_ws = torch.empty(L.spec_accept_workspace_bytes(self.batch, w.V),
+                                  dtype=torch.uint8, device=dev)
+        self.new_len = torch.empty(B, dtype=torch.int32, device=dev)
+        mbps = int(w.block_table.shape[1]) if w.block_table is not None else 1
+        self.freed = torch.empty((B, mbps), dtype=torch.int32, device=dev)
+        self.temperature = w.temperature if temperature is None else temperature
+        self.seed = w.seed if seed is None else seed
+        self.step = w.step if step is None else step
+
+    # -- the five calls -------------------------------------------------------
+    def build_mask(self, stream=None):
+        L.spec_tree_build_mask(self.batch, self.parents, self.mask, self.depth, self.position,
+                               self.err_row, stream)
+
+    def append(self, stream=None):
+        L.spec_kv_append(self.batch, self.kv, self.w.k_new, self.w.v_new, stream)
+
+    def attention(self, stream=None):
+        L.spec_tree_attn_verify(self.batch, self.kv, self.w.q, self.w.Hq, self.mask, self.scale,
+                                self.attn_out, self.attn_ws, stream)
+
+    def accept(self, stream=None):
+        q = self.w.q_logits if self.temperature > 0 else None
+        L.spec_accept_sample(self.batch, self.parents, self.tokens, self.w.p_logits, q,
+                             self.w.V, self.temperature, self.seed, self.step, self.acc,
+                             self.acc_ws, stream=stream)
+
+    def commit(self, stream=None):
+        L.spec_kv_commit(self.batch, self.kv, self.acc.accept_len, self.acc.path, self.new_len,
+                         self.freed if self.w.kv_layout == "paged" else None, stream)
+
+    def run(self, stream=None, commit=True):
+        self.build_mask(stream)
+        self.append(stream)
+        self.attention(stream)
+        self.accept(stream)
+        if commit:
+            self.commit(stream)
