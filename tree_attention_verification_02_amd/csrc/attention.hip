@@ -34,7 +34,8 @@ constexpr int kTileKeys = 64;
 constexpr int kAttnWaves = 4;
 constexpr int kRowsPerWave = 32;
 constexpr int kRowsPerBlock = kAttnWaves * kRowsPerWave;
-constexpr int kVtStride = kTileKeys + 8;   // bf16 per transposed-V row in LDS
+constexpr int kVtStride = kTileKeys + 4;   // bf16 per transposed-V row in LDS (136 B)
+constexpr int kMaxSplit = 8192;            // keys per split (block ids kept in LDS)
 
 struct AttnArgs {
   const int32_t* row_offsets;
@@ -100,6 +101,99 @@ SPEC_DEVICE void locate(int64_t x, const AttnArgs& a, int& b_out, int64_t& base_
   base_out = 0;
 }
 
+
+typedef const __attribute__((address_space(1))) uint16_t* gptr_u16;
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef const __attribute__((address_space(1))) u32x4* gptr_u4;
+
+// 16-byte load through an explicitly global pointer (plain global_load, so
+// LDS waits in the loop do not also wait on the prefetch).
+SPEC_DEVICE uint4 gload16(gptr_u16 p) {
+  const u32x4 v = *(gptr_u4)p;
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// Element offset of absolute key kk: contiguous rows, or a paged block whose
+// id was staged in LDS (s_blk holds the split's block ids from block blk0).
+SPEC_DEVICE int64_t kv_key_offset(int kk, bool paged, const int* s_blk, int blk0, int64_t blk_stride,
+                                  int d) {
+  if (!paged) return (int64_t)kk * d;
+  return (int64_t)s_blk[(kk >> 4) - blk0] * blk_stride + (kk & 15) * d;
+}
+
+// Global -> registers for one 64-key tile: K as 16-byte row chunks, V as
+// 4 consecutive keys x 8 dims per thread (transposed when stored).
+template <int D>
+SPEC_DEVICE void load_kv_tile(gptr_u16 gk, gptr_u16 gv, int t0, int key_end, bool paged,
+                              const int* s_blk, int blk0, int64_t blk_stride, int tid,
+                              uint4 (&kreg)[kTileKeys * (D / 8) / 256],
+                              uint4 (&vreg)[((kTileKeys / 4) * (D / 8) + 255) / 256][4]) {
+  constexpr int DC = D / 8;
+  constexpr int KCH = kTileKeys * DC / 256;
+  constexpr int VUN = (kTileKeys / 4) * DC;
+  constexpr int VPT = (VUN + 255) / 256;
+#pragma unroll
+  for (int j = 0; j < KCH; ++j) {
+    const int c = tid + 256 * j;
+    const int kk = t0 + c / DC;
+    uint4 val = make_uint4(0, 0, 0, 0);
+    if (kk < key_end)
+      val = gload16(gk + kv_key_offset(kk, paged, s_blk, blk0, blk_stride, D) + (c % DC) * 8);
+    kreg[j] = val;
+  }
+#pragma unroll
+  for (int j = 0; j < VPT; ++j) {
+    const int u = tid + 256 * j;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int kk = t0 + (u / DC) * 4 + r;
+      uint4 val = make_uint4(0, 0, 0, 0);
+      if (u < VUN && kk < key_end)
+        val = gload16(gv + kv_key_offset(kk, paged, s_blk, blk0, blk_stride, D) + (u % DC) * 8);
+      vreg[j][r] = val;
+    }
+  }
+}
+
+// Registers -> LDS: K row-major (stride D + 8), V transposed to [dim][key].
+template <int D>
+SPEC_DEVICE void store_kv_tile(uint16_t* ks, uint16_t* vt, int tid,
+                               const uint4 (&kreg)[kTileKeys * (D / 8) / 256],
+                               const uint4 (&vreg)[((kTileKeys / 4) * (D / 8) + 255) / 256][4]) {
+  constexpr int DC = D / 8;
+  constexpr int KS = D + 8;
+  constexpr int KCH = kTileKeys * DC / 256;
+  constexpr int VUN = (kTileKeys / 4) * DC;
+  constexpr int VPT = (VUN + 255) / 256;
+#pragma unroll
+  for (int j = 0; j < KCH; ++j) {
+    const int c = tid + 256 * j;
+    *reinterpret_cast<uint4*>(&ks[(c / DC) * KS + (c % DC) * 8]) = kreg[j];
+  }
+#pragma unroll
+  for (int j = 0; j < VPT; ++j) {
+    const int u = tid + 256 * j;
+    if (u < VUN) {
+      const int kg = u / DC, dc = u % DC;
+      const uint32_t w0[4] = {vreg[j][0].x, vreg[j][0].y, vreg[j][0].z, vreg[j][0].w};
+      const uint32_t w1[4] = {vreg[j][1].x, vreg[j][1].y, vreg[j][1].z, vreg[j][1].w};
+      const uint32_t w2[4] = {vreg[j][2].x, vreg[j][2].y, vreg[j][2].z, vreg[j][2].w};
+      const uint32_t w3[4] = {vreg[j][3].x, vreg[j][3].y, vreg[j][3].z, vreg[j][3].w};
+#pragma unroll
+      for (int i2 = 0; i2 < 4; ++i2) {
+        // dims dc*8 + 2*i2 (low halves) and dc*8 + 2*i2 + 1 (high halves)
+        const uint2 lo = make_uint2((w0[i2] & 0xffffu) | (w1[i2] << 16),
+                                    (w2[i2] & 0xffffu) | (w3[i2] << 16));
+        const uint2 hi = make_uint2((w0[i2] >> 16) | (w1[i2] & 0xffff0000u),
+                                    (w2[i2] >> 16) | (w3[i2] & 0xffff0000u));
+        const int d0 = dc * 8 + 2 * i2;
+        *reinterpret_cast<uint2*>(&vt[d0 * kVtStride + kg * 4]) = lo;
+        *reinterpret_cast<uint2*>(&vt[(d0 + 1) * kVtStride + kg * 4]) = hi;
+      }
+    }
+  }
+}
+
 template <int D>
 __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnArgs a) {
   constexpr int KS = D + 8;                 // bf16 per K row in LDS
@@ -149,7 +243,7 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnArgs a) {
     const uint16_t* qp = a.q + ((int64_t)(o + ti) * a.hq + hh) * D + half * 8;
 #pragma unroll
     for (int kk = 0; kk < NKS; ++kk)
-      qf[kk] = *reinterpret_cast<const bf16x8*>(qp + kk * 16);
+      qf[kk] = __builtin_bit_cast(bf16x8, gload16((gptr_u16)(qp + kk * 16)));
     for (int w = 0; w < a.words; ++w) mw[w] = a.mask[(int64_t)(o + ti) * a.words + w];
   } else {
 #pragma unroll
@@ -167,76 +261,41 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnArgs a) {
   float l_run = 0.0f;
 
   // ---- tile staging -----------------------------------------------------
+  // Paged caches: the block ids of this split are read once into LDS so the
+  // tile loads below carry no dependent global lookups.
+  __shared__ int s_blk[kMaxSplit / kBlock + 2];
+  const int blk0 = key_begin >> 4;
+  const uint16_t* kbase;
+  const uint16_t* vbase;
+  if (a.addr.paged) {
+    const int nblk = ((key_end + kBlock - 1) >> 4) - blk0;
+    for (int i = tid; i < nblk; i += 256)
+      s_blk[i] = a.addr.block_table[(int64_t)b * a.addr.mbps + blk0 + i];
+    kbase = a.k + (int64_t)kvh * kBlock * D;
+    vbase = a.v + (int64_t)kvh * kBlock * D;
+  } else {
+    const int64_t off = ((int64_t)b * a.addr.hkv + kvh) * a.addr.capacity * D;
+    kbase = a.k + off;
+    vbase = a.v + off;
+  }
+  const int64_t blk_stride = (int64_t)a.addr.hkv * kBlock * D;
+  const bool paged = a.addr.paged;
+  const gptr_u16 gk = (const gptr_u16)kbase;
+  const gptr_u16 gv = (const gptr_u16)vbase;
   uint4 kreg[KCH];
   uint4 vreg[VPT][4];
-  const uint4 zero4 = make_uint4(0, 0, 0, 0);
-
-  auto load_tile = [&](int t0) {
-#pragma unroll
-    for (int j = 0; j < KCH; ++j) {
-      const int c = tid + 256 * j;
-      const int key = c / DC, dc = c % DC;
-      const int kk = t0 + key;
-      kreg[j] = (kk < key_end)
-          ? *reinterpret_cast<const uint4*>(a.k + a.addr(b, kvh, kk) + dc * 8)
-          : zero4;
-    }
-#pragma unroll
-    for (int j = 0; j < VPT; ++j) {
-      const int u = tid + 256 * j;
-      if (u < VUN) {
-        const int kg = u / DC, dc = u % DC;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int kk = t0 + kg * 4 + r;
-          vreg[j][r] = (kk < key_end)
-              ? *reinterpret_cast<const uint4*>(a.v + a.addr(b, kvh, kk) + dc * 8)
-              : zero4;
-        }
-      }
-    }
-  };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int j = 0; j < KCH; ++j) {
-      const int c = tid + 256 * j;
-      const int key = c / DC, dc = c % DC;
-      *reinterpret_cast<uint4*>(&ks_lds[buf][key * KS + dc * 8]) = kreg[j];
-    }
-#pragma unroll
-    for (int j = 0; j < VPT; ++j) {
-      const int u = tid + 256 * j;
-      if (u < VUN) {
-        const int kg = u / DC, dc = u % DC;
-        const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&vreg[j][0]);
-        const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&vreg[j][1]);
-        const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&vreg[j][2]);
-        const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&vreg[j][3]);
-#pragma unroll
-        for (int i2 = 0; i2 < 4; ++i2) {
-          // dims dc*8 + 2*i2 (low halves) and dc*8 + 2*i2 + 1 (high halves)
-          uint2 lo, hi;
-          lo.x = (w0[i2] & 0xffffu) | (w1[i2] << 16);
-          lo.y = (w2[i2] & 0xffffu) | (w3[i2] << 16);
-          hi.x = (w0[i2] >> 16) | (w1[i2] & 0xffff0000u);
-          hi.y = (w2[i2] >> 16) | (w3[i2] & 0xffff0000u);
-          const int d0 = dc * 8 + 2 * i2;
-          *reinterpret_cast<uint2*>(&vt_lds[buf][d0 * kVtStride + kg * 4]) = lo;
-          *reinterpret_cast<uint2*>(&vt_lds[buf][(d0 + 1) * kVtStride + kg * 4]) = hi;
-        }
-      }
-    }
-  };
 
   const int ntiles = (key_end - key_begin + kTileKeys - 1) / kTileKeys;
-  load_tile(key_begin);
-  store_tile(0);
+  __syncthreads();
+  load_kv_tile<D>(gk, gv, key_begin, key_end, paged, s_blk, blk0, blk_stride, tid, kreg, vreg);
+  store_kv_tile<D>(ks_lds[0], vt_lds[0], tid, kreg, vreg);
   __syncthreads();
 
   for (int t = 0; t < ntiles; ++t) {
     const int buf = t & 1;
     const int t0 = key_begin + t * kTileKeys;
-    if (t + 1 < ntiles) load_tile(t0 + kTileKeys);
+    if (t + 1 < ntiles)
+      load_kv_tile<D>(gk, gv, t0 + kTileKeys, key_end, paged, s_blk, blk0, blk_stride, tid, kreg, vreg);
 
     if (wave_active) {
       // S^T (64 keys x 32 rows) as two 32x32 blocks.
@@ -306,14 +365,12 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnArgs a) {
             const uint16_t* vp = &vt_lds[buf][(db * 32 + col) * kVtStride + kb];
             const uint2 lo = *reinterpret_cast<const uint2*>(vp);
             const uint2 hi = *reinterpret_cast<const uint2*>(vp + 8);
-            bf16x8 vf;
-            uint32_t* vw = reinterpret_cast<uint32_t*>(&vf);
-            vw[0] = lo.x; vw[1] = lo.y; vw[2] = hi.x; vw[3] = hi.y;
+            const bf16x8 vf = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
             acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[kh][mm], acc[db], 0, 0, 0);
           }
         }
     }
-    if (t + 1 < ntiles) store_tile(buf ^ 1);
+    if (t + 1 < ntiles) store_kv_tile<D>(ks_lds[buf ^ 1], vt_lds[buf ^ 1], tid, kreg, vreg);
     __syncthreads();
   }
 
@@ -531,6 +588,7 @@ AttnPlan plan_attention(int B, const int32_t* row_offsets_h, const int32_t* pref
   int64_t split = (work + target - 1) / target;
   split = ((split + kTileKeys - 1) / kTileKeys) * kTileKeys;
   if (split < 256) split = 256;
+  if (split > kMaxSplit) split = kMaxSplit;
   AttnPlan p;
   p.rows_per_block = kRowsPerBlock;
   p.split_keys = (int)split;
