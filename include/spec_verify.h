@@ -211,7 +211,8 @@ spec_status spec_tree_attn_verify(const spec_batch *batch, const spec_kv *kv,
  */
 #define SPEC_FLAG_ZERO_RESIDUAL 1   /* a residual had zero mass; R kept unchanged */
 #define SPEC_FLAG_PATH_TRUNCATED 2  /* path longer than path_stride; walk cut short */
-#define SPEC_FLAG_BAD_TREE 4        /* parent array invalid on the device; nothing emitted */
+#define SPEC_FLAG_BAD_TREE 4        /* parent array invalid on the device; accept_len = -1 */
+#define SPEC_FLAG_SYNC_TIMEOUT 8    /* walk workgroups did not meet in time; accept_len = -1 */
 
 typedef struct {
   int32_t *accept_len_d;

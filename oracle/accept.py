@@ -48,8 +48,12 @@ Readings taken where the pages are silent or garbled:
    beyond GPU = oracle; the statistics it must produce are pinned).
 
 Decisions whose outcome is within rounding of its threshold are reported as
-flagged: |r - R(x)/Q_u(x)| < FLAG_EPS for a child test, and a sampling target
-within FLAG_EPS * Z of a cumulative boundary.
+flagged: |r - R(x)/Q_u(x)| < FLAG_EPS (1e-6) for a child test, and a sampling
+target within FLAG_EPS_DRAW * Z (1e-9) of a cumulative boundary.  The draw
+window is narrower because a vocabulary of 128256 entries puts that many
+cumulative boundaries in [0, Z]: a 1e-6 window would flag about a quarter of
+all draws, while a float64 evaluation (as the GPU library does) places the
+boundaries within about 1e-11 * Z.
 """
 from __future__ import annotations
 
@@ -59,6 +63,7 @@ from .tree import children as tree_children
 from .tree import validate
 
 FLAG_EPS = 1e-6
+FLAG_EPS_DRAW = 1e-9
 
 
 def softmax(x: np.ndarray) -> np.ndarray:
@@ -112,10 +117,10 @@ class WalkResult:
     def accept_len(self) -> int:
         return len(self.path) - 1
 
-    def first_flag(self, eps: float = FLAG_EPS):
+    def first_flag(self, eps: float = FLAG_EPS, eps_draw: float = FLAG_EPS_DRAW):
         """Index into ``decisions`` of the first near-threshold decision, or None."""
-        for i, (_, _, m) in enumerate(self.decisions):
-            if m < eps:
+        for i, (kind, _, m) in enumerate(self.decisions):
+            if m < (eps_draw if kind == "sample" else eps):
                 return i
         return None
 

@@ -64,6 +64,15 @@ def test_small_greedy(lib, case):
     check_commit(w, vs)
 
 
+@pytest.mark.parametrize("slices", ["1", "3", "64"])
+def test_walk_slices(lib, slices, monkeypatch):
+    """The walk gives the same result however many workgroups share a request."""
+    monkeypatch.setenv("SPEC_WALK_SLICES", slices)
+    w = make("dynamic", B=5, L=("uniform", 30, 300), V=20000)
+    vs = run_step(w, temperature=1.0, seed=2, step=1, commit=False)
+    check_accept(w, vs, 1.0, 2, 1)
+
+
 @pytest.mark.parametrize("case,T,seed,step", [("dynamic-small", 0.7, 5, 3),
                                               ("medusa-small", 1.6, 1, 9)])
 def test_small_other_temperatures(lib, case, T, seed, step):

@@ -23,6 +23,7 @@ SPEC_BF16, SPEC_F32 = 0, 1
 SPEC_KV_CONTIGUOUS, SPEC_KV_PAGED = 0, 1
 SPEC_MAX_TREE_ROWS = 256
 SPEC_FLAG_ZERO_RESIDUAL, SPEC_FLAG_PATH_TRUNCATED, SPEC_FLAG_BAD_TREE = 1, 2, 4
+SPEC_FLAG_SYNC_TIMEOUT = 8
 STATUS_NAMES = {0: "SPEC_OK", 1: "SPEC_ERR_NULL", 2: "SPEC_ERR_SHAPE", 3: "SPEC_ERR_TREE",
                 4: "SPEC_ERR_CAPACITY", 5: "SPEC_ERR_DTYPE", 6: "SPEC_ERR_HIP",
                 7: "SPEC_ERR_UNSUPPORTED", 8: "SPEC_ERR_WORKSPACE"}

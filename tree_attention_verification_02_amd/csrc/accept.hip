@@ -3,23 +3,34 @@
 // Pages: CSDN "推理加速：推测解码与级联推理" sections 7.1-7.2 (accept with
 // probability min(1, p/q); on rejection draw from norm(max(0, p - q)); the
 // emitted length counts the final token); guijiagi.com speculative-decoding
-// post, rejection-sampling section (first rejection ends the step);
+// post, rejection-sampling section (the first rejection ends the step);
 // cnblogs "投机推理算法的常见优化手段", tree-mask section (row i's target
 // distribution predicts i's children; every level of the tree is checked).
 //
-// Two kernels:
-//  * accept_stats: one workgroup per (row, {target, draft}) streams the
-//    vocabulary row once with 16-byte loads and keeps, per thread, the
-//    running max, the sum of exp((x - max)/T) in fp64 and the first argmax;
-//    workgroup reduction, then the child probabilities P_u(x_c), Q_u(x_c) of
-//    that row's children are gathered in fp64.  Draft rows of leaves are
-//    never read.
-//  * accept_walk: one workgroup per request runs the sequential walk.  The
-//    sibling tests are scalar fp64; each rejection needs the residual mass
-//    Z = sum max(0, R - Q), and each final draw an inverse CDF, both as
-//    vocabulary passes in which every wave reduces a contiguous 256-element
-//    segment; ordered fp64 segment sums make the draw a two-level search
-//    (segment, then element) that re-reads one segment.
+// Residuals in closed form.  With P and Q fixed at a node, the residual after
+// any number of rejected siblings is R = max(0, P - t Q) / N for a scalar t:
+// starting from (t, N) = (0, 1), a rejection moves to t' = t + N and
+// N' = G(t') with G(t) = sum_y max(0, P_y - t Q_y) (and keeps (t, N) when
+// G(t') = 0).  So every rejection costs one vocabulary pass at a scalar t,
+// and the final draw after the last rejection reuses that pass's sums.
+//
+// Kernels:
+//  * accept_stats: one workgroup per (row, {target, draft}) streams the row
+//    once (16-byte loads) and produces the fp64 log-sum-exp of logits/T, the
+//    first argmax, and the child probabilities P_u(x_c), Q_u(x_c).  Draft rows
+//    of leaves are never read.
+//  * accept_walk (cooperative launch): S workgroups per request.  Each pass
+//    is split over the S workgroups by 1024-element segments; segment sums go
+//    to global memory and the S workgroups meet at a per-request counter
+//    barrier (bounded spin).  Every workgroup then sums the segments in the
+//    same order and replays the same scalar decisions, so no further
+//    broadcast is needed; the owner of the drawn segment rescans it.
+//  * accept_greedy: temperature 0, one workgroup per request.
+//
+// Every quantity that decides an integer (accept tests, residual masses,
+// inverse-CDF boundaries) is evaluated in fp64, with a table-driven fp64
+// exponential, so decisions agree with a float64 reference except within
+// ~1e-11 of a threshold.
 #include <math.h>
 
 #include "common.hpp"
@@ -31,45 +42,162 @@ namespace spec {
 constexpr int kStatThreads = 512;
 constexpr int kWalkThreads = 1024;
 constexpr int kWalkWaves = kWalkThreads / 64;
-constexpr int kTileElems = kWalkThreads * 4;           // elements per walk tile
-constexpr int kMaxSegs = 4096;                          // vocab <= 2^20
+constexpr int kSeg = kWalkThreads * 4;        // elements per segment
+constexpr int kMaxSegs = (1 << 20) / kSeg;    // vocab <= 2^20
+constexpr int kMaxSlices = 64;
+constexpr int kMaxSpins = 1 << 21;
 
+// ---------------------------------------------------------------------------
+// exp in double precision: x = k ln2/256 + r with |r| <= ln2/512;
+// exp(x) = 2^(k/256) e^r, 2^(j/256) from a table (values rounded to nearest
+// double) and e^r - 1 by its Taylor polynomial to degree 4 (truncation below
+// 4e-17 relative).  ln2/256 is split in two parts so that k * hi is exact for
+// every k below the overflow bound.
+__constant__ double kExp2Frac[256] = {
+    0x1.0000000000000p+0, 0x1.00b1afa5abcbfp+0, 0x1.0163da9fb3335p+0, 0x1.02168143b0281p+0,
+    0x1.02c9a3e778061p+0, 0x1.037d42e11bbccp+0, 0x1.04315e86e7f85p+0, 0x1.04e5f72f654b1p+0,
+    0x1.059b0d3158574p+0, 0x1.0650a0e3c1f89p+0, 0x1.0706b29ddf6dep+0, 0x1.07bd42b72a836p+0,
+    0x1.0874518759bc8p+0, 0x1.092bdf66607e0p+0, 0x1.09e3ecac6f383p+0, 0x1.0a9c79b1f3919p+0,
+    0x1.0b5586cf9890fp+0, 0x1.0c0f145e46c85p+0, 0x1.0cc922b7247f7p+0, 0x1.0d83b23395decp+0,
+    0x1.0e3ec32d3d1a2p+0, 0x1.0efa55fdfa9c5p+0, 0x1.0fb66affed31bp+0, 0x1.1073028d7233ep+0,
+    0x1.11301d0125b51p+0, 0x1.11edbab5e2ab6p+0, 0x1.12abdc06c31ccp+0, 0x1.136a814f204abp+0,
+    0x1.1429aaea92de0p+0, 0x1.14e95934f312ep+0, 0x1.15a98c8a58e51p+0, 0x1.166a45471c3c2p+0,
+    0x1.172b83c7d517bp+0, 0x1.17ed48695bbc0p+0, 0x1.18af9388c8deap+0, 0x1.1972658375d2fp+0,
+    0x1.1a35beb6fcb75p+0, 0x1.1af99f8138a1cp+0, 0x1.1bbe084045cd4p+0, 0x1.1c82f95281c6bp+0,
+    0x1.1d4873168b9aap+0, 0x1.1e0e75eb44027p+0, 0x1.1ed5022fcd91dp+0, 0x1.1f9c18438ce4dp+0,
+    0x1.2063b88628cd6p+0, 0x1.212be3578a819p+0, 0x1.21f49917ddc96p+0, 0x1.22bdda27912d1p+0,
+    0x1.2387a6e756238p+0, 0x1.2451ffb82140ap+0, 0x1.251ce4fb2a63fp+0, 0x1.25e85711ece75p+0,
+    0x1.26b4565e27cddp+0, 0x1.2780e341ddf29p+0, 0x1.284dfe1f56381p+0, 0x1.291ba7591bb70p+0,
+    0x1.29e9df51fdee1p+0, 0x1.2ab8a66d10f13p+0, 0x1.2b87fd0dad990p+0, 0x1.2c57e39771b2fp+0,
+    0x1.2d285a6e4030bp+0, 0x1.2df961f641589p+0, 0x1.2ecafa93e2f56p+0, 0x1.2f9d24abd886bp+0,
+    0x1.306fe0a31b715p+0, 0x1.31432edeeb2fdp+0, 0x1.32170fc4cd831p+0, 0x1.32eb83ba8ea32p+0,
+    0x1.33c08b26416ffp+0, 0x1.3496266e3fa2dp+0, 0x1.356c55f929ff1p+0, 0x1.36431a2de883bp+0,
+    0x1.371a7373aa9cbp+0, 0x1.37f26231e754ap+0, 0x1.38cae6d05d866p+0, 0x1.39a401b7140efp+0,
+    0x1.3a7db34e59ff7p+0, 0x1.3b57fbfec6cf4p+0, 0x1.3c32dc313a8e5p+0, 0x1.3d0e544ede173p+0,
+    0x1.3dea64c123422p+0, 0x1.3ec70df1c5175p+0, 0x1.3fa4504ac801cp+0, 0x1.40822c367a024p+0,
+    0x1.4160a21f72e2ap+0, 0x1.423fb2709468ap+0, 0x1.431f5d950a897p+0, 0x1.43ffa3f84b9d4p+0,
+    0x1.44e086061892dp+0, 0x1.45c2042a7d232p+0, 0x1.46a41ed1d0057p+0, 0x1.4786d668b3237p+0,
+    0x1.486a2b5c13cd0p+0, 0x1.494e1e192aed2p+0, 0x1.4a32af0d7d3dep+0, 0x1.4b17dea6db7d7p+0,
+    0x1.4bfdad5362a27p+0, 0x1.4ce41b817c114p+0, 0x1.4dcb299fddd0dp+0, 0x1.4eb2d81d8abffp+0,
+    0x1.4f9b2769d2ca7p+0, 0x1.508417f4531eep+0, 0x1.516daa2cf6642p+0, 0x1.5257de83f4eefp+0,
+    0x1.5342b569d4f82p+0, 0x1.542e2f4f6ad27p+0, 0x1.551a4ca5d920fp+0, 0x1.56070dde910d2p+0,
+    0x1.56f4736b527dap+0, 0x1.57e27dbe2c4cfp+0, 0x1.58d12d497c7fdp+0, 0x1.59c0827ff07ccp+0,
+    0x1.5ab07dd485429p+0, 0x1.5ba11fba87a03p+0, 0x1.5c9268a5946b7p+0, 0x1.5d84590998b93p+0,
+    0x1.5e76f15ad2148p+0, 0x1.5f6a320dceb71p+0, 0x1.605e1b976dc09p+0, 0x1.6152ae6cdf6f4p+0,
+    0x1.6247eb03a5585p+0, 0x1.633dd1d1929fdp+0, 0x1.6434634ccc320p+0, 0x1.652b9febc8fb7p+0,
+    0x1.6623882552225p+0, 0x1.671c1c70833f6p+0, 0x1.68155d44ca973p+0, 0x1.690f4b19e9538p+0,
+    0x1.6a09e667f3bcdp+0, 0x1.6b052fa75173ep+0, 0x1.6c012750bdabfp+0, 0x1.6cfdcddd47645p+0,
+    0x1.6dfb23c651a2fp+0, 0x1.6ef9298593ae5p+0, 0x1.6ff7df9519484p+0, 0x1.70f7466f42e87p+0,
+    0x1.71f75e8ec5f74p+0, 0x1.72f8286ead08ap+0, 0x1.73f9a48a58174p+0, 0x1.74fbd35d7cbfdp+0,
+    0x1.75feb564267c9p+0, 0x1.77024b1ab6e09p+0, 0x1.780694fde5d3fp+0, 0x1.790b938ac1cf6p+0,
+    0x1.7a11473eb0187p+0, 0x1.7b17b0976cfdbp+0, 0x1.7c1ed0130c132p+0, 0x1.7d26a62ff86f0p+0,
+    0x1.7e2f336cf4e62p+0, 0x1.7f3878491c491p+0, 0x1.80427543e1a12p+0, 0x1.814d2add106d9p+0,
+    0x1.82589994cce13p+0, 0x1.8364c1eb941f7p+0, 0x1.8471a4623c7adp+0, 0x1.857f4179f5b21p+0,
+    0x1.868d99b4492edp+0, 0x1.879cad931a436p+0, 0x1.88ac7d98a6699p+0, 0x1.89bd0a478580fp+0,
+    0x1.8ace5422aa0dbp+0, 0x1.8be05bad61778p+0, 0x1.8cf3216b5448cp+0, 0x1.8e06a5e0866d9p+0,
+    0x1.8f1ae99157736p+0, 0x1.902fed0282c8ap+0, 0x1.9145b0b91ffc6p+0, 0x1.925c353aa2fe2p+0,
+    0x1.93737b0cdc5e5p+0, 0x1.948b82b5f98e5p+0, 0x1.95a44cbc8520fp+0, 0x1.96bdd9a7670b3p+0,
+    0x1.97d829fde4e50p+0, 0x1.98f33e47a22a2p+0, 0x1.9a0f170ca07bap+0, 0x1.9b2bb4d53fe0dp+0,
+    0x1.9c49182a3f090p+0, 0x1.9d674194bb8d5p+0, 0x1.9e86319e32323p+0, 0x1.9fa5e8d07f29ep+0,
+    0x1.a0c667b5de565p+0, 0x1.a1e7aed8eb8bbp+0, 0x1.a309bec4a2d33p+0, 0x1.a42c980460ad8p+0,
+    0x1.a5503b23e255dp+0, 0x1.a674a8af46052p+0, 0x1.a799e1330b358p+0, 0x1.a8bfe53c12e59p+0,
+    0x1.a9e6b5579fdbfp+0, 0x1.ab0e521356ebap+0, 0x1.ac36bbfd3f37ap+0, 0x1.ad5ff3a3c2774p+0,
+    0x1.ae89f995ad3adp+0, 0x1.afb4ce622f2ffp+0, 0x1.b0e07298db666p+0, 0x1.b20ce6c9a8952p+0,
+    0x1.b33a2b84f15fbp+0, 0x1.b468415b749b1p+0, 0x1.b59728de5593ap+0, 0x1.b6c6e29f1c52ap+0,
+    0x1.b7f76f2fb5e47p+0, 0x1.b928cf22749e4p+0, 0x1.ba5b030a1064ap+0, 0x1.bb8e0b79a6f1fp+0,
+    0x1.bcc1e904bc1d2p+0, 0x1.bdf69c3f3a207p+0, 0x1.bf2c25bd71e09p+0, 0x1.c06286141b33dp+0,
+    0x1.c199bdd85529cp+0, 0x1.c2d1cd9fa652cp+0, 0x1.c40ab5fffd07ap+0, 0x1.c544778fafb22p+0,
+    0x1.c67f12e57d14bp+0, 0x1.c7ba88988c933p+0, 0x1.c8f6d9406e7b5p+0, 0x1.ca3405751c4dbp+0,
+    0x1.cb720dcef9069p+0, 0x1.ccb0f2e6d1675p+0, 0x1.cdf0b555dc3fap+0, 0x1.cf3155b5bab74p+0,
+    0x1.d072d4a07897cp+0, 0x1.d1b532b08c968p+0, 0x1.d2f87080d89f2p+0, 0x1.d43c8eacaa1d6p+0,
+    0x1.d5818dcfba487p+0, 0x1.d6c76e862e6d3p+0, 0x1.d80e316c98398p+0, 0x1.d955d71ff6075p+0,
+    0x1.da9e603db3285p+0, 0x1.dbe7cd63a8315p+0, 0x1.dd321f301b460p+0, 0x1.de7d5641c0658p+0,
+    0x1.dfc97337b9b5fp+0, 0x1.e11676b197d17p+0, 0x1.e264614f5a129p+0, 0x1.e3b333b16ee12p+0,
+    0x1.e502ee78b3ff6p+0, 0x1.e653924676d76p+0, 0x1.e7a51fbc74c83p+0, 0x1.e8f7977cdb740p+0,
+    0x1.ea4afa2a490dap+0, 0x1.eb9f4867cca6ep+0, 0x1.ecf482d8e67f1p+0, 0x1.ee4aaa2188510p+0,
+    0x1.efa1bee615a27p+0, 0x1.f0f9c1cb6412ap+0, 0x1.f252b376bba97p+0, 0x1.f3ac948dd7274p+0,
+    0x1.f50765b6e4540p+0, 0x1.f6632798844f8p+0, 0x1.f7bfdad9cbe14p+0, 0x1.f91d802243c89p+0,
+    0x1.fa7c1819e90d8p+0, 0x1.fbdba3692d514p+0, 0x1.fd3c22b8f71f1p+0, 0x1.fe9d96b2a23d9p+0,
+};
+constexpr double kInvLn2x256 = 0x1.71547652b82fep+8;
+constexpr double kLn2by256Hi = 0x1.62e42ff000000p-9;
+constexpr double kLn2by256Lo = -0x1.718432a1b0e26p-43;
+
+SPEC_DEVICE double exp_f64(double x, const double* tab) {
+  // Results below e^-708 (about 3e-308) are flushed to zero.  k is rounded
+  // with a 1.5 * 2^52 shifter so that its value sits in the low word, and
+  // the power of two is assembled from the exponent bits: only full-rate
+  // fp64 operations (fma/add/mul) are used.
+  if (!(x >= -708.0)) return 0.0;
+  constexpr double kShift = 0x1.8p52;
+  const double t = fma(x, kInvLn2x256, kShift);
+  const double k = t - kShift;
+  const int ki = (int)(uint32_t)__double_as_longlong(t);
+  const double r = fma(-k, kLn2by256Lo, fma(-k, kLn2by256Hi, x));
+  const double p = r * fma(r, fma(r, fma(r, 1.0 / 24, 1.0 / 6), 0.5), 1.0);
+  const double s = tab[ki & 255];
+  const double scale = __longlong_as_double((long long)((ki >> 8) + 1023) << 52);
+  return fma(s, p, s) * scale;
+}
+
+SPEC_DEVICE void load_exp_table(double* s_tab) {
+  for (int i = threadIdx.x; i < 256; i += blockDim.x) s_tab[i] = kExp2Frac[i];
+}
+
+// ---------------------------------------------------------------------------
+// Workspace.
 struct AcceptWs {
-  double* s;      // [2][R] sum of exp((x - m)/T)
-  float* m;       // [2][R] row max of the raw logits
-  int32_t* am;    // [R] argmax of the target row
+  double* lse;      // [2][R] log-sum-exp of logits / T (target rows, draft rows)
+  int32_t* am;      // [R]   first argmax of the target row
+  int32_t* sync;    // [B]   walk barrier counters (zeroed by accept_stats)
+  double* seg;      // [B][2][kMaxSegs] per-pass segment sums (double-buffered)
+  int32_t* last;    // [B][2][kMaxSlices] last positive index per slice
 };
 
-__host__ __device__ inline AcceptWs accept_ws(void* base, int R) {
+__host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+__host__ __device__ inline AcceptWs accept_ws(void* base, int R, int B, int nseg) {
+  char* p = (char*)base;
   AcceptWs w;
-  w.s = (double*)base;
-  w.m = (float*)(w.s + 2 * (size_t)R);
-  w.am = (int32_t*)(w.m + 2 * (size_t)R);
+  w.lse = (double*)p;
+  p += align256(2 * (size_t)R * sizeof(double));
+  w.am = (int32_t*)p;
+  p += align256((size_t)R * sizeof(int32_t));
+  w.sync = (int32_t*)p;
+  p += align256((size_t)B * sizeof(int32_t));
+  w.seg = (double*)p;
+  p += align256((size_t)B * 2 * nseg * sizeof(double));
+  w.last = (int32_t*)p;
   return w;
 }
 
-size_t accept_workspace_bytes(int R, int B) {
-  (void)B;
-  return 2 * (size_t)R * sizeof(double) + 2 * (size_t)R * sizeof(float) +
-         (size_t)R * sizeof(int32_t) + 256;
+static int segs_for(int vocab) { return (vocab + kSeg - 1) / kSeg; }
+
+size_t accept_workspace_bytes(int R, int B, int vocab) {
+  const int nseg = segs_for(vocab);
+  return align256(2 * (size_t)R * sizeof(double)) + align256((size_t)R * sizeof(int32_t)) +
+         align256((size_t)B * sizeof(int32_t)) + align256((size_t)B * 2 * nseg * sizeof(double)) +
+         align256((size_t)B * 2 * kMaxSlices * sizeof(int32_t));
 }
 
-// (max, sum, argmax) triple merge; sums are relative to their own max.
-SPEC_DEVICE void merge_stat(float& m, double& s, int& am, float m2, double s2, int am2, float invT) {
-  const float M = fmaxf(m, m2);
-  if (M == -INFINITY) {
-    am = (am < 0) ? am2 : (am2 < 0 ? am : min(am, am2));
-    return;
+// ---------------------------------------------------------------------------
+// Statistics.
+
+// (reference, sum) pairs: sum of exp(z - reference).
+SPEC_DEVICE void merge_ref(double& ref, double& s, double ref2, double s2, const double* tab) {
+  if (ref2 > ref) {
+    s = s * exp_f64(ref - ref2, tab) + s2;
+    ref = ref2;
+  } else if (s2 != 0.0) {
+    s += s2 * exp_f64(ref2 - ref, tab);
   }
-  const double w1 = (m == -INFINITY) ? 0.0 : exp((double)(m - M) * (double)invT);
-  const double w2 = (m2 == -INFINITY) ? 0.0 : exp((double)(m2 - M) * (double)invT);
-  int a;
-  if (m > m2) a = am;
-  else if (m2 > m) a = am2;
-  else a = (am < 0) ? am2 : (am2 < 0 ? am : min(am, am2));
-  s = s * w1 + s2 * w2;
-  m = M;
-  am = a;
+}
+
+SPEC_DEVICE void merge_arg(float& m, int& am, float m2, int am2) {
+  if (m2 > m || (m2 == m && am2 >= 0 && (am < 0 || am2 < am))) {
+    m = m2;
+    am = am2;
+  }
 }
 
 __global__ void __launch_bounds__(kStatThreads)
@@ -78,10 +206,14 @@ accept_stats_kernel(const int32_t* __restrict__ row_offsets, int B, int R,
                     const float* __restrict__ p_logits, const float* __restrict__ q_logits,
                     int64_t ld, int vocab, float temperature, AcceptWs ws,
                     float* __restrict__ child_p, float* __restrict__ child_q) {
+  __shared__ double s_tab[256];
   __shared__ float red_m[kStatThreads / 64];
-  __shared__ double red_s[kStatThreads / 64];
   __shared__ int red_a[kStatThreads / 64];
+  __shared__ double red_r[kStatThreads / 64];
+  __shared__ double red_s[kStatThreads / 64];
   __shared__ int has_kids;
+  __shared__ double s_lse;
+  __shared__ int s_am;
   const int which = blockIdx.x >= R ? 1 : 0;          // 0: target p, 1: draft q
   const int r = blockIdx.x - which * R;
   const int b = request_of_row(row_offsets, B, r);
@@ -90,22 +222,29 @@ accept_stats_kernel(const int32_t* __restrict__ row_offsets, int B, int R,
   const int u = r - o;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const bool greedy = temperature == 0.0f;
+  if (blockIdx.x == 0)
+    for (int i = tid; i < B; i += kStatThreads) ws.sync[i] = 0;
+  load_exp_table(s_tab);
+  if (tid == 0) has_kids = 0;
+  __syncthreads();
   if (which == 1) {
-    if (tid == 0) has_kids = 0;
-    __syncthreads();
     for (int i = tid; i < n; i += kStatThreads)
       if (i > 0 && parents[o + i] == u) has_kids = 1;
     __syncthreads();
     if (!has_kids) return;
   }
-  const float invT = greedy ? 1.0f : 1.0f / temperature;
+  const double invT = greedy ? 1.0 : 1.0 / (double)temperature;
   const float* row = (which ? q_logits : p_logits) + (int64_t)r * ld;
   const float4* row4 = reinterpret_cast<const float4*>(row);
   const int v4 = (vocab + 3) >> 2;
 
   float m = -INFINITY;
-  double s = 0.0;
   int am = -1;
+  // common reference for the exponent sums: the row's first logit (rare
+  // per-thread rescale when a value exceeds it by more than e^64)
+  double ref = (double)row[0] * invT;
+  if (!(ref > -INFINITY && ref < INFINITY)) ref = 0.0;
+  double s = 0.0;
   constexpr int U = 4;
   for (int f0 = tid; f0 < v4; f0 += kStatThreads * U) {
     float4 x[U];
@@ -121,59 +260,55 @@ accept_stats_kernel(const int32_t* __restrict__ row_offsets, int B, int R,
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const float xv = (y0 + j < vocab) ? xs[j] : -INFINITY;
-        if (xv > m) {
-          if (!greedy) s = (m == -INFINITY) ? 0.0 : s * exp((double)(m - xv) * (double)invT);
-          m = xv;
-          am = y0 + j;
+        const bool gt = xv > m;
+        m = gt ? xv : m;
+        am = gt ? y0 + j : am;
+        if (!greedy && xv != -INFINITY) {
+          const double d = (double)xv * invT - ref;
+          if (d > 64.0) {                         // rare: move the reference up
+            s *= exp_f64(-d, s_tab);
+            ref += d;
+            s += 1.0;
+          } else {
+            s += exp_f64(d, s_tab);
+          }
         }
-        if (!greedy && xv != -INFINITY) s += (double)expf((xv - m) * invT);
       }
     }
   }
   // wave then workgroup reduction
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) {
-    const float m2 = __shfl_xor(m, off, 64);
-    const double s2 = __shfl_xor(s, off, 64);
-    const int a2 = __shfl_xor(am, off, 64);
-    merge_stat(m, s, am, m2, s2, a2, invT);
+    merge_arg(m, am, __shfl_xor(m, off, 64), __shfl_xor(am, off, 64));
+    if (!greedy) merge_ref(ref, s, __shfl_xor(ref, off, 64), __shfl_xor(s, off, 64), s_tab);
   }
   if (lane == 0) {
     red_m[wave] = m;
-    red_s[wave] = s;
     red_a[wave] = am;
+    red_r[wave] = ref;
+    red_s[wave] = s;
   }
   __syncthreads();
-  if (wave == 0) {
-    m = (lane < kStatThreads / 64) ? red_m[lane] : -INFINITY;
-    s = (lane < kStatThreads / 64) ? red_s[lane] : 0.0;
-    am = (lane < kStatThreads / 64) ? red_a[lane] : -1;
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-      const float m2 = __shfl_xor(m, off, 64);
-      const double s2 = __shfl_xor(s, off, 64);
-      const int a2 = __shfl_xor(am, off, 64);
-      merge_stat(m, s, am, m2, s2, a2, invT);
+  if (tid == 0) {
+    for (int w = 1; w < kStatThreads / 64; ++w) {
+      merge_arg(m, am, red_m[w], red_a[w]);
+      if (!greedy) merge_ref(ref, s, red_r[w], red_s[w], s_tab);
     }
-    if (lane == 0) {
-      ws.m[which * R + r] = m;
-      ws.s[which * R + r] = s;
-      if (which == 0) ws.am[r] = am;
-      red_m[0] = m;
-      red_s[0] = s;
-      red_a[0] = am;
-    }
+    const double lse = greedy ? 0.0 : ref + log(s);
+    if (!greedy) ws.lse[which * R + r] = lse;
+    if (which == 0) ws.am[r] = am;
+    s_lse = lse;
+    s_am = am;
   }
   __syncthreads();
-  m = red_m[0];
-  s = red_s[0];
-  am = red_a[0];
-  float* dst = which ? child_q : child_p;
-  if (dst == nullptr || (which == 1 && greedy)) return;
+  const double lse = s_lse;
+  am = s_am;
   if (which == 0 && u == 0 && tid == 0) {                          // root: no draft
     if (child_p) child_p[o] = __int_as_float(0x7fc00000);
     if (child_q && !greedy) child_q[o] = __int_as_float(0x7fc00000);
   }
+  float* dst = which ? child_q : child_p;
+  if (dst == nullptr || (which == 1 && greedy)) return;
   for (int i = tid; i < n; i += kStatThreads) {
     if (i > 0 && parents[o + i] == u) {
       const int x = tokens[o + i];
@@ -181,8 +316,7 @@ accept_stats_kernel(const int32_t* __restrict__ row_offsets, int B, int R,
       if (greedy) {
         val = (x == am) ? 1.0f : 0.0f;
       } else {
-        const float lx = (x >= 0 && x < vocab) ? row[x] : -INFINITY;
-        val = (float)(exp(((double)lx - (double)m) * (double)invT) / s);
+        val = (x >= 0 && x < vocab) ? (float)exp_f64((double)row[x] * invT - lse, s_tab) : 0.0f;
       }
       dst[o + i] = val;
     }
@@ -192,137 +326,192 @@ accept_stats_kernel(const int32_t* __restrict__ row_offsets, int B, int R,
 // ---------------------------------------------------------------------------
 // Walk.
 
-struct WalkRow {
-  const float* p;
-  const float* q;
-  float mp, mq, invT;
-  double inv_sp, inv_sq;
-};
-
-// Weight of vocabulary entry y after `nres` residual steps.  final_res
-// selects max(0, R - Q) (the next residual's mass) instead of R itself.
-SPEC_DEVICE double walk_weight(const WalkRow& w, float py, float qy, int nres, const double* zinv,
-                               bool final_res) {
-  double R = (double)expf((py - w.mp) * w.invT) * w.inv_sp;
-  if (nres == 0 && !final_res) return R;
-  const double Q = (double)expf((qy - w.mq) * w.invT) * w.inv_sq;
-  for (int i = 0; i < nres; ++i) {
-    const double rn = fmax(0.0, R - Q);
-    R = (zinv[i] > 0.0) ? rn * zinv[i] : R;
-  }
-  return final_res ? fmax(0.0, R - Q) : R;
-}
-
-// Inclusive wave scan (Hillis-Steele) of doubles.
-SPEC_DEVICE double wave_incl_scan(double v, int lane) {
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const double t = __shfl_up(v, o, 64);
-    if (lane >= o) v += t;
-  }
-  return v;
-}
-
 struct WalkShared {
   int par[kMaxRows];
   int tok[kMaxRows];
   int kid_start[kMaxRows + 1];
   int kid_list[kMaxRows];
-  double seg[kMaxSegs];
-  double zinv[kMaxRows];
-  double lane_excl[64];
-  int last_pos;
-  int bad;
-  // broadcast slots
+  int path[kMaxRows];
+  int toks[kMaxRows + 1];
+  double tab[256];
+  double wave_tot[4][kWalkWaves];   // per unrolled segment, per wave
+  double lane_excl[64];             // prefix of the segment sums, per lane block
   double total;
   double c0;
   int found_seg;
+  int last_pos;
   int pick;
+  int bad;
+  int timeout;
+  // walk state (broadcast from thread 0)
+  int u, len, ntok, done, accept, flags;
 };
 
-// One vocabulary pass: fills seg[] with the ordered segment sums of the
-// weights and returns their total (the last inclusive prefix).
-SPEC_DEVICE double walk_pass(WalkShared& sh, const WalkRow& w, int vocab, int nres, bool final_res,
+// Unnormalised weight of entry y: max(0, P_y - t Q_y), or P_y alone when
+// need_q is false (t = 0 at a leaf).
+SPEC_DEVICE double walk_weight(float py, float qy, double invT, double lse_p, double lse_q,
+                               double t, bool need_q, const double* tab) {
+  const double P = exp_f64((double)py * invT - lse_p, tab);
+  if (!need_q) return P;
+  const double Q = exp_f64((double)qy * invT - lse_q, tab);
+  return fmax(0.0, fma(-t, Q, P));
+}
+
+SPEC_DEVICE double wave_incl_scan(double v, int lane) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const double x = __shfl_up(v, o, 64);
+    if (lane >= o) v += x;
+  }
+  return v;
+}
+
+// Per-request barrier of the S workgroups.  The data exchanged across
+// workgroups (segment sums, last positive index) is written with agent-scope
+// atomic stores and read with agent-scope atomic loads, both coherent at the
+// device level, so no L2 writeback/invalidate is needed: each thread waits
+// for its own stores to complete, then thread 0 arrives on the counter and
+// waits (bounded) for S * pass arrivals.
+SPEC_DEVICE void slice_barrier(WalkShared& sh, int* ctr, int target, int S) {
+  if (S == 1) {                 // nothing crosses workgroups
+    __syncthreads();
+    return;
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    int spins = 0;
+    while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+      __builtin_amdgcn_s_sleep(2);
+      if (++spins > kMaxSpins) {
+        sh.timeout = 1;
+        break;
+      }
+    }
+  }
+  __syncthreads();
+}
+
+SPEC_DEVICE void store_shared_d(double* p, double v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+SPEC_DEVICE double load_shared_d(const double* p) {
+  return __hip_atomic_load(const_cast<double*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+SPEC_DEVICE void store_shared_i(int* p, int v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+SPEC_DEVICE int load_shared_i(const int* p) {
+  return __hip_atomic_load(const_cast<int*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+struct WalkCtx {
+  const float* p;     // target row of the current node
+  const float* q;     // draft row of the current node
+  double invT, lse_p, lse_q;
+  int vocab, nseg, seg_lo, seg_hi, slice, S;
+  double* seg;        // this request's [2][nseg]
+  int* last;          // this request's [2][kMaxSlices]
+};
+
+// One vocabulary pass: this workgroup's segments of max(0, P - tQ) (or P),
+// then the request barrier, then the ordered total over all segments.
+SPEC_DEVICE double walk_pass(WalkShared& sh, const WalkCtx& c, int* ctr, int pass, double t,
                              bool need_q) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int ntiles = (vocab + kTileElems - 1) / kTileElems;
-  const float4* p4 = reinterpret_cast<const float4*>(w.p);
-  const float4* q4 = reinterpret_cast<const float4*>(w.q);
+  const int buf = pass & 1;
+  double* seg = c.seg + buf * c.nseg;
+  const float4* p4 = reinterpret_cast<const float4*>(c.p);
+  const float4* q4 = reinterpret_cast<const float4*>(c.q);
   int last = -1;
-  constexpr int U = 2;
-  for (int t0 = 0; t0 < ntiles; t0 += U) {
+  constexpr int U = 4;
+  for (int s0 = c.seg_lo; s0 < c.seg_hi; s0 += U) {
     float4 pv[U], qv[U];
 #pragma unroll
     for (int k = 0; k < U; ++k) {
-      const int y0 = (t0 + k) * kTileElems + 4 * tid;
-      const bool in = (t0 + k < ntiles) && y0 < vocab;
+      const int y0 = (s0 + k) * kSeg + 4 * tid;
+      const bool in = (s0 + k < c.seg_hi) && y0 < c.vocab;
       pv[k] = in ? p4[y0 >> 2] : make_float4(0.f, 0.f, 0.f, 0.f);
       qv[k] = (in && need_q) ? q4[y0 >> 2] : make_float4(0.f, 0.f, 0.f, 0.f);
     }
 #pragma unroll
     for (int k = 0; k < U; ++k) {
-      if (t0 + k >= ntiles) break;
-      const int y0 = (t0 + k) * kTileElems + 4 * tid;
+      const int y0 = (s0 + k) * kSeg + 4 * tid;
       const float pa[4] = {pv[k].x, pv[k].y, pv[k].z, pv[k].w};
       const float qa[4] = {qv[k].x, qv[k].y, qv[k].z, qv[k].w};
       double acc = 0.0;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        if (y0 + j < vocab) {
-          const double wt = walk_weight(w, pa[j], qa[j], nres, sh.zinv, final_res);
-          acc += wt;
-          if (wt > 0.0) last = y0 + j;
+        if (s0 + k < c.seg_hi && y0 + j < c.vocab) {
+          const double w = walk_weight(pa[j], qa[j], c.invT, c.lse_p, c.lse_q, t, need_q, sh.tab);
+          acc += w;
+          if (w > 0.0) last = y0 + j;
         }
       }
       const double incl = wave_incl_scan(acc, lane);
-      if (lane == 63) sh.seg[(t0 + k) * kWalkWaves + wave] = incl;
+      if (lane == 63) sh.wave_tot[k][wave] = incl;
     }
+    __syncthreads();
+    if (tid < U && s0 + tid < c.seg_hi) {
+      double tot = 0.0;
+      for (int w = 0; w < kWalkWaves; ++w) tot += sh.wave_tot[tid][w];
+      store_shared_d(&seg[s0 + tid], tot);
+    }
+    __syncthreads();
   }
-  // last index with positive weight (fallback of the inverse CDF)
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) last = max(last, __shfl_xor(last, o, 64));
+  if (tid == 0) sh.last_pos = -1;
+  __syncthreads();
   if (lane == 0) atomicMax(&sh.last_pos, last);
   __syncthreads();
+  if (tid == 0) store_shared_i(&c.last[buf * kMaxSlices + c.slice], sh.last_pos);
+  slice_barrier(sh, ctr, pass * c.S, c.S);
   if (wave == 0) {
-    const int nseg = ntiles * kWalkWaves;
-    const int per = (nseg + 63) / 64;
+    const int per = (c.nseg + 63) / 64;
     double part = 0.0;
     for (int k = 0; k < per; ++k) {
       const int sidx = lane * per + k;
-      if (sidx < nseg) part += sh.seg[sidx];
+      if (sidx < c.nseg) part += load_shared_d(&seg[sidx]);
     }
     const double incl = wave_incl_scan(part, lane);
-    if (lane == 63) sh.total = incl;
     sh.lane_excl[lane] = incl - part;
+    if (lane == 63) sh.total = incl;
+    if (lane == 0) {
+      int lp = -1;
+      for (int k = 0; k < c.S; ++k) lp = max(lp, load_shared_i(&c.last[buf * kMaxSlices + k]));
+      sh.last_pos = lp;
+    }
   }
   __syncthreads();
   return sh.total;
 }
 
-// Draw from the weights of the last pass with coin r; returns the index.
-SPEC_DEVICE int walk_draw(WalkShared& sh, const WalkRow& w, int vocab, int nres, bool final_res,
-                          bool need_q, double r) {
+// Inverse-CDF draw from the weights of pass `pass` with coin r.  Returns the
+// token if this workgroup determined it, else -1 (another slice owns it).
+SPEC_DEVICE int walk_draw(WalkShared& sh, const WalkCtx& c, int pass, double t, bool need_q,
+                          double r) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int ntiles = (vocab + kTileElems - 1) / kTileElems;
-  const int nseg = ntiles * kWalkWaves;
+  const double* seg = c.seg + (pass & 1) * c.nseg;
   const double target = r * sh.total;
   if (wave == 0) {
-    const int per = (nseg + 63) / 64;
+    const int per = (c.nseg + 63) / 64;
     double cum = sh.lane_excl[lane];
-    int hit_seg = -1;
+    int hit = -1;
     double hit_c0 = 0.0;
     for (int k = 0; k < per; ++k) {
       const int sidx = lane * per + k;
-      if (sidx < nseg) {
-        const double nxt = cum + sh.seg[sidx];
-        if (hit_seg < 0 && nxt > target) {
-          hit_seg = sidx;
+      if (sidx < c.nseg) {
+        const double nxt = cum + load_shared_d(&seg[sidx]);
+        if (hit < 0 && nxt > target) {
+          hit = sidx;
           hit_c0 = cum;
         }
         cum = nxt;
       }
     }
-    const uint64_t ball = __ballot(hit_seg >= 0);
+    const uint64_t ball = __ballot(hit >= 0);
     if (lane == 0) {
       sh.found_seg = -1;
       sh.pick = -1;
@@ -330,250 +519,359 @@ SPEC_DEVICE int walk_draw(WalkShared& sh, const WalkRow& w, int vocab, int nres,
     if (ball) {
       const int first = __ffsll((long long)ball) - 1;
       if (lane == first) {
-        sh.found_seg = hit_seg;
+        sh.found_seg = hit;
         sh.c0 = hit_c0;
       }
     }
   }
   __syncthreads();
   const int fs = sh.found_seg;
-  if (fs >= 0 && wave == 0) {
-    const int tile = fs / kWalkWaves, wv = fs % kWalkWaves;
-    const int y0 = tile * kTileElems + wv * 256 + 4 * lane;
-    float pa[4] = {0.f, 0.f, 0.f, 0.f}, qa[4] = {0.f, 0.f, 0.f, 0.f};
-    double wt[4] = {0.0, 0.0, 0.0, 0.0};
-    double acc = 0.0;
+  if (fs < 0) return (c.slice == 0) ? sh.last_pos : -1;   // rounding: last positive weight
+  if (fs < c.seg_lo || fs >= c.seg_hi) return -1;
+  // rescan the segment with the same arithmetic as the pass
+  const int y0 = fs * kSeg + 4 * tid;
+  double w[4] = {0.0, 0.0, 0.0, 0.0};
+  double acc = 0.0;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if (y0 + j < vocab) {
-        pa[j] = w.p[y0 + j];
-        if (need_q) qa[j] = w.q[y0 + j];
-        wt[j] = walk_weight(w, pa[j], qa[j], nres, sh.zinv, final_res);
-        acc += wt[j];
-      }
-    }
-    const double incl = wave_incl_scan(acc, lane);
-    const double base = sh.c0;
-    const uint64_t ball = __ballot(base + incl > target);
-    if (ball) {
-      const int first = __ffsll((long long)ball) - 1;
-      if (lane == first) {
-        double c = base + (incl - acc);
-        int pick = -1, lastpos = -1;
-        for (int j = 0; j < 4; ++j) {
-          if (y0 + j >= vocab) break;
-          if (wt[j] > 0.0) lastpos = y0 + j;
-          c += wt[j];
-          if (c > target) { pick = y0 + j; break; }
-        }
-        sh.pick = (pick >= 0) ? pick : lastpos;
-      }
+  for (int j = 0; j < 4; ++j) {
+    if (y0 + j < c.vocab) {
+      w[j] = walk_weight(c.p[y0 + j], need_q ? c.q[y0 + j] : 0.f, c.invT, c.lse_p, c.lse_q, t,
+                         need_q, sh.tab);
+      acc += w[j];
     }
   }
+  const double incl = wave_incl_scan(acc, lane);
+  if (lane == 63) sh.wave_tot[0][wave] = incl;
+  if (tid == 0) sh.pick = 0x7fffffff;
   __syncthreads();
-  int pick = sh.pick;
-  if (pick < 0) pick = sh.last_pos;     // rounding left no crossing: last positive weight
-  return pick;
+  double base = sh.c0;
+  for (int k = 0; k < wave; ++k) base += sh.wave_tot[0][k];
+  double cum = base + (incl - acc);
+  int pick = -1, lastpos = -1;
+  for (int j = 0; j < 4; ++j) {
+    if (y0 + j >= c.vocab) break;
+    if (w[j] > 0.0) lastpos = y0 + j;
+    cum += w[j];
+    if (cum > target) {
+      pick = y0 + j;
+      break;
+    }
+  }
+  if (pick >= 0) atomicMin(&sh.pick, pick);
+  __syncthreads();
+  int res = sh.pick;
+  if (res == 0x7fffffff) {
+    // rounding inside the segment: last positive weight of the segment
+    if (tid == 0) sh.pick = -1;
+    __syncthreads();
+    if (lastpos >= 0) atomicMax(&sh.pick, lastpos);
+    __syncthreads();
+    res = sh.pick;
+    if (res < 0) res = sh.last_pos;
+  }
+  return res;
 }
 
-__global__ void __launch_bounds__(kWalkThreads)
-accept_walk_kernel(const int32_t* __restrict__ row_offsets, int R,
-                   const int32_t* __restrict__ parents, const int32_t* __restrict__ tokens,
-                   const float* __restrict__ p_logits, const float* __restrict__ q_logits,
-                   int64_t ld, int vocab, float temperature, uint64_t seed, uint64_t step,
-                   int path_stride, AcceptWs ws, int32_t* __restrict__ accept_len,
-                   int32_t* __restrict__ path, int32_t* __restrict__ tokens_out,
-                   uint8_t* __restrict__ accept_mask, int32_t* __restrict__ flags) {
-  __shared__ WalkShared sh;
-  __shared__ int s_u, s_done, s_len, s_flags, s_child;
-  __shared__ int s_path[kMaxRows];
-  __shared__ int s_toks[kMaxRows + 1];
-  const int b = blockIdx.x;
-  const int o = row_offsets[b];
-  const int n = row_offsets[b + 1] - o;
+SPEC_DEVICE void load_tree(WalkShared& sh, const int32_t* parents, const int32_t* tokens, int o,
+                           int n) {
   const int tid = threadIdx.x;
-  const bool greedy = temperature == 0.0f;
-  const float invT = greedy ? 1.0f : 1.0f / temperature;
-
   if (tid == 0) sh.bad = 0;
   __syncthreads();
-  if (tid < n) {
-    sh.par[tid] = parents[o + tid];
-    sh.tok[tid] = tokens[o + tid];
-    const int p = sh.par[tid];
-    const bool ok = (tid == 0) ? (p == -1) : (p >= 0 && p < tid);
+  for (int i = tid; i < n; i += blockDim.x) {
+    const int p = parents[o + i];
+    sh.par[i] = p;
+    sh.tok[i] = tokens[o + i];
+    const bool ok = (i == 0) ? (p == -1) : (p >= 0 && p < i);
     if (!ok) sh.bad = 1;
   }
   __syncthreads();
-  if (sh.bad) {
-    for (int k = tid; k < path_stride; k += kWalkThreads) {
-      path[(int64_t)b * path_stride + k] = -1;
-      tokens_out[(int64_t)b * path_stride + k] = -1;
-    }
-    if (accept_mask)
-      for (int i = tid; i < n; i += kWalkThreads) accept_mask[o + i] = 0;
-    if (tid == 0) {
-      accept_len[b] = -1;
-      if (flags) flags[b] = kFlagBadTree;
-    }
-    return;
-  }
-  // children lists in ascending row order
-  if (tid < n) {
-    int c = 0;
-    for (int i = tid + 1; i < n; ++i) c += (sh.par[i] == tid);
-    sh.kid_start[tid + 1] = c;
+  if (sh.bad) return;
+  for (int i = tid; i < n; i += blockDim.x) {
+    int cnt = 0;
+    for (int j = i + 1; j < n; ++j) cnt += (sh.par[j] == i);
+    sh.kid_start[i + 1] = cnt;
   }
   __syncthreads();
   if (tid == 0) {
     sh.kid_start[0] = 0;
     for (int i = 1; i <= n; ++i) sh.kid_start[i] += sh.kid_start[i - 1];
-    s_u = 0;
-    s_done = 0;
-    s_len = 1;
-    s_flags = 0;
-    s_path[0] = 0;
   }
   __syncthreads();
-  if (tid < n) {
-    int pos = sh.kid_start[tid];
-    for (int i = tid + 1; i < n; ++i)
-      if (sh.par[i] == tid) sh.kid_list[pos++] = i;
+  for (int i = tid; i < n; i += blockDim.x) {
+    int pos = sh.kid_start[i];
+    for (int j = i + 1; j < n; ++j)
+      if (sh.par[j] == i) sh.kid_list[pos++] = j;
   }
   __syncthreads();
+}
 
-  int ntok = 0;   // tokens emitted (thread 0's copy is authoritative)
+struct WalkOut {
+  int32_t* accept_len;
+  int32_t* path;
+  int32_t* tokens_out;
+  uint8_t* accept_mask;
+  int32_t* flags;
+  int path_stride;
+};
+
+// Writes path, tokens (except index `skip`, written by the slice that drew
+// the final token), accept mask, length and flags.
+SPEC_DEVICE void write_outputs(WalkShared& sh, const WalkOut& w, int b, int o, int n, int skip) {
+  const int tid = threadIdx.x;
+  const int len = sh.len, nt = sh.ntok;
+  for (int k = tid; k < w.path_stride; k += blockDim.x) {
+    w.path[(int64_t)b * w.path_stride + k] = (k < len) ? sh.path[k] : -1;
+    if (k != skip)
+      w.tokens_out[(int64_t)b * w.path_stride + k] = (k < nt) ? sh.toks[k] : -1;
+  }
+  if (w.accept_mask) {
+    for (int i = tid; i < n; i += blockDim.x) w.accept_mask[o + i] = 0;
+    __syncthreads();
+    for (int k = tid; k < len; k += blockDim.x) w.accept_mask[o + sh.path[k]] = 1;
+  }
+  if (tid == 0) {
+    w.accept_len[b] = len - 1;
+    if (w.flags) w.flags[b] = sh.flags;
+  }
+}
+
+SPEC_DEVICE void write_bad_tree(const WalkOut& w, int b, int o, int n) {
+  const int tid = threadIdx.x;
+  for (int k = tid; k < w.path_stride; k += blockDim.x) {
+    w.path[(int64_t)b * w.path_stride + k] = -1;
+    w.tokens_out[(int64_t)b * w.path_stride + k] = -1;
+  }
+  if (w.accept_mask)
+    for (int i = tid; i < n; i += blockDim.x) w.accept_mask[o + i] = 0;
+  if (tid == 0) {
+    w.accept_len[b] = -1;
+    if (w.flags) w.flags[b] = kFlagBadTree;
+  }
+}
+
+// Per-request walk state, kept in LDS and advanced by thread 0.
+struct WalkState {
+  int u;            // current node (local row)
+  int kidx;         // next child of u to test (index into kid_list)
+  double t, N;      // residual R = max(0, P_u - t Q_u) / N
+  double pass_t;    // t of the weights the last pass left (-1: none at u)
+  int action;       // 0: pass, 1: pass then draw, 2: draw from the last pass, 3: stop
+  double act_t;     // t of the pass to run
+  int act_q;        // whether the pass needs the draft row
+};
+
+// Thread 0: run sibling tests and moves until a vocabulary pass (or a draw)
+// is needed.  Coins: purpose 0 for the accept test of child c, purpose 1 for
+// the draw at the node where the walk stops.
+SPEC_DEVICE void walk_decide(WalkShared& sh, WalkState& st, const float* p_logits,
+                             const float* q_logits, int64_t ld, int o, int vocab, double invT,
+                             const double* lse, int R, uint64_t seed, uint64_t step, int b,
+                             int path_stride) {
   while (true) {
-    const int u = s_u;
+    const int u = st.u;
     const int k0 = sh.kid_start[u], k1 = sh.kid_start[u + 1];
-    if (greedy) {
-      if (tid == 0) {
-        const int g = ws.am[o + u];
-        int nxt = -1;
-        for (int k = k0; k < k1; ++k)
-          if (sh.tok[sh.kid_list[k]] == g) { nxt = sh.kid_list[k]; break; }
-        if (nxt >= 0 && s_len >= path_stride) {
-          s_flags |= kFlagPathTruncated;
-          s_done = 1;
-        } else {
-          s_toks[ntok++] = g;
-          if (nxt >= 0) {
-            s_path[s_len++] = nxt;
-            s_u = nxt;
-          } else {
-            s_done = 1;
-          }
-        }
+    if (k1 == k0) {                      // leaf: bonus token from P_u
+      st.action = 1;
+      st.act_t = 0.0;
+      st.act_q = 0;
+      return;
+    }
+    if (st.kidx >= k1) {                 // every child rejected: draw from the residual
+      if (st.pass_t == st.t) {
+        st.action = 2;
+      } else {
+        st.action = 1;
+        st.act_t = st.t;
+        st.act_q = 1;
       }
-      __syncthreads();
-      if (s_done) break;
+      return;
+    }
+    const int ch = sh.kid_list[st.kidx];
+    const int x = sh.tok[ch];
+    const float* prow = p_logits + (int64_t)(o + u) * ld;
+    const float* qrow = q_logits + (int64_t)(o + u) * ld;
+    double Px = 0.0, Qx = 0.0;
+    if (x >= 0 && x < vocab) {
+      Px = exp_f64((double)prow[x] * invT - lse[o + u], sh.tab);
+      Qx = exp_f64((double)qrow[x] * invT - lse[R + o + u], sh.tab);
+    }
+    const double r = verify_uniform(seed, step, (uint64_t)b, (uint64_t)ch, 0);
+    const double Rx = fmax(0.0, fma(-st.t, Qx, Px)) / st.N;
+    if (r * Qx < Rx) {                   // accept: move to the child
+      if (sh.len >= path_stride) {
+        sh.flags |= kFlagPathTruncated;
+        st.action = 3;
+        return;
+      }
+      sh.toks[sh.ntok++] = x;
+      sh.path[sh.len++] = ch;
+      st.u = ch;
+      st.kidx = sh.kid_start[ch];
+      st.t = 0.0;
+      st.N = 1.0;
+      st.pass_t = -1.0;
       continue;
     }
-    // sampling walk at node u
-    WalkRow w;
-    w.p = p_logits + (int64_t)(o + u) * ld;
-    w.q = q_logits ? q_logits + (int64_t)(o + u) * ld : nullptr;
-    w.invT = invT;
-    w.mp = ws.m[o + u];
-    w.inv_sp = 1.0 / ws.s[o + u];
-    const bool leaf = (k1 == k0);
-    if (leaf) {
-      w.mq = 0.f;
-      w.inv_sq = 0.0;
-      if (tid == 0) sh.last_pos = -1;
-      __syncthreads();
-      walk_pass(sh, w, vocab, 0, false, false);
-      const double r = verify_uniform(seed, step, (uint64_t)b, (uint64_t)u, 1);
-      const int t = walk_draw(sh, w, vocab, 0, false, false, r);
-      if (tid == 0) s_toks[ntok++] = t;
-      break;
-    }
-    w.mq = ws.m[R + o + u];
-    w.inv_sq = 1.0 / ws.s[R + o + u];
-    int nres = 0;
-    bool moved = false;
-    for (int k = k0; k < k1; ++k) {
-      const int c = sh.kid_list[k];
-      if (tid == 0) {
-        const int x = sh.tok[c];
-        const double r = verify_uniform(seed, step, (uint64_t)b, (uint64_t)c, 0);
-        double Px = 0.0, Qx = 0.0;
-        if (x >= 0 && x < vocab) {
-          Px = exp(((double)w.p[x] - (double)w.mp) * (double)invT) * w.inv_sp;
-          Qx = exp(((double)w.q[x] - (double)w.mq) * (double)invT) * w.inv_sq;
-        }
-        double Rx = Px;
-        for (int i = 0; i < nres; ++i) {
-          const double rn = fmax(0.0, Rx - Qx);
-          Rx = (sh.zinv[i] > 0.0) ? rn * sh.zinv[i] : Rx;
-        }
-        s_child = (r * Qx < Rx) ? 1 : 0;
-        if (s_child && s_len >= path_stride) {
-          s_flags |= kFlagPathTruncated;
-          s_done = 1;
-          s_child = 0;
-        }
-      }
-      __syncthreads();
-      if (s_done) break;
-      if (s_child) {
+    // reject: the next residual needs G(t + N)
+    st.action = 0;
+    st.act_t = st.t + st.N;
+    st.act_q = 1;
+    return;
+  }
+}
+
+__global__ void __launch_bounds__(kWalkThreads)
+accept_walk_kernel(const int32_t* __restrict__ row_offsets, int R, int S,
+                   const int32_t* __restrict__ parents, const int32_t* __restrict__ tokens,
+                   const float* __restrict__ p_logits, const float* __restrict__ q_logits,
+                   int64_t ld, int vocab, float temperature, uint64_t seed, uint64_t step,
+                   AcceptWs ws, WalkOut out) {
+  __shared__ WalkShared sh;
+  __shared__ WalkState st;
+  const int b = blockIdx.x / S;
+  const int slice = blockIdx.x % S;
+  const int o = row_offsets[b];
+  const int n = row_offsets[b + 1] - o;
+  const int tid = threadIdx.x;
+  load_exp_table(sh.tab);
+  if (tid == 0) sh.timeout = 0;
+  load_tree(sh, parents, tokens, o, n);
+  if (sh.bad) {
+    if (slice == 0) write_bad_tree(out, b, o, n);
+    return;
+  }
+  WalkCtx c;
+  c.invT = 1.0 / (double)temperature;
+  c.vocab = vocab;
+  c.nseg = (vocab + kSeg - 1) / kSeg;
+  const int per = (c.nseg + S - 1) / S;
+  c.seg_lo = min(c.nseg, slice * per);
+  c.seg_hi = min(c.nseg, c.seg_lo + per);
+  c.slice = slice;
+  c.S = S;
+  c.seg = ws.seg + (size_t)b * 2 * c.nseg;
+  c.last = ws.last + (size_t)b * 2 * kMaxSlices;
+  int* ctr = ws.sync + b;
+  if (tid == 0) {
+    sh.len = 1;
+    sh.ntok = 0;
+    sh.flags = 0;
+    sh.path[0] = 0;
+    st.u = 0;
+    st.kidx = sh.kid_start[0];
+    st.t = 0.0;
+    st.N = 1.0;
+    st.pass_t = -1.0;
+  }
+  int pass = 0;
+  int final_token = -1;
+  bool final_here = false;
+  while (true) {
+    if (tid == 0)
+      walk_decide(sh, st, p_logits, q_logits, ld, o, vocab, c.invT, ws.lse, R, seed, step, b,
+                  out.path_stride);
+    __syncthreads();
+    const int action = st.action;
+    if (action == 3) break;
+    const int u = st.u;
+    c.p = p_logits + (int64_t)(o + u) * ld;
+    c.q = q_logits + (int64_t)(o + u) * ld;
+    c.lse_p = ws.lse[o + u];
+    c.lse_q = st.act_q ? ws.lse[R + o + u] : 0.0;
+    const double act_t = st.act_t;
+    const bool act_q = st.act_q != 0;
+    if (action != 2) {
+      const double G = walk_pass(sh, c, ctr, ++pass, act_t, act_q);
+      if (sh.timeout) break;
+      if (action == 0) {
         if (tid == 0) {
-          s_toks[ntok++] = sh.tok[c];
-          s_path[s_len++] = c;
-          s_u = c;
+          st.pass_t = act_t;
+          if (G > 0.0) {
+            st.t = act_t;
+            st.N = G;
+          } else {
+            sh.flags |= kFlagZeroResidual;
+          }
+          st.kidx += 1;
         }
-        moved = true;
         __syncthreads();
-        break;
+        continue;
       }
-      // rejected: residual mass for the next sibling (or the final draw)
-      if (tid == 0) sh.last_pos = -1;
-      __syncthreads();
-      const double Z = walk_pass(sh, w, vocab, nres, true, true);
-      if (tid == 0) {
-        sh.zinv[nres] = (Z > 0.0) ? 1.0 / Z : 0.0;
-        if (!(Z > 0.0)) s_flags |= kFlagZeroResidual;
-      }
-      __syncthreads();
-      ++nres;
     }
-    if (s_done) break;
-    if (moved) continue;
-    // every child rejected: draw from the current residual R_nres
+    // draw from the weights the last pass left
     const double r = verify_uniform(seed, step, (uint64_t)b, (uint64_t)u, 1);
-    int t;
-    if (sh.zinv[nres - 1] > 0.0) {
-      // weights max(0, R_{nres-1} - Q) of the last pass are R_nres unnormalised
-      t = walk_draw(sh, w, vocab, nres - 1, true, true, r);
-    } else {
-      if (tid == 0) sh.last_pos = -1;
-      __syncthreads();
-      walk_pass(sh, w, vocab, nres, false, true);
-      t = walk_draw(sh, w, vocab, nres, false, true, r);
-    }
-    if (tid == 0) s_toks[ntok++] = t;
+    const double dt = (action == 2) ? st.pass_t : act_t;
+    const bool dq = (action == 2) ? true : act_q;
+    final_token = walk_draw(sh, c, pass, dt, dq, r);
+    final_here = final_token >= 0;
     break;
   }
   __syncthreads();
-  // outputs
-  if (tid == 0) {
-    accept_len[b] = s_len - 1;
-    if (flags) flags[b] = s_flags;
-    const int nt = s_len - 1 + ((s_flags & kFlagPathTruncated) ? 0 : 1);
-    s_child = nt;   // reuse as token count broadcast
+  if (sh.timeout) {
+    if (slice == 0 && tid == 0) {
+      sh.flags |= kFlagSyncTimeout;
+      out.accept_len[b] = -1;
+      if (out.flags) out.flags[b] = sh.flags;
+    }
+    return;
+  }
+  const bool has_final = !(sh.flags & kFlagPathTruncated);
+  if (tid == 0 && has_final) sh.ntok += 1;       // the final token's slot
+  __syncthreads();
+  if (slice == 0) write_outputs(sh, out, b, o, n, has_final ? sh.ntok - 1 : -1);
+  if (has_final && final_here && tid == 0)
+    out.tokens_out[(int64_t)b * out.path_stride + sh.ntok - 1] = final_token;
+}
+
+// Greedy (temperature 0): one workgroup per request, decisions by thread 0.
+__global__ void __launch_bounds__(kWalkThreads)
+accept_greedy_kernel(const int32_t* __restrict__ row_offsets, const int32_t* __restrict__ parents,
+                     const int32_t* __restrict__ tokens, AcceptWs ws, WalkOut out) {
+  __shared__ WalkShared sh;
+  const int b = blockIdx.x;
+  const int o = row_offsets[b];
+  const int n = row_offsets[b + 1] - o;
+  load_tree(sh, parents, tokens, o, n);
+  if (sh.bad) {
+    write_bad_tree(out, b, o, n);
+    return;
+  }
+  if (threadIdx.x == 0) {
+    int u = 0, len = 1, nt = 0, flags = 0;
+    sh.path[0] = 0;
+    while (true) {
+      const int g = ws.am[o + u];
+      int nxt = -1;
+      for (int k = sh.kid_start[u]; k < sh.kid_start[u + 1]; ++k)
+        if (sh.tok[sh.kid_list[k]] == g) {
+          nxt = sh.kid_list[k];
+          break;
+        }
+      if (nxt >= 0 && len >= out.path_stride) {
+        flags |= kFlagPathTruncated;
+        break;
+      }
+      sh.toks[nt++] = g;
+      if (nxt < 0) break;
+      sh.path[len++] = nxt;
+      u = nxt;
+    }
+    sh.len = len;
+    sh.ntok = nt;
+    sh.flags = flags;
   }
   __syncthreads();
-  const int len = s_len;
-  const int nt = s_child;
-  for (int k = tid; k < path_stride; k += kWalkThreads) {
-    path[(int64_t)b * path_stride + k] = (k < len) ? s_path[k] : -1;
-    tokens_out[(int64_t)b * path_stride + k] = (k < nt) ? s_toks[k] : -1;
-  }
-  if (accept_mask) {
-    for (int i = tid; i < n; i += kWalkThreads) accept_mask[o + i] = 0;
-    __syncthreads();
-    for (int k = tid; k < len; k += kWalkThreads) accept_mask[o + s_path[k]] = 1;
-  }
+  write_outputs(sh, out, b, o, n, -1);
+}
+
+int walk_slices(int B, int vocab, int capacity_blocks) {
+  const int nseg = segs_for(vocab);
+  int S = capacity_blocks / (B > 0 ? B : 1);
+  const int want = nseg;                       // at least one segment per slice
+  if (S > want) S = want;
+  if (S > kMaxSlices) S = kMaxSlices;
+  if (S < 1) S = 1;
+  return S;
 }
 
 hipError_t launch_accept(const LaunchCtx& cx, int R, const int32_t* parents, const int32_t* tokens,
@@ -581,19 +879,48 @@ hipError_t launch_accept(const LaunchCtx& cx, int R, const int32_t* parents, con
                          float temperature, uint64_t seed, uint64_t step, int path_stride,
                          int32_t* accept_len, int32_t* path, int32_t* tokens_out,
                          uint8_t* accept_mask, float* child_p, float* child_q, int32_t* flags,
-                         void* workspace) {
-  AcceptWs ws = accept_ws(workspace, R);
+                         void* workspace, int slices_override) {
+  static_assert(sizeof(WalkShared) < 20480, "walk LDS");
+  const int nseg = segs_for(vocab);
+  AcceptWs ws = accept_ws(workspace, R, cx.B, nseg);
   const int nblk = (temperature == 0.0f) ? R : 2 * R;
   hipLaunchKernelGGL(accept_stats_kernel, dim3(nblk), dim3(kStatThreads), 0, cx.stream,
                      cx.row_offsets_d, cx.B, R, parents, tokens, p_logits, q_logits, ld, vocab,
                      temperature, ws, child_p, child_q);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(accept_walk_kernel, dim3(cx.B), dim3(kWalkThreads), 0, cx.stream,
-                     cx.row_offsets_d, R, parents, tokens, p_logits, q_logits, ld, vocab,
-                     temperature, seed, step, path_stride, ws, accept_len, path, tokens_out,
-                     accept_mask, flags);
-  return hipGetLastError();
+  WalkOut out{accept_len, path, tokens_out, accept_mask, flags, path_stride};
+  if (temperature == 0.0f) {
+    hipLaunchKernelGGL(accept_greedy_kernel, dim3(cx.B), dim3(kWalkThreads), 0, cx.stream,
+                       cx.row_offsets_d, parents, tokens, ws, out);
+    return hipGetLastError();
+  }
+  int dev = 0, cus = 0, per_cu = 0;
+  if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
+  if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess)
+    return e;
+  if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, accept_walk_kernel, kWalkThreads,
+                                                        0)) != hipSuccess)
+    return e;
+  const int capacity = cus * per_cu;
+  int S = walk_slices(cx.B, vocab, capacity);
+  if (slices_override > 0) S = slices_override < S ? slices_override : S;
+  if (S == 1) {
+    // one workgroup per request: no cross-workgroup waiting, any grid size
+    WalkOut o1 = out;
+    hipLaunchKernelGGL(accept_walk_kernel, dim3(cx.B), dim3(kWalkThreads), 0, cx.stream,
+                       cx.row_offsets_d, R, 1, parents, tokens, p_logits, q_logits, ld, vocab,
+                       temperature, seed, step, ws, o1);
+    return hipGetLastError();
+  }
+  const int32_t* ro = cx.row_offsets_d;
+  int S_arg = S;
+  void* args[] = {(void*)&ro,         (void*)&R,     (void*)&S_arg,    (void*)&parents,
+                  (void*)&tokens,     (void*)&p_logits, (void*)&q_logits, (void*)&ld,
+                  (void*)&vocab,      (void*)&temperature, (void*)&seed, (void*)&step,
+                  (void*)&ws,         (void*)&out};
+  return hipLaunchCooperativeKernel((const void*)accept_walk_kernel, dim3(cx.B * S),
+                                    dim3(kWalkThreads), args, 0, cx.stream);
 }
 
 }  // namespace spec

@@ -3,6 +3,7 @@
 // returns a status and leaves a thread-local message.
 #include <stdarg.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <algorithm>
@@ -16,6 +17,7 @@ static_assert(SPEC_KV_BLOCK == spec::kBlock, "block size");
 static_assert(SPEC_FLAG_ZERO_RESIDUAL == spec::kFlagZeroResidual, "flag");
 static_assert(SPEC_FLAG_PATH_TRUNCATED == spec::kFlagPathTruncated, "flag");
 static_assert(SPEC_FLAG_BAD_TREE == spec::kFlagBadTree, "flag");
+static_assert(SPEC_FLAG_SYNC_TIMEOUT == spec::kFlagSyncTimeout, "flag");
 
 namespace {
 
@@ -117,6 +119,13 @@ spec_status launched(hipError_t e, const char* what) {
 }
 
 int esize(spec_dtype d) { return d == SPEC_BF16 ? 2 : 4; }
+
+// Test hook: SPEC_WALK_SLICES=<n> caps the workgroups per request of the
+// sampling walk (default: as many as fit, up to 64).
+int walk_slices_override() {
+  const char* v = getenv("SPEC_WALK_SLICES");
+  return v ? atoi(v) : 0;
+}
 
 }  // namespace
 
@@ -220,7 +229,7 @@ size_t spec_accept_workspace_bytes(const spec_batch* batch, int32_t vocab) {
     fail(SPEC_ERR_UNSUPPORTED, "vocab = %d, supported 1..%d", vocab, kMaxVocab);
     return 0;
   }
-  return spec::accept_workspace_bytes(R, batch->batch);
+  return spec::accept_workspace_bytes(R, batch->batch, vocab);
 }
 
 spec_status spec_accept_sample(const spec_batch* batch, const int32_t* parents_d, const int32_t* tokens_d,
@@ -241,7 +250,7 @@ spec_status spec_accept_sample(const spec_batch* batch, const int32_t* parents_d
   if (path_stride < 1) return fail(SPEC_ERR_SHAPE, "path_stride = %d, need >= 1", path_stride);
   if (!out || !out->accept_len_d || !out->path_d || !out->tokens_d)
     return fail(SPEC_ERR_NULL, "out, accept_len_d, path_d and tokens_d are required");
-  const size_t need = spec::accept_workspace_bytes(R, batch->batch);
+  const size_t need = spec::accept_workspace_bytes(R, batch->batch, vocab);
   if (!workspace_d || workspace_bytes < need)
     return fail(SPEC_ERR_WORKSPACE, "accept workspace %zu bytes < required %zu", workspace_bytes, need);
   if (!aligned16(workspace_d)) return fail(SPEC_ERR_SHAPE, "workspace must be 16-byte aligned");
@@ -249,7 +258,7 @@ spec_status spec_accept_sample(const spec_batch* batch, const int32_t* parents_d
                                       temperature > 0.0f ? q_logits_d : nullptr, logits_ld, vocab,
                                       temperature, seed, step, path_stride, out->accept_len_d,
                                       out->path_d, out->tokens_d, out->accept_mask_d, out->child_p_d,
-                                      out->child_q_d, out->flags_d, workspace_d),
+                                      out->child_q_d, out->flags_d, workspace_d, walk_slices_override()),
                   "spec_accept_sample");
 }
 

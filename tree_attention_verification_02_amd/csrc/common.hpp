@@ -16,6 +16,7 @@ constexpr int kBlock = 16;         // paged KV block (tokens)
 constexpr int kFlagZeroResidual = 1;
 constexpr int kFlagPathTruncated = 2;
 constexpr int kFlagBadTree = 4;
+constexpr int kFlagSyncTimeout = 8;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));

@@ -46,12 +46,12 @@ hipError_t launch_attention_f32(const LaunchCtx& cx, int R, const KvAddr& addr, 
                                 const float* k_cache, const float* v_cache, void* out, int out_f32);
 
 // Acceptance.
-size_t accept_workspace_bytes(int R, int B);
+size_t accept_workspace_bytes(int R, int B, int vocab);
 hipError_t launch_accept(const LaunchCtx& cx, int R, const int32_t* parents, const int32_t* tokens,
                          const float* p_logits, const float* q_logits, int64_t ld, int vocab,
                          float temperature, uint64_t seed, uint64_t step, int path_stride,
                          int32_t* accept_len, int32_t* path, int32_t* tokens_out,
                          uint8_t* accept_mask, float* child_p, float* child_q, int32_t* flags,
-                         void* workspace);
+                         void* workspace, int slices_override);
 
 }  // namespace spec
