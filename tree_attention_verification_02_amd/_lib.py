@@ -63,7 +63,7 @@ class CAcceptOut(ctypes.Structure):
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with "
-                          "`python -m tree_attention_verification_02_amd.build`")
+                          "`python tree_attention_verification_02_amd/build.py`")
     lib = ctypes.CDLL(LIB_PATH)
     vp, i32, i64, u64, f32, sz = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
                                   ctypes.c_uint64, ctypes.c_float, ctypes.c_size_t)

@@ -1,6 +1,8 @@
 """Build libspecverify.so (HIP for gfx950) in-tree.
 
-    python -m tree_attention_verification_02_amd.build
+    python tree_attention_verification_02_amd/build.py
+
+(run as a script: importing the package itself needs the built library)
 
 Every translation unit is compiled by hipcc for gfx950 only, with packed
 fp32 instructions disabled, then linked into

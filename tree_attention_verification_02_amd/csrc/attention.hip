@@ -25,16 +25,19 @@
 //    lie wholly inside the prefix.
 #include <math.h>
 
+#include <algorithm>
+
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace spec {
 
 constexpr int kTileKeys = 64;
-constexpr int kAttnWaves = 4;
 constexpr int kRowsPerWave = 32;
-constexpr int kRowsPerBlock = kAttnWaves * kRowsPerWave;
-constexpr int kVtStride = kTileKeys + 4;   // bf16 per transposed-V row in LDS (136 B)
+constexpr int kMaxRowsPerBlock = 8 * kRowsPerWave;
+constexpr int kWaves = 8;                  // waves per bf16 workgroup
+constexpr int kStages = 4;                 // LDS ring depth (tiles)
+constexpr int kCombineRows = 32;           // query rows per combine workgroup
 constexpr int kMaxSplit = 8192;            // keys per split (block ids kept in LDS)
 
 struct AttnArgs {
@@ -53,13 +56,14 @@ struct AttnArgs {
   const uint16_t* v;
   void* out;
   int out_f32;
-  float* part;       // [items][kRowsPerBlock][D] unnormalised outputs
-  float* part_ml;    // [items][kRowsPerBlock][2]  (running max, running sum)
+  int rows_per_block;
+  float* part;       // [items][rows_per_block][D] unnormalised outputs
+  float* part_ml;    // [items][rows_per_block][2]  (running max, running sum)
 };
 
 // Per-request work counts, shared by the planner (host) and kernels (device).
-__host__ __device__ inline int attn_row_blocks(int n, int G) {
-  return (n * G + kRowsPerBlock - 1) / kRowsPerBlock;
+__host__ __device__ inline int attn_row_blocks(int n, int G, int rpb) {
+  return (n * G + rpb - 1) / rpb;
 }
 __host__ __device__ inline int attn_splits(int keys, int split) {
   return (keys + split - 1) / split;
@@ -76,7 +80,7 @@ SPEC_DEVICE void locate(int64_t x, const AttnArgs& a, int& b_out, int64_t& base_
     int64_t cnt = 0;
     if (b < a.B) {
       const int n = a.row_offsets[b + 1] - a.row_offsets[b];
-      const int nrb = attn_row_blocks(n, a.G);
+      const int nrb = attn_row_blocks(n, a.G, a.rows_per_block);
       cnt = (int64_t)a.addr.hkv * nrb;
       if (!kUnits) cnt *= attn_splits(a.prefix_len[b] + n, a.split);
     }
@@ -103,114 +107,214 @@ SPEC_DEVICE void locate(int64_t x, const AttnArgs& a, int& b_out, int64_t& base_
 
 
 typedef const __attribute__((address_space(1))) uint16_t* gptr_u16;
+typedef const __attribute__((address_space(1))) void* gptr_void;
+typedef __attribute__((address_space(3))) void* lptr_void;
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4* lptr_i16x4;
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef const __attribute__((address_space(1))) u32x4* gptr_u4;
 
-// 16-byte load through an explicitly global pointer (plain global_load, so
-// LDS waits in the loop do not also wait on the prefetch).
+// s_waitcnt immediate: vmcnt <= n, expcnt and lgkmcnt left at their maxima.
+#define SPEC_VMCNT(n) ((((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8)))
+// s_waitcnt immediate: lgkmcnt == 0, vmcnt and expcnt left at their maxima.
+#define SPEC_LGKMCNT0 0xc07f
+
+// 16-byte load through an explicitly global pointer.
 SPEC_DEVICE uint4 gload16(gptr_u16 p) {
   const u32x4 v = *(gptr_u4)p;
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
-// Element offset of absolute key kk: contiguous rows, or a paged block whose
-// id was staged in LDS (s_blk holds the split's block ids from block blk0).
-SPEC_DEVICE int64_t kv_key_offset(int kk, bool paged, const int* s_blk, int blk0, int64_t blk_stride,
-                                  int d) {
-  if (!paged) return (int64_t)kk * d;
-  return (int64_t)s_blk[(kk >> 4) - blk0] * blk_stride + (kk & 15) * d;
+// LDS layout of a 64-key tile (K or V), in 1 KB blocks: block
+// (chunk group cg = c / 4, row group rg = row / 16) sits at block index
+// cg * 4 + rg; inside it, 16-byte chunk c of key row `row` goes to slot
+// (c % 4) * 16 + ((row % 16) ^ (4 * (c % 4))).  One direct-to-LDS
+// instruction fills one block (16 rows x 64 contiguous bytes each); the
+// 16-byte K reads of 32 rows and the transposed V reads of 8 rows x 4
+// chunks both reach the minimum number of LDS cycles, and every read
+// address is a per-lane base plus a compile-time offset.
+SPEC_DEVICE int tile_slot_bytes(int row, int c) {
+  const int cl = c & 3;
+  return ((c >> 2) * 4 + (row >> 4)) * 1024 + (cl * 16 + ((row & 15) ^ (4 * cl))) * 16;
 }
 
-// Global -> registers for one 64-key tile: K as 16-byte row chunks, V as
-// 4 consecutive keys x 8 dims per thread (transposed when stored).
+// Issue the direct-to-LDS loads of one 64-key K and V tile; each wave issues
+// PER_WAVE of the tile's 1 KB blocks.  A block is 16 consecutive keys (one
+// paged KV block: the tile start is 64-aligned), so its base address is
+// uniform; lane l writes LDS slot l and loads the global chunk that the
+// layout above puts there.  Keys at or past the split end read its last key
+// instead (finite data; they are masked out of the softmax), which keeps
+// every access inside the cache rows the caller owns.
 template <int D>
-SPEC_DEVICE void load_kv_tile(gptr_u16 gk, gptr_u16 gv, int t0, int key_end, bool paged,
-                              const int* s_blk, int blk0, int64_t blk_stride, int tid,
-                              uint4 (&kreg)[kTileKeys * (D / 8) / 256],
-                              uint4 (&vreg)[((kTileKeys / 4) * (D / 8) + 255) / 256][4]) {
-  constexpr int DC = D / 8;
-  constexpr int KCH = kTileKeys * DC / 256;
-  constexpr int VUN = (kTileKeys / 4) * DC;
-  constexpr int VPT = (VUN + 255) / 256;
+SPEC_DEVICE void issue_tile(uint16_t* ks, uint16_t* vs, gptr_u16 gk, gptr_u16 gv, int t0,
+                            int key_end, bool paged, const int* s_blk, int blk0,
+                            int64_t blk_stride, int wave, int lane) {
+  constexpr int NB = D / 8;                  // 1 KB blocks per K (or V) tile
+  constexpr int PER_WAVE = 2 * NB / kWaves;
+  const int last = key_end - 1;
+  const int cl = lane >> 4;
+  const int rr = (lane & 15) ^ (4 * cl);
 #pragma unroll
-  for (int j = 0; j < KCH; ++j) {
-    const int c = tid + 256 * j;
-    const int kk = t0 + c / DC;
-    uint4 val = make_uint4(0, 0, 0, 0);
-    if (kk < key_end)
-      val = gload16(gk + kv_key_offset(kk, paged, s_blk, blk0, blk_stride, D) + (c % DC) * 8);
-    kreg[j] = val;
+  for (int j = 0; j < PER_WAVE; ++j) {
+    const int gi = wave * PER_WAVE + j;      // uniform
+    const bool isv = gi >= NB;
+    const int bi = isv ? gi - NB : gi;
+    const int grp = bi & 3;
+    const int gs = min(t0 + 16 * grp, last);
+    const int blk = gs >> 4;
+    const int64_t base =
+        paged ? (int64_t)__builtin_amdgcn_readfirstlane(s_blk[blk - blk0]) * blk_stride
+              : (int64_t)blk * (kBlock * D);
+    const int key = min(t0 + 16 * grp + rr, last);     // same 16-key block as gs
+    const int c = (bi >> 2) * 4 + cl;
+    const gptr_u16 src = (isv ? gv : gk) + base + ((key & 15) * D + c * 8);
+    uint16_t* dst = (isv ? vs : ks) + bi * 512;
+    __builtin_amdgcn_global_load_lds((gptr_void)src, (lptr_void)dst, 16, 0, 0);
   }
+}
+
+// Maximum / sum of the two values a query row holds in lanes l and l ^ 32
+// (v_permlane32_swap: each lane ends up with both halves' values).
+SPEC_DEVICE float row_pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+SPEC_DEVICE float row_pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Visibility of keys kb0 .. kb0+31 for one query row: a prefix key (< L)
+// always, tree key L + j when bit j of the row's ancestor mask is set, and
+// nothing at or past key_end.
+SPEC_DEVICE uint32_t visible_bits(int kb0, int L, int key_end, uint64_t mw0, uint64_t mw1,
+                                  uint64_t mw2, uint64_t mw3) {
+  const int r = kb0 - L;
+  uint64_t tree;
+  if (r >= 0) {
+    const int w = r >> 6, s = r & 63;
+    const uint64_t lo = (w == 0) ? mw0 : (w == 1) ? mw1 : (w == 2) ? mw2 : mw3;
+    const uint64_t hi = (w == 0) ? mw1 : (w == 1) ? mw2 : (w == 2) ? mw3 : 0ull;
+    tree = s ? ((lo >> s) | (hi << (64 - s))) : lo;
+  } else {
+    tree = (r <= -64) ? 0ull : (mw0 << (-r));
+  }
+  const int np = min(max(L - kb0, 0), 32);
+  const uint32_t pre = (np >= 32) ? 0xffffffffu : ((1u << np) - 1u);
+  const int nv = min(max(key_end - kb0, 0), 32);
+  const uint32_t lim = (nv >= 32) ? 0xffffffffu : ((1u << nv) - 1u);
+  return ((uint32_t)tree | pre) & lim;
+}
+
+// One 32-key half (hk) of a staged tile for one wave's 32 query rows:
+// S^T = K Q^T (a 32x32 block), mask, online softmax in the exp2 domain,
+// O^T += V^T P^T.  kb0 is the absolute index of the half's first key.
+template <int D>
+SPEC_DEVICE void compute_half(const uint16_t* ks, const uint16_t* vs, int hk, int kb0, int lane,
+                              int L, int key_end, float scale_log2, uint64_t mw0, uint64_t mw1,
+                              uint64_t mw2, uint64_t mw3, const bf16x8 (&qf)[D / 16],
+                              f32x16 (&acc)[D / 32], float& m_run, float& l_run) {
+  constexpr int NKS = D / 16;
+  constexpr int NDB = D / 32;
+  const int col = lane & 31, half = lane >> 5;
+  f32x16 sc;
 #pragma unroll
-  for (int j = 0; j < VPT; ++j) {
-    const int u = tid + 256 * j;
+  for (int e = 0; e < 16; ++e) sc[e] = 0.0f;
+  const int krow = hk * 32 + col;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int kk = t0 + (u / DC) * 4 + r;
-      uint4 val = make_uint4(0, 0, 0, 0);
-      if (u < VUN && kk < key_end)
-        val = gload16(gv + kv_key_offset(kk, paged, s_blk, blk0, blk_stride, D) + (u % DC) * 8);
-      vreg[j][r] = val;
+  for (int kk = 0; kk < NKS; ++kk) {
+    const bf16x8 kf = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const char*>(ks) +
+                                                       tile_slot_bytes(krow, kk * 2 + half));
+    sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], sc, 0, 0, 0);
+  }
+  // sc[e] is the score of key kb0 + half*4 + 8*(e/4) + e%4 (C layout of S^T).
+  if (kb0 + 32 > min(L, key_end)) {          // uniform: only tiles at the tree or split end
+    const uint32_t vis = visible_bits(kb0, L, key_end, mw0, mw1, mw2, mw3);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int i = half * 4 + 8 * (e >> 2) + (e & 3);
+      sc[e] = ((vis >> i) & 1u) ? sc[e] : -INFINITY;
+    }
+  }
+  float mx = sc[0];
+#pragma unroll
+  for (int e = 1; e < 16; ++e) mx = fmaxf(mx, sc[e]);
+  mx = row_pair_max(mx);
+  // scale_log2 > 0, so the row maximum commutes with the scaling.
+  const float m_new = fmaxf(m_run, mx * scale_log2);
+  // A row with no visible key yet keeps m = -inf; 0 as the reference then
+  // gives alpha = 0 and p = 0 without a divergent branch.
+  const float m_ref = (m_new == -INFINITY) ? 0.0f : m_new;
+  const float alpha = __builtin_amdgcn_exp2f(m_run - m_ref);
+  float rs = 0.0f;
+  bf16x8 pb[2];
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const float p = __builtin_amdgcn_exp2f(fmaf(sc[e], scale_log2, -m_ref));
+    rs += p;
+    pb[e >> 3][e & 7] = (__bf16)p;
+  }
+  rs = row_pair_sum(rs);
+  l_run = l_run * alpha + rs;
+  m_run = m_new;
+  if (__any(alpha != 1.0f)) {                // the running max moved for some row
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[db][e] *= alpha;
+  }
+  // V^T operand by transposed LDS reads: this lane supplies the address of 4
+  // dims of one key; lane 4q+c of each 16-lane group receives dim dbase+4q+c
+  // of 4 consecutive keys.  The k-slots of P^T (key half*4 + 8*(e/4) + e%4 of
+  // each 16-key step) and of V^T follow the same order.
+  const int grp = lane >> 4, j = lane & 15;
+  const int h = grp >> 1;
+  const int dsub = (grp & 1) * 16 + 4 * (j & 3);
+  const int ksub = j >> 2;
+  const char* vbase = reinterpret_cast<const char*>(vs);
+#pragma unroll
+  for (int mm = 0; mm < 2; ++mm) {
+    const int kb = hk * 32 + mm * 16 + h * 4;
+    const int ra = kb + ksub, rb = kb + 8 + ksub;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      const int dim = db * 32 + dsub;
+      const uint16_t* pa =
+          reinterpret_cast<const uint16_t*>(vbase + tile_slot_bytes(ra, dim >> 3)) + (dim & 7);
+      const uint16_t* pbp =
+          reinterpret_cast<const uint16_t*>(vbase + tile_slot_bytes(rb, dim >> 3)) + (dim & 7);
+      const i16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lptr_i16x4)pa);
+      const i16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lptr_i16x4)pbp);
+      const bf16x8 vf = __builtin_bit_cast(
+          bf16x8, make_uint4(__builtin_bit_cast(uint2, va).x, __builtin_bit_cast(uint2, va).y,
+                             __builtin_bit_cast(uint2, vb).x, __builtin_bit_cast(uint2, vb).y));
+      acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[mm], acc[db], 0, 0, 0);
     }
   }
 }
 
-// Registers -> LDS: K row-major (stride D + 8), V transposed to [dim][key].
+// Main kernel: one workgroup of 8 waves per (request, KV head, block of up
+// to 256 query rows, key split).  Query rows form groups of 32 (one wave's
+// MFMA columns).  With at most 4 groups, two waves share a group and each
+// takes one 32-key half of every tile (their partial softmax states merge at
+// the end), so small trees still keep every SIMD busy.  K/V tiles of 64 keys
+// stream through a 4-stage LDS ring filled by direct-to-LDS loads, three
+// tiles ahead of the compute.
 template <int D>
-SPEC_DEVICE void store_kv_tile(uint16_t* ks, uint16_t* vt, int tid,
-                               const uint4 (&kreg)[kTileKeys * (D / 8) / 256],
-                               const uint4 (&vreg)[((kTileKeys / 4) * (D / 8) + 255) / 256][4]) {
-  constexpr int DC = D / 8;
-  constexpr int KS = D + 8;
-  constexpr int KCH = kTileKeys * DC / 256;
-  constexpr int VUN = (kTileKeys / 4) * DC;
-  constexpr int VPT = (VUN + 255) / 256;
-#pragma unroll
-  for (int j = 0; j < KCH; ++j) {
-    const int c = tid + 256 * j;
-    *reinterpret_cast<uint4*>(&ks[(c / DC) * KS + (c % DC) * 8]) = kreg[j];
-  }
-#pragma unroll
-  for (int j = 0; j < VPT; ++j) {
-    const int u = tid + 256 * j;
-    if (u < VUN) {
-      const int kg = u / DC, dc = u % DC;
-      const uint32_t w0[4] = {vreg[j][0].x, vreg[j][0].y, vreg[j][0].z, vreg[j][0].w};
-      const uint32_t w1[4] = {vreg[j][1].x, vreg[j][1].y, vreg[j][1].z, vreg[j][1].w};
-      const uint32_t w2[4] = {vreg[j][2].x, vreg[j][2].y, vreg[j][2].z, vreg[j][2].w};
-      const uint32_t w3[4] = {vreg[j][3].x, vreg[j][3].y, vreg[j][3].z, vreg[j][3].w};
-#pragma unroll
-      for (int i2 = 0; i2 < 4; ++i2) {
-        // dims dc*8 + 2*i2 (low halves) and dc*8 + 2*i2 + 1 (high halves)
-        const uint2 lo = make_uint2((w0[i2] & 0xffffu) | (w1[i2] << 16),
-                                    (w2[i2] & 0xffffu) | (w3[i2] << 16));
-        const uint2 hi = make_uint2((w0[i2] >> 16) | (w1[i2] & 0xffff0000u),
-                                    (w2[i2] >> 16) | (w3[i2] & 0xffff0000u));
-        const int d0 = dc * 8 + 2 * i2;
-        *reinterpret_cast<uint2*>(&vt[d0 * kVtStride + kg * 4]) = lo;
-        *reinterpret_cast<uint2*>(&vt[(d0 + 1) * kVtStride + kg * 4]) = hi;
-      }
-    }
-  }
-}
-
-template <int D>
-__global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnArgs a) {
-  constexpr int KS = D + 8;                 // bf16 per K row in LDS
-  constexpr int DC = D / 8;                 // 16-byte chunks per row
-  constexpr int KCH = kTileKeys * DC / 256; // K chunks per thread per tile
-  constexpr int VUN = (kTileKeys / 4) * DC; // V transpose units per tile
-  constexpr int VPT = (VUN + 255) / 256;    // V units per thread
-  constexpr int NKS = D / 16;               // MFMA k-steps for q.k
-  constexpr int NDB = D / 32;               // 32-dim output blocks
-  __shared__ __attribute__((aligned(16))) uint16_t ks_lds[2][kTileKeys * KS];
-  __shared__ __attribute__((aligned(16))) uint16_t vt_lds[2][D * kVtStride];
+__global__ void __launch_bounds__(kWaves * 64, 1) attn_bf16_kernel(AttnArgs a) {
+  constexpr int NKS = D / 16;
+  constexpr int NDB = D / 32;
+  constexpr int ROWS = kWaves * kRowsPerWave;
+  constexpr int TILE = kTileKeys * D;                 // bf16 per K (or V) tile
+  constexpr int PER_WAVE = 2 * (D / 8) / kWaves;      // DMA blocks per wave per tile
+  static_assert(PER_WAVE * 3 < 64, "vmcnt range");
+  __shared__ __attribute__((aligned(16))) uint16_t k0[TILE], k1[TILE], k2[TILE], k3[TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t v0[TILE], v1[TILE], v2[TILE], v3[TILE];
+  __shared__ int s_blk[kMaxSplit / kBlock + 2];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int col = lane & 31;     // query row within the wave tile
-  const int half = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
   int b;
   int64_t ibase;
@@ -219,39 +323,48 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnArgs a) {
   if (b < 0) return;
   const int o = a.row_offsets[b];
   const int n = a.row_offsets[b + 1] - o;
-  const int L = a.prefix_len[b];
+  const int L = __builtin_amdgcn_readfirstlane(a.prefix_len[b]);
   const int total_keys = L + n;
-  const int nrb = attn_row_blocks(n, a.G);
+  const int nrb = attn_row_blocks(n, a.G, ROWS);
   const int ns = attn_splits(total_keys, a.split);
   const int64_t local = item - ibase;
   const int s = (int)(local % ns);
   const int rb = (int)((local / ns) % nrb);
   const int kvh = (int)(local / ((int64_t)ns * nrb));
-  const int key_begin = s * a.split;
-  const int key_end = min(key_begin + a.split, total_keys);
+  const int key_begin = __builtin_amdgcn_readfirstlane(s * a.split);
+  const int key_end = __builtin_amdgcn_readfirstlane(min(key_begin + a.split, total_keys));
   const int M = n * a.G;
 
-  // ---- this lane's query row --------------------------------------------
-  const int row = rb * kRowsPerBlock + wave * kRowsPerWave + col;
-  const bool row_ok = row < M;
-  const bool wave_active = rb * kRowsPerBlock + wave * kRowsPerWave < M;
+  const int groups = (min(ROWS, M - rb * ROWS) + kRowsPerWave - 1) / kRowsPerWave;
+  const bool pair = groups <= kWaves / 2;
+  const int g = pair ? (wave >> 1) : wave;
+  const int h_lo = pair ? (wave & 1) : 0;
+  const int h_hi = pair ? h_lo + 1 : 2;
+  const bool wave_active = g < groups;
+
+  const int col = lane & 31, half = lane >> 5;
+  const int row = rb * ROWS + g * kRowsPerWave + col;
+  const bool row_ok = wave_active && row < M;
   const int ti = row_ok ? row / a.G : 0;
   const int hh = kvh * a.G + (row_ok ? row % a.G : 0);
   bf16x8 qf[NKS];
-  uint64_t mw[kMaxWords] = {0, 0, 0, 0};
+  uint64_t mw0 = 0, mw1 = 0, mw2 = 0, mw3 = 0;
   if (row_ok) {
     const uint16_t* qp = a.q + ((int64_t)(o + ti) * a.hq + hh) * D + half * 8;
 #pragma unroll
     for (int kk = 0; kk < NKS; ++kk)
       qf[kk] = __builtin_bit_cast(bf16x8, gload16((gptr_u16)(qp + kk * 16)));
-    for (int w = 0; w < a.words; ++w) mw[w] = a.mask[(int64_t)(o + ti) * a.words + w];
+    const uint64_t* mrow = a.mask + (int64_t)(o + ti) * a.words;
+    mw0 = mrow[0];
+    if (a.words > 1) mw1 = mrow[1];
+    if (a.words > 2) mw2 = mrow[2];
+    if (a.words > 3) mw3 = mrow[3];
   } else {
 #pragma unroll
     for (int kk = 0; kk < NKS; ++kk)
 #pragma unroll
       for (int e = 0; e < 8; ++e) qf[kk][e] = (__bf16)0.0f;
   }
-
   f32x16 acc[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
@@ -260,16 +373,14 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnArgs a) {
   float m_run = -INFINITY;
   float l_run = 0.0f;
 
-  // ---- tile staging -----------------------------------------------------
-  // Paged caches: the block ids of this split are read once into LDS so the
-  // tile loads below carry no dependent global lookups.
-  __shared__ int s_blk[kMaxSplit / kBlock + 2];
+  // Paged caches: the split's block ids go to LDS once.
   const int blk0 = key_begin >> 4;
+  const bool paged = a.addr.paged;
   const uint16_t* kbase;
   const uint16_t* vbase;
-  if (a.addr.paged) {
+  if (paged) {
     const int nblk = ((key_end + kBlock - 1) >> 4) - blk0;
-    for (int i = tid; i < nblk; i += 256)
+    for (int i = tid; i < nblk; i += kWaves * 64)
       s_blk[i] = a.addr.block_table[(int64_t)b * a.addr.mbps + blk0 + i];
     kbase = a.k + (int64_t)kvh * kBlock * D;
     vbase = a.v + (int64_t)kvh * kBlock * D;
@@ -279,102 +390,88 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnArgs a) {
     vbase = a.v + off;
   }
   const int64_t blk_stride = (int64_t)a.addr.hkv * kBlock * D;
-  const bool paged = a.addr.paged;
-  const gptr_u16 gk = (const gptr_u16)kbase;
-  const gptr_u16 gv = (const gptr_u16)vbase;
-  uint4 kreg[KCH];
-  uint4 vreg[VPT][4];
+  const gptr_u16 gk = (gptr_u16)kbase;
+  const gptr_u16 gv = (gptr_u16)vbase;
+  __syncthreads();
 
+  // Ring of 4 stages: tile t lives in stage t % 4.  Step t waits for this
+  // wave's loads of tile t (tiles t+1 and t+2 stay in flight), meets the other
+  // waves -- after which all of them are done with tile t-1 -- refills that
+  // tile's stage with tile t+3, and computes tile t.
   const int ntiles = (key_end - key_begin + kTileKeys - 1) / kTileKeys;
-  __syncthreads();
-  load_kv_tile<D>(gk, gv, key_begin, key_end, paged, s_blk, blk0, blk_stride, tid, kreg, vreg);
-  store_kv_tile<D>(ks_lds[0], vt_lds[0], tid, kreg, vreg);
-  __syncthreads();
+  issue_tile<D>(k0, v0, gk, gv, key_begin, key_end, paged, s_blk, blk0, blk_stride, wave, lane);
+  issue_tile<D>(k1, v1, gk, gv, key_begin + kTileKeys, key_end, paged, s_blk, blk0, blk_stride,
+                wave, lane);
+  issue_tile<D>(k2, v2, gk, gv, key_begin + 2 * kTileKeys, key_end, paged, s_blk, blk0,
+                blk_stride, wave, lane);
 
-  for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
-    const int t0 = key_begin + t * kTileKeys;
-    if (t + 1 < ntiles)
-      load_kv_tile<D>(gk, gv, t0 + kTileKeys, key_end, paged, s_blk, blk0, blk_stride, tid, kreg, vreg);
-
-    if (wave_active) {
-      // S^T (64 keys x 32 rows) as two 32x32 blocks.
-      f32x16 sc[2];
-#pragma unroll
-      for (int kh = 0; kh < 2; ++kh) {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) sc[kh][e] = 0.0f;
-        const uint16_t* kp = &ks_lds[buf][(kh * 32 + col) * KS + half * 8];
-#pragma unroll
-        for (int kk = 0; kk < NKS; ++kk) {
-          const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kp + kk * 16);
-          sc[kh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], sc[kh], 0, 0, 0);
-        }
-      }
-      // scale, mask, running max
-      const bool full = (t0 + kTileKeys <= L) && (t0 + kTileKeys <= key_end);
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          float x = sc[kh][e] * a.scale_log2;
-          if (!full) {
-            const int kk = t0 + kh * 32 + half * 4 + 8 * (e >> 2) + (e & 3);
-            bool vis = kk < key_end;
-            if (vis && kk >= L) {
-              const int j = kk - L;
-              vis = (mw[j >> 6] >> (j & 63)) & 1ull;
-            }
-            x = vis ? x : -INFINITY;
-          }
-          sc[kh][e] = x;
-          mx = fmaxf(mx, x);
-        }
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float m_new = fmaxf(m_run, mx);
-      // A row with no visible key yet keeps m = -inf; using 0 as the
-      // reference then gives alpha = 0 and p = 0 without a (divergent) branch.
-      const float m_ref = (m_new == -INFINITY) ? 0.0f : m_new;
-      const float alpha = exp2f(m_run - m_ref);
-      float rs = 0.0f;
-      bf16x8 pb[2][2];
-#pragma unroll
-      for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const float p = exp2f(sc[kh][e] - m_ref);
-          rs += p;
-          pb[kh][e >> 3][e & 7] = (__bf16)p;
-        }
-      rs += __shfl_xor(rs, 32, 64);
-      l_run = l_run * alpha + rs;
-      m_run = m_new;
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) acc[db][e] *= alpha;
-      // O^T += V^T P^T over the 64 keys: 2 halves x 2 16-key steps
-#pragma unroll
-      for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-        for (int mm = 0; mm < 2; ++mm) {
-          const int kb = kh * 32 + mm * 16 + half * 4;
-#pragma unroll
-          for (int db = 0; db < NDB; ++db) {
-            const uint16_t* vp = &vt_lds[buf][(db * 32 + col) * kVtStride + kb];
-            const uint2 lo = *reinterpret_cast<const uint2*>(vp);
-            const uint2 hi = *reinterpret_cast<const uint2*>(vp + 8);
-            const bf16x8 vf = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
-            acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[kh][mm], acc[db], 0, 0, 0);
-          }
-        }
-    }
-    if (t + 1 < ntiles) store_kv_tile<D>(ks_lds[buf ^ 1], vt_lds[buf ^ 1], tid, kreg, vreg);
-    __syncthreads();
+#define SPEC_ATTN_STEP(KC, VC, KN, VN, T)                                                       \
+  {                                                                                              \
+    const int t0_ = key_begin + (T) * kTileKeys;                                                 \
+    __builtin_amdgcn_s_waitcnt(SPEC_VMCNT(2 * PER_WAVE));                                        \
+    __builtin_amdgcn_s_barrier();                                                                \
+    issue_tile<D>(KN, VN, gk, gv, t0_ + 3 * kTileKeys, key_end, paged, s_blk, blk0, blk_stride,  \
+                  wave, lane);                                                                   \
+    if (wave_active) {                                                                           \
+      for (int hk = h_lo; hk < h_hi; ++hk)                                                       \
+        compute_half<D>(KC, VC, hk, t0_ + 32 * hk, lane, L, key_end, a.scale_log2, mw0, mw1,     \
+                        mw2, mw3, qf, acc, m_run, l_run);                                        \
+    }                                                                                            \
+    __builtin_amdgcn_s_waitcnt(SPEC_LGKMCNT0);                                                   \
   }
 
+  for (int t = 0; t < ntiles; t += kStages) {
+    SPEC_ATTN_STEP(k0, v0, k3, v3, t);
+    if (t + 1 >= ntiles) break;
+    SPEC_ATTN_STEP(k1, v1, k0, v0, t + 1);
+    if (t + 2 >= ntiles) break;
+    SPEC_ATTN_STEP(k2, v2, k1, v1, t + 2);
+    if (t + 3 >= ntiles) break;
+    SPEC_ATTN_STEP(k3, v3, k2, v2, t + 3);
+  }
+#undef SPEC_ATTN_STEP
+  // Drain the loads still in flight (clamped tail tiles); then the ring is
+  // free for the merge of the two key halves of each row group.
+  __builtin_amdgcn_s_waitcnt(SPEC_VMCNT(0));
+  __syncthreads();
+  constexpr int NV4 = NDB * 4;                         // float4 per lane of acc
+  if (pair && wave_active && (wave & 1)) {
+    uint16_t* slot = (g == 0) ? k0 : (g == 1) ? k1 : (g == 2) ? k2 : k3;
+    float4* xs = reinterpret_cast<float4*>(slot);
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int ai = 0; ai < 4; ++ai)
+        xs[(db * 4 + ai) * 64 + lane] = make_float4(acc[db][4 * ai], acc[db][4 * ai + 1],
+                                                    acc[db][4 * ai + 2], acc[db][4 * ai + 3]);
+    float2* ml = reinterpret_cast<float2*>(v0) + g * 64 + lane;
+    *ml = make_float2(m_run, l_run);
+  }
+  static_assert(NV4 * 64 * 16 <= TILE * 2, "merge slot size");
+  __syncthreads();
+  if (pair && (wave & 1)) return;
   if (!row_ok) return;
+  if (pair) {
+    const uint16_t* slot = (g == 0) ? k0 : (g == 1) ? k1 : (g == 2) ? k2 : k3;
+    const float4* xs = reinterpret_cast<const float4*>(slot);
+    const float2 ml = reinterpret_cast<const float2*>(v0)[g * 64 + lane];
+    const float m_new = fmaxf(m_run, ml.x);
+    const float m_ref = (m_new == -INFINITY) ? 0.0f : m_new;
+    const float a0 = __builtin_amdgcn_exp2f(m_run - m_ref);
+    const float a1 = __builtin_amdgcn_exp2f(ml.x - m_ref);
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int ai = 0; ai < 4; ++ai) {
+        const float4 x = xs[(db * 4 + ai) * 64 + lane];
+        acc[db][4 * ai] = acc[db][4 * ai] * a0 + x.x * a1;
+        acc[db][4 * ai + 1] = acc[db][4 * ai + 1] * a0 + x.y * a1;
+        acc[db][4 * ai + 2] = acc[db][4 * ai + 2] * a0 + x.z * a1;
+        acc[db][4 * ai + 3] = acc[db][4 * ai + 3] * a0 + x.w * a1;
+      }
+    l_run = l_run * a0 + ml.y * a1;
+    m_run = m_new;
+  }
   // acc[db][4*ai + c] holds output dim db*32 + half*4 + 8*ai + c of this row.
   if (ns == 1) {
     const float inv = 1.0f / l_run;
@@ -384,20 +481,20 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
       for (int ai = 0; ai < 4; ++ai) {
         const int d0 = db * 32 + half * 4 + 8 * ai;
-        const float v0 = acc[db][4 * ai] * inv, v1 = acc[db][4 * ai + 1] * inv;
-        const float v2 = acc[db][4 * ai + 2] * inv, v3 = acc[db][4 * ai + 3] * inv;
+        const float v0f = acc[db][4 * ai] * inv, v1f = acc[db][4 * ai + 1] * inv;
+        const float v2f = acc[db][4 * ai + 2] * inv, v3f = acc[db][4 * ai + 3] * inv;
         if (a.out_f32) {
-          *reinterpret_cast<float4*>((float*)a.out + obase + d0) = make_float4(v0, v1, v2, v3);
+          *reinterpret_cast<float4*>((float*)a.out + obase + d0) = make_float4(v0f, v1f, v2f, v3f);
         } else {
           uint2 pk;
-          pk.x = f32_to_bf16_bits(v0) | ((uint32_t)f32_to_bf16_bits(v1) << 16);
-          pk.y = f32_to_bf16_bits(v2) | ((uint32_t)f32_to_bf16_bits(v3) << 16);
+          pk.x = f32_to_bf16_bits(v0f) | ((uint32_t)f32_to_bf16_bits(v1f) << 16);
+          pk.y = f32_to_bf16_bits(v2f) | ((uint32_t)f32_to_bf16_bits(v3f) << 16);
           *reinterpret_cast<uint2*>((uint16_t*)a.out + obase + d0) = pk;
         }
       }
   } else {
-    const int r_in_block = wave * kRowsPerWave + col;
-    float* pp = a.part + (item * kRowsPerBlock + r_in_block) * D;
+    const int r_in_block = g * kRowsPerWave + col;
+    float* pp = a.part + (item * ROWS + r_in_block) * D;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -407,71 +504,98 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnArgs a) {
             make_float4(acc[db][4 * ai], acc[db][4 * ai + 1], acc[db][4 * ai + 2], acc[db][4 * ai + 3]);
       }
     if (half == 0) {
-      float* ml = a.part_ml + (item * kRowsPerBlock + r_in_block) * 2;
+      float* ml = a.part_ml + (item * ROWS + r_in_block) * 2;
       ml[0] = m_run;
       ml[1] = l_run;
     }
   }
 }
 
-// Merge split partials of one (request, KV head, row block).
+// Merge split partials.  One workgroup per 32 query rows of one (request, KV
+// head, row block): 8 threads per row find the row's maximum and weighted sum
+// over the splits, then each thread accumulates float4 columns of four rows,
+// split after split (coalesced 512-byte rows of partials).
 template <int D>
 __global__ void __launch_bounds__(256) attn_combine_kernel(AttnArgs a) {
+  constexpr int ROWS = kWaves * kRowsPerWave;
+  constexpr int CHUNKS = ROWS / kCombineRows;
+  constexpr int C4 = D / 4;                        // float4 per row
+  constexpr int RPI = 256 / C4;                    // rows per pass of the block
+  __shared__ float s_m[kCombineRows], s_inv[kCombineRows];
+  const int64_t unit = blockIdx.x / CHUNKS;
+  const int chunk = blockIdx.x % CHUNKS;
   int b;
   int64_t ubase;
-  locate<true>((int64_t)blockIdx.x, a, b, ubase);
+  locate<true>(unit, a, b, ubase);
   if (b < 0) return;
   const int o = a.row_offsets[b];
   const int n = a.row_offsets[b + 1] - o;
   const int L = a.prefix_len[b];
   const int ns = attn_splits(L + n, a.split);
   if (ns == 1) return;
-  const int nrb = attn_row_blocks(n, a.G);
-  const int64_t u = blockIdx.x - ubase;            // kvh * nrb + rb
+  const int nrb = attn_row_blocks(n, a.G, ROWS);
+  const int M = n * a.G;
+  const int64_t u = unit - ubase;                  // kvh * nrb + rb
   const int rb = (int)(u % nrb);
   const int kvh = (int)(u / nrb);
-  // first item of this request: same prefix order as the main kernel
-  int bb;
-  int64_t ibase = 0;
-  {
-    // items of earlier requests = sum over b' < b; recover via locate on units
-    // is not enough, so accumulate directly (wave-parallel).
-    const int lane = threadIdx.x & 63;
-    int64_t acc = 0;
-    for (int base = 0; base < b; base += 64) {
-      const int bq = base + lane;
-      int64_t cnt = 0;
-      if (bq < b) {
-        const int nq = a.row_offsets[bq + 1] - a.row_offsets[bq];
-        cnt = (int64_t)a.addr.hkv * attn_row_blocks(nq, a.G) * attn_splits(a.prefix_len[bq] + nq, a.split);
-      }
-      acc += cnt;
+  const int r0 = chunk * kCombineRows;             // first row (within the block)
+  const int rows = min(kCombineRows, min(ROWS, M - rb * ROWS) - r0);
+  if (rows <= 0) return;
+  // first item of request b: items of all earlier requests
+  const int lane = threadIdx.x & 63;
+  int64_t cnt = 0;
+  for (int base = 0; base < b; base += 64) {
+    const int bq = base + lane;
+    if (bq < b) {
+      const int nq = a.row_offsets[bq + 1] - a.row_offsets[bq];
+      cnt += (int64_t)a.addr.hkv * attn_row_blocks(nq, a.G, ROWS) *
+             attn_splits(a.prefix_len[bq] + nq, a.split);
     }
-    ibase = wave_sum(acc);
-    bb = b;
   }
-  (void)bb;
-  const int64_t item0 = ibase + u * ns;            // split 0 of this unit
-  const int M = n * a.G;
-  const int rows = min(kRowsPerBlock, M - rb * kRowsPerBlock);
-  constexpr int C4 = D / 4;
-  for (int w = threadIdx.x; w < rows * C4; w += blockDim.x) {
-    const int r = w / C4, c4 = w % C4;
-    float mmax = -INFINITY;
-    for (int s = 0; s < ns; ++s)
-      mmax = fmaxf(mmax, a.part_ml[((item0 + s) * kRowsPerBlock + r) * 2]);
-    float lsum = 0.0f;
+  const int64_t item0 = wave_sum(cnt) + u * ns;    // split 0 of this unit
+  const float2* ml = reinterpret_cast<const float2*>(a.part_ml);
+
+  {  // per-row maximum and weighted sum: 8 threads per row, splits strided
+    const int r = threadIdx.x >> 3, j = threadIdx.x & 7;
+    float mx = -INFINITY;
+    if (r < rows)
+      for (int s = j; s < ns; s += 8) mx = fmaxf(mx, ml[(item0 + s) * ROWS + r0 + r].x);
+    mx = fmaxf(mx, __shfl_xor(mx, 1, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 2, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 4, 64));
+    const float ref = (mx == -INFINITY) ? 0.0f : mx;
+    float l = 0.0f;
+    if (r < rows)
+      for (int s = j; s < ns; s += 8) {
+        const float2 v = ml[(item0 + s) * ROWS + r0 + r];
+        l += v.y * __builtin_amdgcn_exp2f(v.x - ref);
+      }
+    l += __shfl_xor(l, 1, 64);
+    l += __shfl_xor(l, 2, 64);
+    l += __shfl_xor(l, 4, 64);
+    if (j == 0 && r < kCombineRows) {
+      s_m[r] = ref;
+      s_inv[r] = 1.0f / l;
+    }
+  }
+  __syncthreads();
+  const int c4 = threadIdx.x % C4;
+  const int rsub = threadIdx.x / C4;
+#pragma unroll
+  for (int rp = 0; rp < kCombineRows / RPI; ++rp) {
+    const int r = rp * RPI + rsub;
+    if (r >= rows) break;
+    const float ref = s_m[r];
     float4 accv = make_float4(0.f, 0.f, 0.f, 0.f);
+    const int64_t prow = (item0 * ROWS + r0 + r);
     for (int s = 0; s < ns; ++s) {
-      const float* ml = a.part_ml + ((item0 + s) * kRowsPerBlock + r) * 2;
-      const float wgt = (ml[0] == -INFINITY) ? 0.0f : exp2f(ml[0] - mmax);
-      lsum += ml[1] * wgt;
-      const float4 pv = *reinterpret_cast<const float4*>(
-          a.part + ((item0 + s) * kRowsPerBlock + r) * D + c4 * 4);
+      const int64_t pr = prow + (int64_t)s * ROWS;
+      const float wgt = __builtin_amdgcn_exp2f(ml[pr].x - ref);
+      const float4 pv = *reinterpret_cast<const float4*>(a.part + pr * D + c4 * 4);
       accv.x += pv.x * wgt; accv.y += pv.y * wgt; accv.z += pv.z * wgt; accv.w += pv.w * wgt;
     }
-    const float inv = 1.0f / lsum;
-    const int grow = rb * kRowsPerBlock + r;
+    const float inv = s_inv[r];
+    const int grow = rb * ROWS + r0 + r;
     const int ti = grow / a.G;
     const int hh = kvh * a.G + grow % a.G;
     const int64_t obase = ((int64_t)(o + ti) * a.hq + hh) * D + c4 * 4;
@@ -576,21 +700,28 @@ attn_f32_kernel(const int32_t* __restrict__ row_offsets, const int32_t* __restri
 AttnPlan plan_attention(int B, const int32_t* row_offsets_h, const int32_t* prefix_len_h, int hq,
                         int hkv) {
   const int G = hq / hkv;
+  int max_rows = 0;
+  for (int b = 0; b < B; ++b)
+    max_rows = std::max(max_rows, (row_offsets_h[b + 1] - row_offsets_h[b]) * G);
+  AttnPlan p;
+  // 8 waves of 32 query rows: most (request, KV head) pairs fit in one
+  // workgroup, so every KV tile is read once.
+  p.rows_per_block = kWaves * kRowsPerWave;
+  (void)max_rows;
   int64_t work = 0, units = 0;
   for (int b = 0; b < B; ++b) {
     const int n = row_offsets_h[b + 1] - row_offsets_h[b];
-    const int nrb = attn_row_blocks(n, G);
+    const int nrb = attn_row_blocks(n, G, p.rows_per_block);
     units += (int64_t)hkv * nrb;
     work += (int64_t)hkv * nrb * (prefix_len_h[b] + n);
   }
-  // Aim at ~4 workgroups per CU (256 CUs), splits of at least 256 keys.
+  // One workgroup per CU at a time: aim at ~4 workgroups per CU (256 CUs),
+  // splits of at least 256 keys.
   const int64_t target = 1024;
   int64_t split = (work + target - 1) / target;
   split = ((split + kTileKeys - 1) / kTileKeys) * kTileKeys;
   if (split < 256) split = 256;
   if (split > kMaxSplit) split = kMaxSplit;
-  AttnPlan p;
-  p.rows_per_block = kRowsPerBlock;
   p.split_keys = (int)split;
   p.items = 0;
   p.partial_items = 0;
@@ -598,7 +729,7 @@ AttnPlan plan_attention(int B, const int32_t* row_offsets_h, const int32_t* pref
   for (int b = 0; b < B; ++b) {
     const int n = row_offsets_h[b + 1] - row_offsets_h[b];
     const int ns = attn_splits(prefix_len_h[b] + n, p.split_keys);
-    const int64_t it = (int64_t)hkv * attn_row_blocks(n, G) * ns;
+    const int64_t it = (int64_t)hkv * attn_row_blocks(n, G, p.rows_per_block) * ns;
     p.items += it;
     if (ns > 1) p.partial_items += it;
   }
@@ -607,7 +738,7 @@ AttnPlan plan_attention(int B, const int32_t* row_offsets_h, const int32_t* pref
 
 size_t attention_workspace_bytes(const AttnPlan& plan, int d) {
   if (plan.partial_items == 0) return 256;
-  return (size_t)plan.items * kRowsPerBlock * (d + 2) * sizeof(float) + 256;
+  return (size_t)plan.items * plan.rows_per_block * (d + 2) * sizeof(float) + 256;
 }
 
 hipError_t launch_attention_bf16(const LaunchCtx& cx, const AttnPlan& plan, const KvAddr& addr,
@@ -630,17 +761,20 @@ hipError_t launch_attention_bf16(const LaunchCtx& cx, const AttnPlan& plan, cons
   a.v = (const uint16_t*)v_cache;
   a.out = out;
   a.out_f32 = out_f32;
+  a.rows_per_block = plan.rows_per_block;
   a.part = (float*)workspace;
-  a.part_ml = a.part + (size_t)plan.items * kRowsPerBlock * addr.d;
+  a.part_ml = a.part + (size_t)plan.items * plan.rows_per_block * addr.d;
   if (plan.items > 0x7fffffff) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)plan.items);
+  if (plan.rows_per_block != kWaves * kRowsPerWave) return hipErrorInvalidValue;
   if (addr.d == 128) {
-    hipLaunchKernelGGL(attn_bf16_kernel<128>, dim3((unsigned)plan.items), dim3(256), 0, cx.stream, a);
+    hipLaunchKernelGGL(attn_bf16_kernel<128>, grid, dim3(kWaves * 64), 0, cx.stream, a);
     if (plan.partial_items)
-      hipLaunchKernelGGL(attn_combine_kernel<128>, dim3((unsigned)plan.units), dim3(256), 0, cx.stream, a);
+      hipLaunchKernelGGL(attn_combine_kernel<128>, dim3((unsigned)(plan.units * (kWaves * kRowsPerWave / kCombineRows))), dim3(256), 0, cx.stream, a);
   } else {
-    hipLaunchKernelGGL(attn_bf16_kernel<64>, dim3((unsigned)plan.items), dim3(256), 0, cx.stream, a);
+    hipLaunchKernelGGL(attn_bf16_kernel<64>, grid, dim3(kWaves * 64), 0, cx.stream, a);
     if (plan.partial_items)
-      hipLaunchKernelGGL(attn_combine_kernel<64>, dim3((unsigned)plan.units), dim3(256), 0, cx.stream, a);
+      hipLaunchKernelGGL(attn_combine_kernel<64>, dim3((unsigned)(plan.units * (kWaves * kRowsPerWave / kCombineRows))), dim3(256), 0, cx.stream, a);
   }
   return hipGetLastError();
 }
