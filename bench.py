@@ -55,6 +55,30 @@ def algorithmic(w):
     return a_attn, f_attn, a_acc
 
 
+def measured_traffic(config):
+    """HBM bytes per attention call from the committed counter summary.
+
+    profiles/attn_<config>_traffic.json holds FETCH_SIZE + WRITE_SIZE of the
+    attention kernels (two rocprofv3 --pmc runs, calibrated against a 1 GiB
+    device copy) and the sha256 of the sources they were built from.  When
+    those sources have changed since, the counters describe another kernel
+    and the traffic is reported as null.
+    """
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"attn_{config}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    h = hashlib.sha256()
+    for src in rec["sources"]:
+        with open(os.path.join(ROOT, src), "rb") as f:
+            h.update(f.read())
+    if h.hexdigest() != rec["sources_sha256"]:
+        return None
+    return rec["traffic_bytes_per_call"]
+
+
 def cpu_baseline(w, budget_s):
     """Time the oracle on the first requests of the workload (bounded)."""
     import numpy as np
@@ -176,7 +200,8 @@ def main():
                    "kv_tokens": int(w.prefix_len.sum()) + R, "vocab": w.V},
         "roofline": {"bound": "hbm", "kernel": "spec_tree_attn_verify (split-KV main + combine)",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(args.config),
+                     "traffic_unit": "HBM bytes per call (rocprofv3 FETCH_SIZE + WRITE_SIZE, calibrated)",
                      "algorithmic_bytes": a_attn, "avg_launch_ms": per["attention"],
                      "mfma_tflops": f_attn / t_attn / 1e12,
                      "mfma_frac": f_attn / t_attn / 1e12 / BF16_PEAK_TFLOPS},

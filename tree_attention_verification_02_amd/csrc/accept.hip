@@ -20,7 +20,7 @@
 //    first argmax, and the child probabilities P_u(x_c), Q_u(x_c).  Draft rows
 //    of leaves are never read.
 //  * accept_walk (cooperative launch): S workgroups per request.  Each pass
-//    is split over the S workgroups by 1024-element segments; segment sums go
+//    is split over the S workgroups by 4096-element segments; segment sums go
 //    to global memory and the S workgroups meet at a per-request counter
 //    barrier (bounded spin).  Every workgroup then sums the segments in the
 //    same order and replays the same scalar decisions, so no further
