@@ -184,6 +184,11 @@ size_t spec_tree_attn_workspace_bytes(const spec_batch* batch, const spec_kv* kv
   if (kv->dtype == SPEC_F32) return 256;
   const spec::AttnPlan p = spec::plan_attention(batch->batch, batch->row_offsets_h, batch->prefix_len_h,
                                                 num_q_heads, kv->num_kv_heads);
+  if (p.items < 0) {
+    fail(SPEC_ERR_UNSUPPORTED, "a request holds more than %lld keys",
+         (long long)spec::kMaxAttnKeys);
+    return 0;
+  }
   return spec::attention_workspace_bytes(p, kv->head_dim);
 }
 
@@ -212,6 +217,8 @@ spec_status spec_tree_attn_verify(const spec_batch* batch, const spec_kv* kv, co
   }
   const spec::AttnPlan p = spec::plan_attention(batch->batch, batch->row_offsets_h, batch->prefix_len_h,
                                                 num_q_heads, kv->num_kv_heads);
+  if (p.items < 0)
+    return fail(SPEC_ERR_UNSUPPORTED, "a request holds more than %lld keys", (long long)spec::kMaxAttnKeys);
   const size_t need = spec::attention_workspace_bytes(p, kv->head_dim);
   if (!workspace_d || workspace_bytes < need)
     return fail(SPEC_ERR_WORKSPACE, "attention workspace %zu bytes < required %zu", workspace_bytes, need);

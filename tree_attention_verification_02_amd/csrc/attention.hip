@@ -38,7 +38,9 @@ constexpr int kMaxRowsPerBlock = 8 * kRowsPerWave;
 constexpr int kWaves = 8;                  // waves per bf16 workgroup
 constexpr int kStages = 4;                 // LDS ring depth (tiles)
 constexpr int kCombineRows = 32;           // query rows per combine workgroup
+constexpr int kMaxSplitsCombine = 1024;    // splits per request the combine handles
 constexpr int kMaxSplit = 8192;            // keys per split (block ids kept in LDS)
+static_assert((int64_t)kMaxSplit * 1024 == kMaxAttnKeys, "key limit");
 
 struct AttnArgs {
   const int32_t* row_offsets;
@@ -59,6 +61,9 @@ struct AttnArgs {
   int rows_per_block;
   float* part;       // [items][rows_per_block][D] unnormalised outputs
   float* part_ml;    // [items][rows_per_block][2]  (running max, running sum)
+  int lpt;           // two-phase (longest-first) item order, see AttnPlan
+  int64_t items_a;   // items of the first phase
+  uint16_t order[kLptMax];
 };
 
 // Per-request work counts, shared by the planner (host) and kernels (device).
@@ -105,6 +110,98 @@ SPEC_DEVICE void locate(int64_t x, const AttnArgs& a, int& b_out, int64_t& base_
   base_out = 0;
 }
 
+
+// Workgroup index -> (request, KV head, row block, split).  Phase A: every
+// split but the last of each request when `lpt` is set (every split
+// otherwise), request by request, then (KV head, row block, split).  Phase B
+// (`lpt` only): the last split of each request, requests in `order`, then
+// (KV head, row block).  Wave-parallel over requests; uniform results;
+// b = -1 past the end.
+SPEC_DEVICE void locate_item(int64_t x, const AttnArgs& a, int& b, int& kvh, int& rb, int& s) {
+  const int lane = threadIdx.x & 63;
+  const int tail = a.lpt;
+  const int rpb = a.rows_per_block;
+  b = -1;
+  kvh = rb = s = 0;
+  const bool phase_a = x < a.items_a;
+  if (!phase_a) x -= a.items_a;
+  int64_t running = 0;
+  for (int base = 0; base < a.B; base += 64) {
+    int bq = -1, nrb = 0, ns = 0;
+    int64_t cnt = 0;
+    if (base + lane < a.B) {
+      bq = phase_a ? base + lane : (int)a.order[base + lane];
+      const int n = a.row_offsets[bq + 1] - a.row_offsets[bq];
+      nrb = attn_row_blocks(n, a.G, rpb);
+      ns = attn_splits(a.prefix_len[bq] + n, a.split);
+      cnt = (int64_t)a.addr.hkv * nrb * (phase_a ? ns - tail : 1);
+    }
+    int64_t incl = cnt;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int64_t t = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += t;
+    }
+    const int64_t total = __shfl(incl, 63, 64);
+    if (x < running + total) {
+      const uint64_t hit = __ballot(running + incl > x);
+      const int f = __ffsll((long long)hit) - 1;
+      const int64_t local = x - running - __shfl(incl - cnt, f, 64);
+      b = __shfl(bq, f, 64);
+      const int nrb_b = __shfl(nrb, f, 64);
+      const int ns_b = __shfl(ns, f, 64);
+      if (phase_a) {
+        const int nsa = ns_b - tail;
+        s = (int)(local % nsa);
+        rb = (int)((local / nsa) % nrb_b);
+        kvh = (int)(local / ((int64_t)nsa * nrb_b));
+      } else {
+        s = ns_b - 1;
+        rb = (int)(local % nrb_b);
+        kvh = (int)(local / nrb_b);
+      }
+      return;
+    }
+    running += total;
+  }
+}
+
+// Item index of split s of unit u = kvh * nrb + rb of request b (inverse of
+// locate_item).  Wave-parallel; uniform.
+SPEC_DEVICE int64_t item_of(const AttnArgs& a, int b, int64_t u, int ns, int s) {
+  const int lane = threadIdx.x & 63;
+  const int tail = a.lpt;
+  const int rpb = a.rows_per_block;
+  if (s < ns - tail) {
+    int64_t cnt = 0;
+    for (int base = 0; base < b; base += 64) {
+      const int bq = base + lane;
+      if (bq < b) {
+        const int n = a.row_offsets[bq + 1] - a.row_offsets[bq];
+        cnt += (int64_t)a.addr.hkv * attn_row_blocks(n, a.G, rpb) *
+               (attn_splits(a.prefix_len[bq] + n, a.split) - tail);
+      }
+    }
+    return wave_sum(cnt) + u * (ns - tail) + s;
+  }
+  int64_t running = 0;
+  for (int base = 0; base < a.B; base += 64) {
+    int bq = -1;
+    int64_t cnt = 0;
+    if (base + lane < a.B) {
+      bq = a.order[base + lane];
+      const int n = a.row_offsets[bq + 1] - a.row_offsets[bq];
+      cnt = (int64_t)a.addr.hkv * attn_row_blocks(n, a.G, rpb);
+    }
+    const uint64_t hit = __ballot(bq == b);
+    if (hit) {
+      const int f = __ffsll((long long)hit) - 1;
+      return a.items_a + running + wave_sum(lane < f ? cnt : (int64_t)0) + u;
+    }
+    running += wave_sum(cnt);
+  }
+  return -1;
+}
 
 typedef const __attribute__((address_space(1))) uint16_t* gptr_u16;
 typedef const __attribute__((address_space(1))) void* gptr_void;
@@ -316,21 +413,15 @@ __global__ void __launch_bounds__(kWaves * 64, 1) attn_bf16_kernel(AttnArgs a) {
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-  int b;
-  int64_t ibase;
   const int64_t item = blockIdx.x;
-  locate<false>(item, a, b, ibase);
+  int b, kvh, rb, s;
+  locate_item(item, a, b, kvh, rb, s);
   if (b < 0) return;
   const int o = a.row_offsets[b];
   const int n = a.row_offsets[b + 1] - o;
   const int L = __builtin_amdgcn_readfirstlane(a.prefix_len[b]);
   const int total_keys = L + n;
-  const int nrb = attn_row_blocks(n, a.G, ROWS);
   const int ns = attn_splits(total_keys, a.split);
-  const int64_t local = item - ibase;
-  const int s = (int)(local % ns);
-  const int rb = (int)((local / ns) % nrb);
-  const int kvh = (int)(local / ((int64_t)ns * nrb));
   const int key_begin = __builtin_amdgcn_readfirstlane(s * a.split);
   const int key_end = __builtin_amdgcn_readfirstlane(min(key_begin + a.split, total_keys));
   const int M = n * a.G;
@@ -541,25 +632,25 @@ __global__ void __launch_bounds__(256) attn_combine_kernel(AttnArgs a) {
   const int r0 = chunk * kCombineRows;             // first row (within the block)
   const int rows = min(kCombineRows, min(ROWS, M - rb * ROWS) - r0);
   if (rows <= 0) return;
-  // first item of request b: items of all earlier requests
-  const int lane = threadIdx.x & 63;
-  int64_t cnt = 0;
-  for (int base = 0; base < b; base += 64) {
-    const int bq = base + lane;
-    if (bq < b) {
-      const int nq = a.row_offsets[bq + 1] - a.row_offsets[bq];
-      cnt += (int64_t)a.addr.hkv * attn_row_blocks(nq, a.G, ROWS) *
-             attn_splits(a.prefix_len[bq] + nq, a.split);
+  // Item of each split of this unit, kept in LDS for the loops below.
+  __shared__ int64_t s_item[kMaxSplitsCombine];
+  if (ns > kMaxSplitsCombine) return;      // excluded by the planner
+  if (threadIdx.x < 64) {
+    const int64_t first = item_of(a, b, u, ns, 0);
+    for (int sp = threadIdx.x; sp < ns - a.lpt; sp += 64) s_item[sp] = first + sp;
+    if (a.lpt) {
+      const int64_t last = item_of(a, b, u, ns, ns - 1);
+      if (threadIdx.x == 0) s_item[ns - 1] = last;
     }
   }
-  const int64_t item0 = wave_sum(cnt) + u * ns;    // split 0 of this unit
+  __syncthreads();
   const float2* ml = reinterpret_cast<const float2*>(a.part_ml);
 
   {  // per-row maximum and weighted sum: 8 threads per row, splits strided
     const int r = threadIdx.x >> 3, j = threadIdx.x & 7;
     float mx = -INFINITY;
     if (r < rows)
-      for (int s = j; s < ns; s += 8) mx = fmaxf(mx, ml[(item0 + s) * ROWS + r0 + r].x);
+      for (int s = j; s < ns; s += 8) mx = fmaxf(mx, ml[s_item[s] * ROWS + r0 + r].x);
     mx = fmaxf(mx, __shfl_xor(mx, 1, 64));
     mx = fmaxf(mx, __shfl_xor(mx, 2, 64));
     mx = fmaxf(mx, __shfl_xor(mx, 4, 64));
@@ -567,7 +658,7 @@ __global__ void __launch_bounds__(256) attn_combine_kernel(AttnArgs a) {
     float l = 0.0f;
     if (r < rows)
       for (int s = j; s < ns; s += 8) {
-        const float2 v = ml[(item0 + s) * ROWS + r0 + r];
+        const float2 v = ml[s_item[s] * ROWS + r0 + r];
         l += v.y * __builtin_amdgcn_exp2f(v.x - ref);
       }
     l += __shfl_xor(l, 1, 64);
@@ -587,9 +678,8 @@ __global__ void __launch_bounds__(256) attn_combine_kernel(AttnArgs a) {
     if (r >= rows) break;
     const float ref = s_m[r];
     float4 accv = make_float4(0.f, 0.f, 0.f, 0.f);
-    const int64_t prow = (item0 * ROWS + r0 + r);
     for (int s = 0; s < ns; ++s) {
-      const int64_t pr = prow + (int64_t)s * ROWS;
+      const int64_t pr = s_item[s] * ROWS + r0 + r;
       const float wgt = __builtin_amdgcn_exp2f(ml[pr].x - ref);
       const float4 pv = *reinterpret_cast<const float4*>(a.part + pr * D + c4 * 4);
       accv.x += pv.x * wgt; accv.y += pv.y * wgt; accv.z += pv.z * wgt; accv.w += pv.w * wgt;
@@ -700,38 +790,57 @@ attn_f32_kernel(const int32_t* __restrict__ row_offsets, const int32_t* __restri
 AttnPlan plan_attention(int B, const int32_t* row_offsets_h, const int32_t* prefix_len_h, int hq,
                         int hkv) {
   const int G = hq / hkv;
-  int max_rows = 0;
-  for (int b = 0; b < B; ++b)
-    max_rows = std::max(max_rows, (row_offsets_h[b + 1] - row_offsets_h[b]) * G);
   AttnPlan p;
   // 8 waves of 32 query rows: most (request, KV head) pairs fit in one
   // workgroup, so every KV tile is read once.
   p.rows_per_block = kWaves * kRowsPerWave;
-  (void)max_rows;
-  int64_t work = 0, units = 0;
+  int64_t work = 0, units = 0, max_keys = 0;
   for (int b = 0; b < B; ++b) {
     const int n = row_offsets_h[b + 1] - row_offsets_h[b];
     const int nrb = attn_row_blocks(n, G, p.rows_per_block);
     units += (int64_t)hkv * nrb;
     work += (int64_t)hkv * nrb * (prefix_len_h[b] + n);
+    max_keys = std::max<int64_t>(max_keys, prefix_len_h[b] + n);
   }
   // One workgroup per CU at a time: aim at ~4 workgroups per CU (256 CUs),
-  // splits of at least 256 keys.
+  // splits of at least 256 keys and at most kMaxSplitsCombine per request.
   const int64_t target = 1024;
   int64_t split = (work + target - 1) / target;
+  split = std::max<int64_t>(split, (max_keys + kMaxSplitsCombine - 1) / kMaxSplitsCombine);
   split = ((split + kTileKeys - 1) / kTileKeys) * kTileKeys;
   if (split < 256) split = 256;
-  if (split > kMaxSplit) split = kMaxSplit;
-  p.split_keys = (int)split;
+  p.units = units;
   p.items = 0;
   p.partial_items = 0;
-  p.units = units;
+  p.items_a = 0;
+  p.lpt = 0;
+  if (split > kMaxSplit) {          // a request longer than kMaxSplit * kMaxSplitsCombine keys
+    p.split_keys = 0;
+    p.items = -1;
+    return p;
+  }
+  p.split_keys = (int)split;
+  p.lpt = (B <= kLptMax) ? 1 : 0;
   for (int b = 0; b < B; ++b) {
     const int n = row_offsets_h[b + 1] - row_offsets_h[b];
     const int ns = attn_splits(prefix_len_h[b] + n, p.split_keys);
-    const int64_t it = (int64_t)hkv * attn_row_blocks(n, G, p.rows_per_block) * ns;
-    p.items += it;
-    if (ns > 1) p.partial_items += it;
+    const int64_t per = (int64_t)hkv * attn_row_blocks(n, G, p.rows_per_block);
+    p.items += per * ns;
+    p.items_a += per * (ns - p.lpt);
+    if (ns > 1) p.partial_items += per * ns;
+  }
+  if (p.lpt) {
+    // second phase: requests by the length of their last split, longest
+    // first (ties by request index)
+    int64_t tail_len[kLptMax];
+    for (int b = 0; b < B; ++b) {
+      const int keys = prefix_len_h[b] + row_offsets_h[b + 1] - row_offsets_h[b];
+      const int ns = attn_splits(keys, p.split_keys);
+      tail_len[b] = keys - (int64_t)(ns - 1) * p.split_keys;
+      p.order[b] = (uint16_t)b;
+    }
+    std::stable_sort(p.order, p.order + B,
+                     [&](uint16_t x, uint16_t y) { return tail_len[x] > tail_len[y]; });
   }
   return p;
 }
@@ -764,7 +873,10 @@ hipError_t launch_attention_bf16(const LaunchCtx& cx, const AttnPlan& plan, cons
   a.rows_per_block = plan.rows_per_block;
   a.part = (float*)workspace;
   a.part_ml = a.part + (size_t)plan.items * plan.rows_per_block * addr.d;
-  if (plan.items > 0x7fffffff) return hipErrorInvalidValue;
+  a.lpt = plan.lpt;
+  a.items_a = plan.items_a;
+  if (plan.lpt) std::copy(plan.order, plan.order + cx.B, a.order);
+  if (plan.items <= 0 || plan.items > 0x7fffffff) return hipErrorInvalidValue;
   const dim3 grid((unsigned)plan.items);
   if (plan.rows_per_block != kWaves * kRowsPerWave) return hipErrorInvalidValue;
   if (addr.d == 128) {

@@ -15,14 +15,28 @@ struct LaunchCtx {
   hipStream_t stream;
 };
 
+// Longest-first dispatch covers batches of up to this many requests (their
+// order travels in the kernel arguments).
+constexpr int kLptMax = 512;
+// Longest request (prefix + tree) the bf16 attention plans for: splits of at
+// most 8192 keys, at most 1024 splits per request.
+constexpr int64_t kMaxAttnKeys = 8192LL * 1024;
+
 // Split-KV plan of the bf16 tree-attention kernel: every (request, KV head,
-// row block, key split) is one workgroup.
+// row block, key split) is one workgroup.  With `lpt`, workgroups come in two
+// phases: first every split but the last of each request (all of full
+// length), then the last split of each request, requests ordered by that
+// split's length, longest first (`order`), so that the hardware dispatcher's
+// in-order list scheduling ends on the short pieces.
 struct AttnPlan {
   int rows_per_block;   // query rows (tree rows x group heads) per workgroup
   int split_keys;       // keys per split (multiple of the key tile)
   int64_t items;        // total workgroups
   int64_t partial_items;// workgroups whose request needs more than one split
   int64_t units;        // (request, KV head, row block) triples
+  int lpt;              // two-phase order in use
+  int64_t items_a;      // workgroups of the first phase
+  uint16_t order[kLptMax];  // second phase: requests, longest last split first
 };
 
 hipError_t launch_build_mask(const LaunchCtx& cx, const int32_t* parents, uint64_t* mask, int words,
