@@ -38,6 +38,7 @@ constexpr int kMaxRowsPerBlock = 8 * kRowsPerWave;
 constexpr int kWaves = 8;                  // waves per bf16 workgroup
 constexpr int kStages = 4;                 // LDS ring depth (tiles)
 constexpr int kCombineRows = 32;           // query rows per combine workgroup
+constexpr float kLazyMax = 8.0f;           // log2 headroom of the softmax reference
 constexpr int kMaxSplitsCombine = 1024;    // splits per request the combine handles
 constexpr int kMaxSplit = 8192;            // keys per split (block ids kept in LDS)
 static_assert((int64_t)kMaxSplit * 1024 == kMaxAttnKeys, "key limit");
@@ -239,18 +240,52 @@ SPEC_DEVICE int tile_slot_bytes(int row, int c) {
 // PER_WAVE of the tile's 1 KB blocks.  A block is 16 consecutive keys (one
 // paged KV block: the tile start is 64-aligned), so its base address is
 // uniform; lane l writes LDS slot l and loads the global chunk that the
-// layout above puts there.  Keys at or past the split end read its last key
-// instead (finite data; they are masked out of the softmax), which keeps
-// every access inside the cache rows the caller owns.
+// layout above puts there.
+//  * Whole tiles (the common case): the tile's four block ids come from one
+//    16-byte LDS read; per load only a scalar base changes.
+//  * A tile that reaches the split end: keys at or past it read the split's
+//    last key instead (finite data; they are masked out of the softmax), which
+//    keeps every access inside the cache rows the caller owns.
 template <int D>
 SPEC_DEVICE void issue_tile(uint16_t* ks, uint16_t* vs, gptr_u16 gk, gptr_u16 gv, int t0,
                             int key_end, bool paged, const int* s_blk, int blk0,
                             int64_t blk_stride, int wave, int lane) {
   constexpr int NB = D / 8;                  // 1 KB blocks per K (or V) tile
   constexpr int PER_WAVE = 2 * NB / kWaves;
-  const int last = key_end - 1;
   const int cl = lane >> 4;
   const int rr = (lane & 15) ^ (4 * cl);
+  const int last = key_end - 1;
+  if (t0 + kTileKeys <= key_end) {
+    int b0, b1, b2, b3;                      // element offsets / stride of the 4 blocks
+    int64_t stride;
+    if (paged) {
+      const int4 ids = *reinterpret_cast<const int4*>(s_blk + ((t0 >> 4) - blk0));
+      b0 = __builtin_amdgcn_readfirstlane(ids.x);
+      b1 = __builtin_amdgcn_readfirstlane(ids.y);
+      b2 = __builtin_amdgcn_readfirstlane(ids.z);
+      b3 = __builtin_amdgcn_readfirstlane(ids.w);
+      stride = blk_stride;
+    } else {
+      b0 = t0 >> 4;
+      b1 = b0 + 1;
+      b2 = b0 + 2;
+      b3 = b0 + 3;
+      stride = (int64_t)kBlock * D;
+    }
+    const int lane_off = rr * D + cl * 8;    // elements inside a block
+#pragma unroll
+    for (int j = 0; j < PER_WAVE; ++j) {
+      const int gi = wave * PER_WAVE + j;    // uniform
+      const bool isv = gi >= NB;
+      const int bi = isv ? gi - NB : gi;
+      const int grp = bi & 3;
+      const int bid = (grp == 0) ? b0 : (grp == 1) ? b1 : (grp == 2) ? b2 : b3;
+      const gptr_u16 base = (isv ? gv : gk) + ((int64_t)bid * stride + (bi >> 2) * 32);
+      uint16_t* dst = (isv ? vs : ks) + bi * 512;
+      __builtin_amdgcn_global_load_lds((gptr_void)(base + lane_off), (lptr_void)dst, 16, 0, 0);
+    }
+    return;
+  }
 #pragma unroll
   for (int j = 0; j < PER_WAVE; ++j) {
     const int gi = wave * PER_WAVE + j;      // uniform
@@ -337,8 +372,14 @@ SPEC_DEVICE void compute_half(const uint16_t* ks, const uint16_t* vs, int hk, in
 #pragma unroll
   for (int e = 1; e < 16; ++e) mx = fmaxf(mx, sc[e]);
   mx = row_pair_max(mx);
-  // scale_log2 > 0, so the row maximum commutes with the scaling.
-  const float m_new = fmaxf(m_run, mx * scale_log2);
+  // Online softmax with a lazily moved reference (scale_log2 > 0, so the row
+  // maximum commutes with the scaling): a row's reference m only moves when
+  // a score exceeds it by more than kLazyMax (log2 units), so p = 2^(s - m)
+  // stays <= 2^kLazyMax and the O/l rescale is rare.  O/l is unchanged by
+  // the choice of reference.
+  const float cand = mx * scale_log2;
+  const bool move = cand > m_run + kLazyMax;          // false for a fully masked row
+  const float m_new = move ? cand : m_run;
   // A row with no visible key yet keeps m = -inf; 0 as the reference then
   // gives alpha = 0 and p = 0 without a divergent branch.
   const float m_ref = (m_new == -INFINITY) ? 0.0f : m_new;
@@ -353,13 +394,14 @@ SPEC_DEVICE void compute_half(const uint16_t* ks, const uint16_t* vs, int hk, in
   }
   rs = row_pair_sum(rs);
   l_run = l_run * alpha + rs;
-  m_run = m_new;
-  if (__any(alpha != 1.0f)) {                // the running max moved for some row
+  // Rows seen for the first time have O = 0 and need no rescale.
+  if (__any(move && m_run != -INFINITY)) {
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[db][e] *= alpha;
   }
+  m_run = m_new;
   // V^T operand by transposed LDS reads: this lane supplies the address of 4
   // dims of one key; lane 4q+c of each 16-lane group receives dim dbase+4q+c
   // of 4 consecutive keys.  The k-slots of P^T (key half*4 + 8*(e/4) + e%4 of
@@ -407,7 +449,7 @@ __global__ void __launch_bounds__(kWaves * 64, 1) attn_bf16_kernel(AttnArgs a) {
   static_assert(PER_WAVE * 3 < 64, "vmcnt range");
   __shared__ __attribute__((aligned(16))) uint16_t k0[TILE], k1[TILE], k2[TILE], k3[TILE];
   __shared__ __attribute__((aligned(16))) uint16_t v0[TILE], v1[TILE], v2[TILE], v3[TILE];
-  __shared__ int s_blk[kMaxSplit / kBlock + 2];
+  __shared__ __attribute__((aligned(16))) int s_blk[kMaxSplit / kBlock + 4];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
