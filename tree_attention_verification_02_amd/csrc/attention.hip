@@ -225,15 +225,19 @@ SPEC_DEVICE uint4 gload16(gptr_u16 p) {
 
 // LDS layout of a 64-key tile (K or V), in 1 KB blocks: block
 // (chunk group cg = c / 4, row group rg = row / 16) sits at block index
-// cg * 4 + rg; inside it, 16-byte chunk c of key row `row` goes to slot
-// (c % 4) * 16 + ((row % 16) ^ (4 * (c % 4))).  One direct-to-LDS
-// instruction fills one block (16 rows x 64 contiguous bytes each); the
-// 16-byte K reads of 32 rows and the transposed V reads of 8 rows x 4
-// chunks both reach the minimum number of LDS cycles, and every read
-// address is a per-lane base plus a compile-time offset.
+// cg * 4 + rg; inside it, 16-byte chunk c of key row r (r16 = r % 16) goes
+// to slot 4 * r16 + ((c % 4) ^ (r16 / 4)).
+//  * One direct-to-LDS instruction fills one block: lane l loads row l / 4 of
+//    the group, so each 4-lane quad reads one contiguous 64-byte segment of
+//    one key row (in-quad order permuted), which streams close to a plain
+//    contiguous read.
+//  * The 16-byte K reads (32 rows, one chunk) and the transposed V reads
+//    (4 rows x 64 bytes per 32 lanes) both hit every bank exactly once per
+//    cycle, and each lane needs only two base addresses (even / odd chunk);
+//    everything else is a compile-time offset.
 SPEC_DEVICE int tile_slot_bytes(int row, int c) {
-  const int cl = c & 3;
-  return ((c >> 2) * 4 + (row >> 4)) * 1024 + (cl * 16 + ((row & 15) ^ (4 * cl))) * 16;
+  const int r16 = row & 15;
+  return ((c >> 2) * 4 + (row >> 4)) * 1024 + (4 * r16 + ((c & 3) ^ (r16 >> 2))) * 16;
 }
 
 // Issue the direct-to-LDS loads of one 64-key K and V tile; each wave issues
@@ -252,8 +256,8 @@ SPEC_DEVICE void issue_tile(uint16_t* ks, uint16_t* vs, gptr_u16 gk, gptr_u16 gv
                             int64_t blk_stride, int wave, int lane) {
   constexpr int NB = D / 8;                  // 1 KB blocks per K (or V) tile
   constexpr int PER_WAVE = 2 * NB / kWaves;
-  const int cl = lane >> 4;
-  const int rr = (lane & 15) ^ (4 * cl);
+  const int rr = lane >> 2;                  // key row inside the 16-key group
+  const int cl = (lane & 3) ^ (lane >> 4);   // chunk inside the 4-chunk group
   const int last = key_end - 1;
   if (t0 + kTileKeys <= key_end) {
     int b0, b1, b2, b3;                      // element offsets / stride of the 4 blocks
