@@ -39,7 +39,8 @@
 
 namespace spec {
 
-constexpr int kStatThreads = 512;
+constexpr int kStatThreads = 256;
+constexpr int kStatChunks = 8;               // workgroups per logits row
 constexpr int kWalkThreads = 1024;
 constexpr int kWalkWaves = kWalkThreads / 64;
 constexpr int kSeg = kWalkThreads * 4;        // elements per segment
@@ -139,7 +140,21 @@ SPEC_DEVICE double exp_f64(double x, const double* tab) {
   const double scale = __longlong_as_double((long long)((ki >> 8) + 1023) << 52);
   return fma(s, p, s) * scale;
 }
-
+// The same value without a branch (for unrolled streaming loops).
+SPEC_DEVICE double exp_f64_flat(double x, const double* tab) {
+  const bool under = !(x >= -708.0);
+  x = under ? -708.0 : x;
+  constexpr double kShift = 0x1.8p52;
+  const double t = fma(x, kInvLn2x256, kShift);
+  const double k = t - kShift;
+  const int ki = (int)(uint32_t)__double_as_longlong(t);
+  const double r = fma(-k, kLn2by256Lo, fma(-k, kLn2by256Hi, x));
+  const double p = r * fma(r, fma(r, fma(r, 1.0 / 24, 1.0 / 6), 0.5), 1.0);
+  const double s = tab[ki & 255];
+  const double scale = __longlong_as_double((long long)((ki >> 8) + 1023) << 52);
+  const double e = fma(s, p, s) * scale;
+  return under ? 0.0 : e;
+}
 SPEC_DEVICE void load_exp_table(double* s_tab) {
   for (int i = threadIdx.x; i < 256; i += blockDim.x) s_tab[i] = kExp2Frac[i];
 }
@@ -148,7 +163,11 @@ SPEC_DEVICE void load_exp_table(double* s_tab) {
 // Workspace.
 struct AcceptWs {
   double* lse;      // [2][R] log-sum-exp of logits / T (target rows, draft rows)
-  int32_t* am;      // [R]   first argmax of the target row
+  int32_t* am;      // [R]   first argmax of the target row (greedy)
+  double* part_ref; // [2][R][kStatChunks] chunk partials: reference
+  double* part_s;   //                     and sum of exp(z - reference)
+  float* part_m;    // [R][kStatChunks]    chunk max (greedy)
+  int32_t* part_am; //                     and its first index
   int32_t* sync;    // [B]   walk barrier counters (zeroed by accept_stats)
   double* seg;      // [B][2][kMaxSegs] per-pass segment sums (double-buffered)
   int32_t* last;    // [B][2][kMaxSlices] last positive index per slice
@@ -163,6 +182,14 @@ __host__ __device__ inline AcceptWs accept_ws(void* base, int R, int B, int nseg
   p += align256(2 * (size_t)R * sizeof(double));
   w.am = (int32_t*)p;
   p += align256((size_t)R * sizeof(int32_t));
+  w.part_ref = (double*)p;
+  p += align256(2 * (size_t)R * kStatChunks * sizeof(double));
+  w.part_s = (double*)p;
+  p += align256(2 * (size_t)R * kStatChunks * sizeof(double));
+  w.part_m = (float*)p;
+  p += align256((size_t)R * kStatChunks * sizeof(float));
+  w.part_am = (int32_t*)p;
+  p += align256((size_t)R * kStatChunks * sizeof(int32_t));
   w.sync = (int32_t*)p;
   p += align256((size_t)B * sizeof(int32_t));
   w.seg = (double*)p;
@@ -176,6 +203,9 @@ static int segs_for(int vocab) { return (vocab + kSeg - 1) / kSeg; }
 size_t accept_workspace_bytes(int R, int B, int vocab) {
   const int nseg = segs_for(vocab);
   return align256(2 * (size_t)R * sizeof(double)) + align256((size_t)R * sizeof(int32_t)) +
+         2 * align256(2 * (size_t)R * kStatChunks * sizeof(double)) +
+         align256((size_t)R * kStatChunks * sizeof(float)) +
+         align256((size_t)R * kStatChunks * sizeof(int32_t)) +
          align256((size_t)B * sizeof(int32_t)) + align256((size_t)B * 2 * nseg * sizeof(double)) +
          align256((size_t)B * 2 * kMaxSlices * sizeof(int32_t));
 }
@@ -200,128 +230,214 @@ SPEC_DEVICE void merge_arg(float& m, int& am, float m2, int am2) {
   }
 }
 
+// Partial statistics of one (row, chunk): the row is cut into kStatChunks
+// equal pieces so that rows of 128K logits spread evenly over the CUs.
+//  * sampling: (reference, sum of exp(z - reference)) with z = logit / T, in
+//    fp64; the reference follows the running maximum, moved at most once per
+//    16 logits, so the per-logit work is branch-free.
+//  * greedy: (max, first argmax) of the target row.
+// Draft rows of leaves are not read (their partials are left empty).
+template <bool kGreedy>
 __global__ void __launch_bounds__(kStatThreads)
 accept_stats_kernel(const int32_t* __restrict__ row_offsets, int B, int R,
-                    const int32_t* __restrict__ parents, const int32_t* __restrict__ tokens,
-                    const float* __restrict__ p_logits, const float* __restrict__ q_logits,
-                    int64_t ld, int vocab, float temperature, AcceptWs ws,
-                    float* __restrict__ child_p, float* __restrict__ child_q) {
+                    const int32_t* __restrict__ parents, const float* __restrict__ p_logits,
+                    const float* __restrict__ q_logits, int64_t ld, int vocab, float temperature,
+                    AcceptWs ws) {
   __shared__ double s_tab[256];
   __shared__ float red_m[kStatThreads / 64];
   __shared__ int red_a[kStatThreads / 64];
   __shared__ double red_r[kStatThreads / 64];
   __shared__ double red_s[kStatThreads / 64];
   __shared__ int has_kids;
-  __shared__ double s_lse;
-  __shared__ int s_am;
-  const int which = blockIdx.x >= R ? 1 : 0;          // 0: target p, 1: draft q
-  const int r = blockIdx.x - which * R;
-  const int b = request_of_row(row_offsets, B, r);
-  const int o = row_offsets[b];
-  const int n = row_offsets[b + 1] - o;
-  const int u = r - o;
+  const int chunk = blockIdx.x % kStatChunks;
+  const int rr = blockIdx.x / kStatChunks;
+  const int which = rr >= R ? 1 : 0;                   // 0: target p, 1: draft q
+  const int r = rr - which * R;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const bool greedy = temperature == 0.0f;
+  const int slot = rr * kStatChunks + chunk;
   if (blockIdx.x == 0)
     for (int i = tid; i < B; i += kStatThreads) ws.sync[i] = 0;
-  load_exp_table(s_tab);
-  if (tid == 0) has_kids = 0;
-  __syncthreads();
+  if (!kGreedy) load_exp_table(s_tab);
   if (which == 1) {
+    const int b = request_of_row(row_offsets, B, r);
+    const int o = row_offsets[b];
+    const int n = row_offsets[b + 1] - o;
+    const int u = r - o;
+    if (tid == 0) has_kids = 0;
+    __syncthreads();
     for (int i = tid; i < n; i += kStatThreads)
       if (i > 0 && parents[o + i] == u) has_kids = 1;
     __syncthreads();
-    if (!has_kids) return;
+    if (!has_kids) {
+      if (tid == 0) {
+        ws.part_ref[slot] = 0.0;
+        ws.part_s[slot] = 0.0;
+      }
+      return;
+    }
   }
-  const double invT = greedy ? 1.0 : 1.0 / (double)temperature;
   const float* row = (which ? q_logits : p_logits) + (int64_t)r * ld;
   const float4* row4 = reinterpret_cast<const float4*>(row);
   const int v4 = (vocab + 3) >> 2;
-
-  float m = -INFINITY;
-  int am = -1;
-  // common reference for the exponent sums: the row's first logit (rare
-  // per-thread rescale when a value exceeds it by more than e^64)
-  double ref = (double)row[0] * invT;
-  if (!(ref > -INFINITY && ref < INFINITY)) ref = 0.0;
-  double s = 0.0;
+  const int per = (v4 + kStatChunks - 1) / kStatChunks;
+  const int f_begin = chunk * per;
+  const int f_end = min(v4, f_begin + per);
   constexpr int U = 4;
-  for (int f0 = tid; f0 < v4; f0 += kStatThreads * U) {
+  if (kGreedy) {
+    float m = -INFINITY;
+    int am = -1;
+    for (int f0 = f_begin + tid; f0 < f_end; f0 += kStatThreads * U) {
+      float4 x[U];
+#pragma unroll
+      for (int k = 0; k < U; ++k) {
+        const int f = f0 + k * kStatThreads;
+        x[k] = (f < f_end) ? row4[f] : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+      }
+#pragma unroll
+      for (int k = 0; k < U; ++k) {
+        const int y0 = (f0 + k * kStatThreads) * 4;
+        const float xs[4] = {x[k].x, x[k].y, x[k].z, x[k].w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float xv = (y0 + j < vocab) ? xs[j] : -INFINITY;
+          const bool gt = xv > m;                  // strict: the first index wins ties
+          m = gt ? xv : m;
+          am = gt ? y0 + j : am;
+        }
+      }
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1)
+      merge_arg(m, am, __shfl_xor(m, off, 64), __shfl_xor(am, off, 64));
+    if (lane == 0) {
+      red_m[wave] = m;
+      red_a[wave] = am;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      for (int w = 1; w < kStatThreads / 64; ++w) merge_arg(m, am, red_m[w], red_a[w]);
+      ws.part_m[slot] = m;
+      ws.part_am[slot] = am;
+    }
+    return;
+  }
+  const double invT = 1.0 / (double)temperature;
+  double ref = -INFINITY;
+  double s = 0.0;
+  for (int f0 = f_begin + tid; f0 < f_end; f0 += kStatThreads * U) {
     float4 x[U];
 #pragma unroll
     for (int k = 0; k < U; ++k) {
       const int f = f0 + k * kStatThreads;
-      x[k] = (f < v4) ? row4[f] : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+      x[k] = (f < f_end) ? row4[f] : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
     }
+    float cm = -INFINITY;
 #pragma unroll
     for (int k = 0; k < U; ++k) {
       const int y0 = (f0 + k * kStatThreads) * 4;
-      const float xs[4] = {x[k].x, x[k].y, x[k].z, x[k].w};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float xv = (y0 + j < vocab) ? xs[j] : -INFINITY;
-        const bool gt = xv > m;
-        m = gt ? xv : m;
-        am = gt ? y0 + j : am;
-        if (!greedy && xv != -INFINITY) {
-          const double d = (double)xv * invT - ref;
-          if (d > 64.0) {                         // rare: move the reference up
-            s *= exp_f64(-d, s_tab);
-            ref += d;
-            s += 1.0;
-          } else {
-            s += exp_f64(d, s_tab);
-          }
-        }
+      if (y0 + 3 >= vocab) {                       // the row's ragged end
+        if (y0 + 1 >= vocab) x[k].y = -INFINITY;
+        if (y0 + 2 >= vocab) x[k].z = -INFINITY;
+        if (y0 + 3 >= vocab) x[k].w = -INFINITY;
       }
+      cm = fmaxf(cm, fmaxf(fmaxf(x[k].x, x[k].y), fmaxf(x[k].z, x[k].w)));
+    }
+    const double cmd = (double)cm * invT;
+    if (cmd > ref + 64.0) {                        // first values, or a much larger one
+      s = (ref == -INFINITY) ? 0.0 : s * exp_f64(ref - cmd, s_tab);
+      ref = cmd;
+    }
+#pragma unroll
+    for (int k = 0; k < U; ++k) {
+      s += exp_f64_flat(fma((double)x[k].x, invT, -ref), s_tab);
+      s += exp_f64_flat(fma((double)x[k].y, invT, -ref), s_tab);
+      s += exp_f64_flat(fma((double)x[k].z, invT, -ref), s_tab);
+      s += exp_f64_flat(fma((double)x[k].w, invT, -ref), s_tab);
     }
   }
-  // wave then workgroup reduction
 #pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    merge_arg(m, am, __shfl_xor(m, off, 64), __shfl_xor(am, off, 64));
-    if (!greedy) merge_ref(ref, s, __shfl_xor(ref, off, 64), __shfl_xor(s, off, 64), s_tab);
-  }
+  for (int off = 32; off > 0; off >>= 1)
+    merge_ref(ref, s, __shfl_xor(ref, off, 64), __shfl_xor(s, off, 64), s_tab);
   if (lane == 0) {
-    red_m[wave] = m;
-    red_a[wave] = am;
     red_r[wave] = ref;
     red_s[wave] = s;
   }
   __syncthreads();
   if (tid == 0) {
-    for (int w = 1; w < kStatThreads / 64; ++w) {
-      merge_arg(m, am, red_m[w], red_a[w]);
-      if (!greedy) merge_ref(ref, s, red_r[w], red_s[w], s_tab);
-    }
-    const double lse = greedy ? 0.0 : ref + log(s);
-    if (!greedy) ws.lse[which * R + r] = lse;
-    if (which == 0) ws.am[r] = am;
-    s_lse = lse;
-    s_am = am;
-  }
-  __syncthreads();
-  const double lse = s_lse;
-  am = s_am;
-  if (which == 0 && u == 0 && tid == 0) {                          // root: no draft
-    if (child_p) child_p[o] = __int_as_float(0x7fc00000);
-    if (child_q && !greedy) child_q[o] = __int_as_float(0x7fc00000);
-  }
-  float* dst = which ? child_q : child_p;
-  if (dst == nullptr || (which == 1 && greedy)) return;
-  for (int i = tid; i < n; i += kStatThreads) {
-    if (i > 0 && parents[o + i] == u) {
-      const int x = tokens[o + i];
-      float val;
-      if (greedy) {
-        val = (x == am) ? 1.0f : 0.0f;
-      } else {
-        val = (x >= 0 && x < vocab) ? (float)exp_f64((double)row[x] * invT - lse, s_tab) : 0.0f;
-      }
-      dst[o + i] = val;
-    }
+    for (int w = 1; w < kStatThreads / 64; ++w) merge_ref(ref, s, red_r[w], red_s[w], s_tab);
+    ws.part_ref[slot] = ref;
+    ws.part_s[slot] = s;
   }
 }
+
+// Per-row results from the chunk partials, merged in chunk order (so every
+// run gives the same bits): the log-sum-exp of each row (or the target
+// argmax when greedy), and each child's probability under its parent's
+// distributions, P_u(x_c) and Q_u(x_c) (greedy: 1 if x_c is the argmax).
+// One thread per (row, target|draft).
+SPEC_DEVICE void merged_ref_sum(const AcceptWs& ws, int rr, const double* tab, double& ref,
+                                double& s) {
+  ref = ws.part_ref[rr * kStatChunks];
+  s = ws.part_s[rr * kStatChunks];
+  for (int c = 1; c < kStatChunks; ++c)
+    merge_ref(ref, s, ws.part_ref[rr * kStatChunks + c], ws.part_s[rr * kStatChunks + c], tab);
+}
+SPEC_DEVICE int merged_argmax(const AcceptWs& ws, int r) {
+  float m = ws.part_m[r * kStatChunks];
+  int am = ws.part_am[r * kStatChunks];
+  for (int c = 1; c < kStatChunks; ++c)
+    merge_arg(m, am, ws.part_m[r * kStatChunks + c], ws.part_am[r * kStatChunks + c]);
+  return am;
+}
+
+__global__ void __launch_bounds__(256)
+accept_finalize_kernel(const int32_t* __restrict__ row_offsets, int B, int R,
+                       const int32_t* __restrict__ parents, const int32_t* __restrict__ tokens,
+                       const float* __restrict__ p_logits, const float* __restrict__ q_logits,
+                       int64_t ld, int vocab, float temperature, AcceptWs ws,
+                       float* __restrict__ child_p, float* __restrict__ child_q) {
+  __shared__ double s_tab[256];
+  const bool greedy = temperature == 0.0f;
+  if (!greedy) load_exp_table(s_tab);
+  __syncthreads();
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  if (t >= (greedy ? R : 2 * R)) return;
+  const int which = t >= R ? 1 : 0;
+  const int r = t - which * R;
+  const int b = request_of_row(row_offsets, B, r);
+  const int o = row_offsets[b];
+  const int u = r - o;
+  const double invT = greedy ? 1.0 : 1.0 / (double)temperature;
+  if (greedy) {
+    ws.am[r] = merged_argmax(ws, r);
+  } else {
+    double ref, s;
+    merged_ref_sum(ws, which * R + r, s_tab, ref, s);
+    ws.lse[which * R + r] = ref + log(s);
+  }
+  float* dst = which ? child_q : child_p;
+  if (dst == nullptr) return;
+  if (u == 0) {                                    // the root has no draft
+    dst[r] = __int_as_float(0x7fc00000);
+    return;
+  }
+  const int pu = parents[r];
+  const int x = tokens[r];
+  if (pu < 0 || pu >= u) {                         // invalid tree (reported by the walk)
+    dst[r] = __int_as_float(0x7fc00000);
+    return;
+  }
+  if (greedy) {
+    dst[r] = (x == merged_argmax(ws, o + pu)) ? 1.0f : 0.0f;
+    return;
+  }
+  double ref, s;
+  merged_ref_sum(ws, which * R + o + pu, s_tab, ref, s);
+  const double lse = ref + log(s);
+  const float* prow = (which ? q_logits : p_logits) + (int64_t)(o + pu) * ld;
+  dst[r] = (x >= 0 && x < vocab) ? (float)exp_f64((double)prow[x] * invT - lse, s_tab) : 0.0f;
+}
+
 
 // ---------------------------------------------------------------------------
 // Walk.
@@ -883,8 +999,17 @@ hipError_t launch_accept(const LaunchCtx& cx, int R, const int32_t* parents, con
   static_assert(sizeof(WalkShared) < 20480, "walk LDS");
   const int nseg = segs_for(vocab);
   AcceptWs ws = accept_ws(workspace, R, cx.B, nseg);
-  const int nblk = (temperature == 0.0f) ? R : 2 * R;
-  hipLaunchKernelGGL(accept_stats_kernel, dim3(nblk), dim3(kStatThreads), 0, cx.stream,
+  const bool greedy = temperature == 0.0f;
+  const int rows = greedy ? R : 2 * R;
+  if (greedy)
+    hipLaunchKernelGGL(accept_stats_kernel<true>, dim3(rows * kStatChunks), dim3(kStatThreads), 0,
+                       cx.stream, cx.row_offsets_d, cx.B, R, parents, p_logits, q_logits, ld, vocab,
+                       temperature, ws);
+  else
+    hipLaunchKernelGGL(accept_stats_kernel<false>, dim3(rows * kStatChunks), dim3(kStatThreads), 0,
+                       cx.stream, cx.row_offsets_d, cx.B, R, parents, p_logits, q_logits, ld, vocab,
+                       temperature, ws);
+  hipLaunchKernelGGL(accept_finalize_kernel, dim3((rows + 255) / 256), dim3(256), 0, cx.stream,
                      cx.row_offsets_d, cx.B, R, parents, tokens, p_logits, q_logits, ld, vocab,
                      temperature, ws, child_p, child_q);
   hipError_t e = hipGetLastError();
