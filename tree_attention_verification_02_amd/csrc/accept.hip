@@ -168,6 +168,8 @@ struct AcceptWs {
   double* part_s;   //                     and sum of exp(z - reference)
   float* part_m;    // [R][kStatChunks]    chunk max (greedy)
   int32_t* part_am; //                     and its first index
+  double* cp;       // [R] P_parent(x_c) of each child row c (fp64, sampling)
+  double* cq;       // [R] Q_parent(x_c)
   int32_t* sync;    // [B]   walk barrier counters (zeroed by accept_stats)
   double* seg;      // [B][2][kMaxSegs] per-pass segment sums (double-buffered)
   int32_t* last;    // [B][2][kMaxSlices] last positive index per slice
@@ -190,6 +192,10 @@ __host__ __device__ inline AcceptWs accept_ws(void* base, int R, int B, int nseg
   p += align256((size_t)R * kStatChunks * sizeof(float));
   w.part_am = (int32_t*)p;
   p += align256((size_t)R * kStatChunks * sizeof(int32_t));
+  w.cp = (double*)p;
+  p += align256((size_t)R * sizeof(double));
+  w.cq = (double*)p;
+  p += align256((size_t)R * sizeof(double));
   w.sync = (int32_t*)p;
   p += align256((size_t)B * sizeof(int32_t));
   w.seg = (double*)p;
@@ -206,6 +212,7 @@ size_t accept_workspace_bytes(int R, int B, int vocab) {
          2 * align256(2 * (size_t)R * kStatChunks * sizeof(double)) +
          align256((size_t)R * kStatChunks * sizeof(float)) +
          align256((size_t)R * kStatChunks * sizeof(int32_t)) +
+         2 * align256((size_t)R * sizeof(double)) +
          align256((size_t)B * sizeof(int32_t)) + align256((size_t)B * 2 * nseg * sizeof(double)) +
          align256((size_t)B * 2 * kMaxSlices * sizeof(int32_t));
 }
@@ -416,28 +423,31 @@ accept_finalize_kernel(const int32_t* __restrict__ row_offsets, int B, int R,
     ws.lse[which * R + r] = ref + log(s);
   }
   float* dst = which ? child_q : child_p;
-  if (dst == nullptr) return;
   if (u == 0) {                                    // the root has no draft
-    dst[r] = __int_as_float(0x7fc00000);
+    if (dst) dst[r] = __int_as_float(0x7fc00000);
     return;
   }
   const int pu = parents[r];
   const int x = tokens[r];
   if (pu < 0 || pu >= u) {                         // invalid tree (reported by the walk)
-    dst[r] = __int_as_float(0x7fc00000);
+    if (dst) dst[r] = __int_as_float(0x7fc00000);
     return;
   }
   if (greedy) {
-    dst[r] = (x == merged_argmax(ws, o + pu)) ? 1.0f : 0.0f;
+    if (dst) dst[r] = (x == merged_argmax(ws, o + pu)) ? 1.0f : 0.0f;
     return;
   }
-  double ref, s;
-  merged_ref_sum(ws, which * R + o + pu, s_tab, ref, s);
-  const double lse = ref + log(s);
-  const float* prow = (which ? q_logits : p_logits) + (int64_t)(o + pu) * ld;
-  dst[r] = (x >= 0 && x < vocab) ? (float)exp_f64((double)prow[x] * invT - lse, s_tab) : 0.0f;
+  double val = 0.0;
+  if (x >= 0 && x < vocab) {
+    double ref, s;
+    merged_ref_sum(ws, which * R + o + pu, s_tab, ref, s);
+    const double lse = ref + log(s);
+    const float* prow = (which ? q_logits : p_logits) + (int64_t)(o + pu) * ld;
+    val = exp_f64((double)prow[x] * invT - lse, s_tab);
+  }
+  (which ? ws.cq : ws.cp)[r] = val;
+  if (dst) dst[r] = (float)val;
 }
-
 
 // ---------------------------------------------------------------------------
 // Walk.
@@ -449,6 +459,8 @@ struct WalkShared {
   int kid_list[kMaxRows];
   int path[kMaxRows];
   int toks[kMaxRows + 1];
+  double cp[kMaxRows];              // P_parent(x_c), Q_parent(x_c) of each child row
+  double cq[kMaxRows];
   double tab[256];
   double wave_tot[4][kWalkWaves];   // per unrolled segment, per wave
   double lane_excl[64];             // prefix of the segment sums, per lane block
@@ -804,13 +816,7 @@ SPEC_DEVICE void walk_decide(WalkShared& sh, WalkState& st, const float* p_logit
     }
     const int ch = sh.kid_list[st.kidx];
     const int x = sh.tok[ch];
-    const float* prow = p_logits + (int64_t)(o + u) * ld;
-    const float* qrow = q_logits + (int64_t)(o + u) * ld;
-    double Px = 0.0, Qx = 0.0;
-    if (x >= 0 && x < vocab) {
-      Px = exp_f64((double)prow[x] * invT - lse[o + u], sh.tab);
-      Qx = exp_f64((double)qrow[x] * invT - lse[R + o + u], sh.tab);
-    }
+    const double Px = sh.cp[ch], Qx = sh.cq[ch];
     const double r = verify_uniform(seed, step, (uint64_t)b, (uint64_t)ch, 0);
     const double Rx = fmax(0.0, fma(-st.t, Qx, Px)) / st.N;
     if (r * Qx < Rx) {                   // accept: move to the child
@@ -856,6 +862,11 @@ accept_walk_kernel(const int32_t* __restrict__ row_offsets, int R, int S,
     if (slice == 0) write_bad_tree(out, b, o, n);
     return;
   }
+  for (int i = tid; i < n; i += blockDim.x) {
+    sh.cp[i] = ws.cp[o + i];
+    sh.cq[i] = ws.cq[o + i];
+  }
+  __syncthreads();
   WalkCtx c;
   c.invT = 1.0 / (double)temperature;
   c.vocab = vocab;
