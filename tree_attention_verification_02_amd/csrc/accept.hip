@@ -462,7 +462,8 @@ struct WalkShared {
   double cp[kMaxRows];              // P_parent(x_c), Q_parent(x_c) of each child row
   double cq[kMaxRows];
   double tab[256];
-  double wave_tot[4][kWalkWaves];   // per unrolled segment, per wave
+  double wave_tot[4][kWalkWaves];   // per wave (draw rescan)
+  double half_tot[kWalkWaves / 2][2];  // per segment of a pass round, per half
   double lane_excl[64];             // prefix of the segment sums, per lane block
   double total;
   double c0;
@@ -482,6 +483,15 @@ SPEC_DEVICE double walk_weight(float py, float qy, double invT, double lse_p, do
   const double P = exp_f64((double)py * invT - lse_p, tab);
   if (!need_q) return P;
   const double Q = exp_f64((double)qy * invT - lse_q, tab);
+  return fmax(0.0, fma(-t, Q, P));
+}
+
+// The same weight with the branch-free exponential (streaming passes).
+SPEC_DEVICE double walk_weight_flat(float py, float qy, double invT, double lse_p, double lse_q,
+                                    double t, bool need_q, const double* tab) {
+  const double P = exp_f64_flat((double)py * invT - lse_p, tab);
+  if (!need_q) return P;
+  const double Q = exp_f64_flat((double)qy * invT - lse_q, tab);
   return fmax(0.0, fma(-t, Q, P));
 }
 
@@ -543,6 +553,44 @@ struct WalkCtx {
   int* last;          // this request's [2][kMaxSlices]
 };
 
+// One lane's share of half a segment: kF4 float4 of the target row (and of
+// the draft row when kQ), three float4 ahead in flight.  Indices past the row
+// are clamped (in-bounds loads) and masked to weight 0.
+template <bool kQ, int kF4>
+SPEC_DEVICE void pass_half(const WalkCtx& c, const float4* p4, const float4* q4, int f0, int v4,
+                           double t, const double* tab, double& acc, int& last) {
+  constexpr int kAhead = 3;                          // float4 loads in flight per row
+  float4 pb[kF4], qb[kF4];
+#pragma unroll
+  for (int i = 0; i < kAhead && i < kF4; ++i) {
+    const int f = min(f0 + i * 64, v4 - 1);
+    pb[i] = p4[f];
+    if (kQ) qb[i] = q4[f];
+  }
+#pragma unroll
+  for (int i = 0; i < kF4; ++i) {
+    if (i + kAhead < kF4) {
+      const int f = min(f0 + (i + kAhead) * 64, v4 - 1);
+      pb[i + kAhead] = p4[f];
+      if (kQ) qb[i + kAhead] = q4[f];
+    }
+    const int y0 = (f0 + i * 64) * 4;
+    const float pa[4] = {pb[i].x, pb[i].y, pb[i].z, pb[i].w};
+    float qa[4] = {0.f, 0.f, 0.f, 0.f};
+    if (kQ) {
+      qa[0] = qb[i].x; qa[1] = qb[i].y; qa[2] = qb[i].z; qa[3] = qb[i].w;
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const bool in = y0 + j < c.vocab;              // the row's ragged end
+      const double w = walk_weight_flat(in ? pa[j] : -INFINITY, in ? qa[j] : -INFINITY, c.invT,
+                                        c.lse_p, c.lse_q, t, kQ, tab);
+      acc += w;
+      last = (w > 0.0) ? max(last, y0 + j) : last;
+    }
+  }
+}
+
 // One vocabulary pass: this workgroup's segments of max(0, P - tQ) (or P),
 // then the request barrier, then the ordered total over all segments.
 SPEC_DEVICE double walk_pass(WalkShared& sh, const WalkCtx& c, int* ctr, int pass, double t,
@@ -552,40 +600,28 @@ SPEC_DEVICE double walk_pass(WalkShared& sh, const WalkCtx& c, int* ctr, int pas
   double* seg = c.seg + buf * c.nseg;
   const float4* p4 = reinterpret_cast<const float4*>(c.p);
   const float4* q4 = reinterpret_cast<const float4*>(c.q);
+  // Two waves per segment, each a contiguous half of it: a lane sums its
+  // kHalf/64 weights in registers and the wave reduces once per half.
+  constexpr int kSegsPerRound = kWalkWaves / 2;
+  constexpr int kHalf = kSeg / 2;
+  constexpr int kF4 = kHalf / 256;                   // float4 per lane per half
+  const int v4 = (c.vocab + 3) >> 2;
   int last = -1;
-  constexpr int U = 4;
-  for (int s0 = c.seg_lo; s0 < c.seg_hi; s0 += U) {
-    float4 pv[U], qv[U];
-#pragma unroll
-    for (int k = 0; k < U; ++k) {
-      const int y0 = (s0 + k) * kSeg + 4 * tid;
-      const bool in = (s0 + k < c.seg_hi) && y0 < c.vocab;
-      pv[k] = in ? p4[y0 >> 2] : make_float4(0.f, 0.f, 0.f, 0.f);
-      qv[k] = (in && need_q) ? q4[y0 >> 2] : make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int s0 = c.seg_lo; s0 < c.seg_hi; s0 += kSegsPerRound) {
+    const int sg = s0 + (wave >> 1);
+    double acc = 0.0;
+    if (sg < c.seg_hi) {                             // wave-uniform
+      const int f0 = (sg * kSeg + (wave & 1) * kHalf) / 4 + lane;
+      if (need_q)
+        pass_half<true, kF4>(c, p4, q4, f0, v4, t, sh.tab, acc, last);
+      else
+        pass_half<false, kF4>(c, p4, q4, f0, v4, t, sh.tab, acc, last);
     }
-#pragma unroll
-    for (int k = 0; k < U; ++k) {
-      const int y0 = (s0 + k) * kSeg + 4 * tid;
-      const float pa[4] = {pv[k].x, pv[k].y, pv[k].z, pv[k].w};
-      const float qa[4] = {qv[k].x, qv[k].y, qv[k].z, qv[k].w};
-      double acc = 0.0;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        if (s0 + k < c.seg_hi && y0 + j < c.vocab) {
-          const double w = walk_weight(pa[j], qa[j], c.invT, c.lse_p, c.lse_q, t, need_q, sh.tab);
-          acc += w;
-          if (w > 0.0) last = y0 + j;
-        }
-      }
-      const double incl = wave_incl_scan(acc, lane);
-      if (lane == 63) sh.wave_tot[k][wave] = incl;
-    }
+    const double tot = wave_sum(acc);
+    if (lane == 0) sh.half_tot[wave >> 1][wave & 1] = tot;
     __syncthreads();
-    if (tid < U && s0 + tid < c.seg_hi) {
-      double tot = 0.0;
-      for (int w = 0; w < kWalkWaves; ++w) tot += sh.wave_tot[tid][w];
-      store_shared_d(&seg[s0 + tid], tot);
-    }
+    if (tid < kSegsPerRound && s0 + tid < c.seg_hi)
+      store_shared_d(&seg[s0 + tid], sh.half_tot[tid][0] + sh.half_tot[tid][1]);
     __syncthreads();
   }
 #pragma unroll
