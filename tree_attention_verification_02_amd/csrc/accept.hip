@@ -172,7 +172,6 @@ struct AcceptWs {
   double* cq;       // [R] Q_parent(x_c)
   int32_t* sync;    // [B]   walk barrier counters (zeroed by accept_stats)
   double* seg;      // [B][2][kMaxSegs] per-pass segment sums (double-buffered)
-  int32_t* last;    // [B][2][kMaxSlices] last positive index per slice
 };
 
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -199,8 +198,6 @@ __host__ __device__ inline AcceptWs accept_ws(void* base, int R, int B, int nseg
   w.sync = (int32_t*)p;
   p += align256((size_t)B * sizeof(int32_t));
   w.seg = (double*)p;
-  p += align256((size_t)B * 2 * nseg * sizeof(double));
-  w.last = (int32_t*)p;
   return w;
 }
 
@@ -213,8 +210,7 @@ size_t accept_workspace_bytes(int R, int B, int vocab) {
          align256((size_t)R * kStatChunks * sizeof(float)) +
          align256((size_t)R * kStatChunks * sizeof(int32_t)) +
          2 * align256((size_t)R * sizeof(double)) +
-         align256((size_t)B * sizeof(int32_t)) + align256((size_t)B * 2 * nseg * sizeof(double)) +
-         align256((size_t)B * 2 * kMaxSlices * sizeof(int32_t));
+         align256((size_t)B * sizeof(int32_t)) + align256((size_t)B * 2 * nseg * sizeof(double));
 }
 
 // ---------------------------------------------------------------------------
@@ -468,7 +464,6 @@ struct WalkShared {
   double total;
   double c0;
   int found_seg;
-  int last_pos;
   int pick;
   int bad;
   int timeout;
@@ -505,7 +500,7 @@ SPEC_DEVICE double wave_incl_scan(double v, int lane) {
 }
 
 // Per-request barrier of the S workgroups.  The data exchanged across
-// workgroups (segment sums, last positive index) is written with agent-scope
+// workgroups (segment sums) is written with agent-scope
 // atomic stores and read with agent-scope atomic loads, both coherent at the
 // device level, so no L2 writeback/invalidate is needed: each thread waits
 // for its own stores to complete, then thread 0 arrives on the counter and
@@ -550,7 +545,6 @@ struct WalkCtx {
   double invT, lse_p, lse_q;
   int vocab, nseg, seg_lo, seg_hi, slice, S;
   double* seg;        // this request's [2][nseg]
-  int* last;          // this request's [2][kMaxSlices]
 };
 
 // One lane's share of half a segment: kF4 float4 of the target row (and of
@@ -558,7 +552,7 @@ struct WalkCtx {
 // are clamped (in-bounds loads) and masked to weight 0.
 template <bool kQ, int kF4>
 SPEC_DEVICE void pass_half(const WalkCtx& c, const float4* p4, const float4* q4, int f0, int v4,
-                           double t, const double* tab, double& acc, int& last) {
+                           double t, const double* tab, double& acc) {
   constexpr int kAhead = 3;                          // float4 loads in flight per row
   float4 pb[kF4], qb[kF4];
 #pragma unroll
@@ -586,7 +580,6 @@ SPEC_DEVICE void pass_half(const WalkCtx& c, const float4* p4, const float4* q4,
       const double w = walk_weight_flat(in ? pa[j] : -INFINITY, in ? qa[j] : -INFINITY, c.invT,
                                         c.lse_p, c.lse_q, t, kQ, tab);
       acc += w;
-      last = (w > 0.0) ? max(last, y0 + j) : last;
     }
   }
 }
@@ -606,16 +599,15 @@ SPEC_DEVICE double walk_pass(WalkShared& sh, const WalkCtx& c, int* ctr, int pas
   constexpr int kHalf = kSeg / 2;
   constexpr int kF4 = kHalf / 256;                   // float4 per lane per half
   const int v4 = (c.vocab + 3) >> 2;
-  int last = -1;
   for (int s0 = c.seg_lo; s0 < c.seg_hi; s0 += kSegsPerRound) {
     const int sg = s0 + (wave >> 1);
     double acc = 0.0;
     if (sg < c.seg_hi) {                             // wave-uniform
       const int f0 = (sg * kSeg + (wave & 1) * kHalf) / 4 + lane;
       if (need_q)
-        pass_half<true, kF4>(c, p4, q4, f0, v4, t, sh.tab, acc, last);
+        pass_half<true, kF4>(c, p4, q4, f0, v4, t, sh.tab, acc);
       else
-        pass_half<false, kF4>(c, p4, q4, f0, v4, t, sh.tab, acc, last);
+        pass_half<false, kF4>(c, p4, q4, f0, v4, t, sh.tab, acc);
     }
     const double tot = wave_sum(acc);
     if (lane == 0) sh.half_tot[wave >> 1][wave & 1] = tot;
@@ -624,13 +616,6 @@ SPEC_DEVICE double walk_pass(WalkShared& sh, const WalkCtx& c, int* ctr, int pas
       store_shared_d(&seg[s0 + tid], sh.half_tot[tid][0] + sh.half_tot[tid][1]);
     __syncthreads();
   }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) last = max(last, __shfl_xor(last, o, 64));
-  if (tid == 0) sh.last_pos = -1;
-  __syncthreads();
-  if (lane == 0) atomicMax(&sh.last_pos, last);
-  __syncthreads();
-  if (tid == 0) store_shared_i(&c.last[buf * kMaxSlices + c.slice], sh.last_pos);
   slice_barrier(sh, ctr, pass * c.S, c.S);
   if (wave == 0) {
     const int per = (c.nseg + 63) / 64;
@@ -642,11 +627,6 @@ SPEC_DEVICE double walk_pass(WalkShared& sh, const WalkCtx& c, int* ctr, int pas
     const double incl = wave_incl_scan(part, lane);
     sh.lane_excl[lane] = incl - part;
     if (lane == 63) sh.total = incl;
-    if (lane == 0) {
-      int lp = -1;
-      for (int k = 0; k < c.S; ++k) lp = max(lp, load_shared_i(&c.last[buf * kMaxSlices + k]));
-      sh.last_pos = lp;
-    }
   }
   __syncthreads();
   return sh.total;
@@ -662,35 +642,49 @@ SPEC_DEVICE int walk_draw(WalkShared& sh, const WalkCtx& c, int pass, double t, 
   if (wave == 0) {
     const int per = (c.nseg + 63) / 64;
     double cum = sh.lane_excl[lane];
-    int hit = -1;
-    double hit_c0 = 0.0;
+    int hit = -1, pos = -1;
+    double hit_c0 = 0.0, pos_c0 = 0.0;
     for (int k = 0; k < per; ++k) {
       const int sidx = lane * per + k;
       if (sidx < c.nseg) {
-        const double nxt = cum + load_shared_d(&seg[sidx]);
+        const double v = load_shared_d(&seg[sidx]);
+        const double nxt = cum + v;
         if (hit < 0 && nxt > target) {
           hit = sidx;
           hit_c0 = cum;
+        }
+        if (v > 0.0) {
+          pos = sidx;
+          pos_c0 = cum;
         }
         cum = nxt;
       }
     }
     const uint64_t ball = __ballot(hit >= 0);
-    if (lane == 0) {
-      sh.found_seg = -1;
-      sh.pick = -1;
-    }
+    const uint64_t pball = __ballot(pos >= 0);
+    if (lane == 0) sh.pick = -1;
     if (ball) {
       const int first = __ffsll((long long)ball) - 1;
       if (lane == first) {
         sh.found_seg = hit;
         sh.c0 = hit_c0;
       }
+    } else if (pball) {
+      // rounding left the target past the last cumulative sum: the last
+      // segment holding a positive weight, whose rescan then returns its last
+      // positive weight (the last one of the row)
+      const int lastl = 63 - __clzll((long long)pball);
+      if (lane == lastl) {
+        sh.found_seg = pos;
+        sh.c0 = pos_c0;
+      }
+    } else if (lane == 0) {
+      sh.found_seg = -1;
     }
   }
   __syncthreads();
   const int fs = sh.found_seg;
-  if (fs < 0) return (c.slice == 0) ? sh.last_pos : -1;   // rounding: last positive weight
+  if (fs < 0) return -1;                             // no positive weight (not reached)
   if (fs < c.seg_lo || fs >= c.seg_hi) return -1;
   // rescan the segment with the same arithmetic as the pass
   const int y0 = fs * kSeg + 4 * tid;
@@ -731,7 +725,6 @@ SPEC_DEVICE int walk_draw(WalkShared& sh, const WalkCtx& c, int pass, double t, 
     if (lastpos >= 0) atomicMax(&sh.pick, lastpos);
     __syncthreads();
     res = sh.pick;
-    if (res < 0) res = sh.last_pos;
   }
   return res;
 }
@@ -913,7 +906,6 @@ accept_walk_kernel(const int32_t* __restrict__ row_offsets, int R, int S,
   c.slice = slice;
   c.S = S;
   c.seg = ws.seg + (size_t)b * 2 * c.nseg;
-  c.last = ws.last + (size_t)b * 2 * kMaxSlices;
   int* ctr = ws.sync + b;
   if (tid == 0) {
     sh.len = 1;
