@@ -140,7 +140,25 @@ SPEC_DEVICE double exp_f64(double x, const double* tab) {
   const double scale = __longlong_as_double((long long)((ki >> 8) + 1023) << 52);
   return fma(s, p, s) * scale;
 }
-// The same value without a branch (for unrolled streaming loops).
+// The same value for -708 <= x <= 709 only, without the range handling.
+SPEC_DEVICE double exp_f64_raw(double x, const double* tab) {
+  constexpr double kShift = 0x1.8p52;
+  const double t = fma(x, kInvLn2x256, kShift);
+  const double k = t - kShift;
+  const int ki = (int)(uint32_t)__double_as_longlong(t);
+  const double r = fma(-k, kLn2by256Lo, fma(-k, kLn2by256Hi, x));
+  const double p = r * fma(r, fma(r, fma(r, 1.0 / 24, 1.0 / 6), 0.5), 1.0);
+  const double s = tab[ki & 255];
+  const double scale = __longlong_as_double((long long)((ki >> 8) + 1023) << 52);
+  return fma(s, p, s) * scale;
+}
+// Streaming sums: arguments below -708 give e^-708 (about 3e-308) instead of
+// a smaller value or 0 -- invisible in any sum of weights whose total is a
+// probability mass (the draws rescan their segment with exp_f64).
+SPEC_DEVICE double exp_f64_clamped(double x, const double* tab) {
+  return exp_f64_raw(fmax(x, -708.0), tab);
+}
+// The same value as exp_f64 without a branch (for unrolled streaming loops).
 SPEC_DEVICE double exp_f64_flat(double x, const double* tab) {
   const bool under = !(x >= -708.0);
   x = under ? -708.0 : x;
@@ -577,9 +595,14 @@ SPEC_DEVICE void pass_half(const WalkCtx& c, const float4* p4, const float4* q4,
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const bool in = y0 + j < c.vocab;              // the row's ragged end
-      const double w = walk_weight_flat(in ? pa[j] : -INFINITY, in ? qa[j] : -INFINITY, c.invT,
-                                        c.lse_p, c.lse_q, t, kQ, tab);
-      acc += w;
+      const double P = exp_f64_clamped((double)(in ? pa[j] : -INFINITY) * c.invT - c.lse_p, tab);
+      if (kQ) {
+        const double Q =
+            exp_f64_clamped((double)(in ? qa[j] : -INFINITY) * c.invT - c.lse_q, tab);
+        acc += fmax(0.0, fma(-t, Q, P));
+      } else {
+        acc += P;
+      }
     }
   }
 }
