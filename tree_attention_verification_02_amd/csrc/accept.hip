@@ -40,7 +40,8 @@
 namespace spec {
 
 constexpr int kStatThreads = 256;
-constexpr int kStatChunks = 8;               // workgroups per logits row
+constexpr int kStatF4 = 16;                   // float4 per thread per statistics chunk
+constexpr int kStatChunkLen = kStatThreads * kStatF4 * 4;   // logits per chunk
 constexpr int kWalkThreads = 1024;
 constexpr int kWalkWaves = kWalkThreads / 64;
 constexpr int kSeg = kWalkThreads * 4;        // elements per segment
@@ -182,9 +183,10 @@ SPEC_DEVICE void load_exp_table(double* s_tab) {
 struct AcceptWs {
   double* lse;      // [2][R] log-sum-exp of logits / T (target rows, draft rows)
   int32_t* am;      // [R]   first argmax of the target row (greedy)
-  double* part_ref; // [2][R][kStatChunks] chunk partials: reference
+  int nch;          // statistics chunks per row
+  double* part_ref; // [2][R][nch] chunk partials: reference
   double* part_s;   //                     and sum of exp(z - reference)
-  float* part_m;    // [R][kStatChunks]    chunk max (greedy)
+  float* part_m;    // [R][nch]    chunk max (greedy)
   int32_t* part_am; //                     and its first index
   double* cp;       // [R] P_parent(x_c) of each child row c (fp64, sampling)
   double* cq;       // [R] Q_parent(x_c)
@@ -194,21 +196,27 @@ struct AcceptWs {
 
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-__host__ __device__ inline AcceptWs accept_ws(void* base, int R, int B, int nseg) {
+__host__ __device__ inline int stat_chunks(int vocab) {
+  return (vocab + kStatChunkLen - 1) / kStatChunkLen;
+}
+
+__host__ __device__ inline AcceptWs accept_ws(void* base, int R, int B, int vocab) {
+  const int nch = stat_chunks(vocab);
   char* p = (char*)base;
   AcceptWs w;
+  w.nch = nch;
   w.lse = (double*)p;
   p += align256(2 * (size_t)R * sizeof(double));
   w.am = (int32_t*)p;
   p += align256((size_t)R * sizeof(int32_t));
   w.part_ref = (double*)p;
-  p += align256(2 * (size_t)R * kStatChunks * sizeof(double));
+  p += align256(2 * (size_t)R * nch * sizeof(double));
   w.part_s = (double*)p;
-  p += align256(2 * (size_t)R * kStatChunks * sizeof(double));
+  p += align256(2 * (size_t)R * nch * sizeof(double));
   w.part_m = (float*)p;
-  p += align256((size_t)R * kStatChunks * sizeof(float));
+  p += align256((size_t)R * nch * sizeof(float));
   w.part_am = (int32_t*)p;
-  p += align256((size_t)R * kStatChunks * sizeof(int32_t));
+  p += align256((size_t)R * nch * sizeof(int32_t));
   w.cp = (double*)p;
   p += align256((size_t)R * sizeof(double));
   w.cq = (double*)p;
@@ -223,10 +231,11 @@ static int segs_for(int vocab) { return (vocab + kSeg - 1) / kSeg; }
 
 size_t accept_workspace_bytes(int R, int B, int vocab) {
   const int nseg = segs_for(vocab);
+  const int nch = stat_chunks(vocab);
   return align256(2 * (size_t)R * sizeof(double)) + align256((size_t)R * sizeof(int32_t)) +
-         2 * align256(2 * (size_t)R * kStatChunks * sizeof(double)) +
-         align256((size_t)R * kStatChunks * sizeof(float)) +
-         align256((size_t)R * kStatChunks * sizeof(int32_t)) +
+         2 * align256(2 * (size_t)R * nch * sizeof(double)) +
+         align256((size_t)R * nch * sizeof(float)) +
+         align256((size_t)R * nch * sizeof(int32_t)) +
          2 * align256((size_t)R * sizeof(double)) +
          align256((size_t)B * sizeof(int32_t)) + align256((size_t)B * 2 * nseg * sizeof(double));
 }
@@ -251,11 +260,13 @@ SPEC_DEVICE void merge_arg(float& m, int& am, float m2, int am2) {
   }
 }
 
-// Partial statistics of one (row, chunk): the row is cut into kStatChunks
-// equal pieces so that rows of 128K logits spread evenly over the CUs.
-//  * sampling: (reference, sum of exp(z - reference)) with z = logit / T, in
-//    fp64; the reference follows the running maximum, moved at most once per
-//    16 logits, so the per-logit work is branch-free.
+// Partial statistics of one (row, chunk).  A chunk is kStatF4 float4 per
+// thread (16K logits), held in registers: the row is cut into
+// ws.nch = ceil(V / 16K) chunks so that rows of 128K logits spread over the
+// CUs, and every load of a chunk is in flight at once.
+//  * sampling: (reference, sum of exp(z - reference)) with z = logit / T in
+//    fp64 and the chunk's maximum as the reference, so every exponent is
+//    <= 0 and the per-logit work is branch-free.
 //  * greedy: (max, first argmax) of the target row.
 // Draft rows of leaves are not read (their partials are left empty).
 template <bool kGreedy>
@@ -267,15 +278,15 @@ accept_stats_kernel(const int32_t* __restrict__ row_offsets, int B, int R,
   __shared__ double s_tab[256];
   __shared__ float red_m[kStatThreads / 64];
   __shared__ int red_a[kStatThreads / 64];
-  __shared__ double red_r[kStatThreads / 64];
   __shared__ double red_s[kStatThreads / 64];
   __shared__ int has_kids;
-  const int chunk = blockIdx.x % kStatChunks;
-  const int rr = blockIdx.x / kStatChunks;
+  const int nch = ws.nch;
+  const int chunk = blockIdx.x % nch;
+  const int rr = blockIdx.x / nch;
   const int which = rr >= R ? 1 : 0;                   // 0: target p, 1: draft q
   const int r = rr - which * R;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int slot = rr * kStatChunks + chunk;
+  const int slot = rr * nch + chunk;
   if (blockIdx.x == 0)
     for (int i = tid; i < B; i += kStatThreads) ws.sync[i] = 0;
   if (!kGreedy) load_exp_table(s_tab);
@@ -300,31 +311,31 @@ accept_stats_kernel(const int32_t* __restrict__ row_offsets, int B, int R,
   const float* row = (which ? q_logits : p_logits) + (int64_t)r * ld;
   const float4* row4 = reinterpret_cast<const float4*>(row);
   const int v4 = (vocab + 3) >> 2;
-  const int per = (v4 + kStatChunks - 1) / kStatChunks;
-  const int f_begin = chunk * per;
-  const int f_end = min(v4, f_begin + per);
-  constexpr int U = 4;
+  const int f_begin = chunk * (kStatThreads * kStatF4);
+  // the whole chunk in flight: clamped (in-bounds) loads, masked to -inf
+  float4 x[kStatF4];
+#pragma unroll
+  for (int k = 0; k < kStatF4; ++k) x[k] = row4[min(f_begin + k * kStatThreads + tid, v4 - 1)];
+#pragma unroll
+  for (int k = 0; k < kStatF4; ++k) {
+    const int y0 = (f_begin + k * kStatThreads + tid) * 4;
+    if (y0 + 0 >= vocab) x[k].x = -INFINITY;
+    if (y0 + 1 >= vocab) x[k].y = -INFINITY;
+    if (y0 + 2 >= vocab) x[k].z = -INFINITY;
+    if (y0 + 3 >= vocab) x[k].w = -INFINITY;
+  }
   if (kGreedy) {
     float m = -INFINITY;
     int am = -1;
-    for (int f0 = f_begin + tid; f0 < f_end; f0 += kStatThreads * U) {
-      float4 x[U];
 #pragma unroll
-      for (int k = 0; k < U; ++k) {
-        const int f = f0 + k * kStatThreads;
-        x[k] = (f < f_end) ? row4[f] : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
-      }
+    for (int k = 0; k < kStatF4; ++k) {              // a thread's indices increase with k
+      const int y0 = (f_begin + k * kStatThreads + tid) * 4;
+      const float xs[4] = {x[k].x, x[k].y, x[k].z, x[k].w};
 #pragma unroll
-      for (int k = 0; k < U; ++k) {
-        const int y0 = (f0 + k * kStatThreads) * 4;
-        const float xs[4] = {x[k].x, x[k].y, x[k].z, x[k].w};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float xv = (y0 + j < vocab) ? xs[j] : -INFINITY;
-          const bool gt = xv > m;                  // strict: the first index wins ties
-          m = gt ? xv : m;
-          am = gt ? y0 + j : am;
-        }
+      for (int j = 0; j < 4; ++j) {
+        const bool gt = xs[j] > m;                   // strict: the first index wins ties
+        m = gt ? xs[j] : m;
+        am = gt ? y0 + j : am;
       }
     }
 #pragma unroll
@@ -342,52 +353,32 @@ accept_stats_kernel(const int32_t* __restrict__ row_offsets, int B, int R,
     }
     return;
   }
+  float cm = -INFINITY;
+#pragma unroll
+  for (int k = 0; k < kStatF4; ++k)
+    cm = fmaxf(cm, fmaxf(fmaxf(x[k].x, x[k].y), fmaxf(x[k].z, x[k].w)));
+  cm = wave_max(cm);
+  if (lane == 0) red_m[wave] = cm;
+  __syncthreads();
+  for (int w = 0; w < kStatThreads / 64; ++w) cm = fmaxf(cm, red_m[w]);
   const double invT = 1.0 / (double)temperature;
-  double ref = -INFINITY;
+  const double ref = (cm == -INFINITY) ? 0.0 : (double)cm * invT;
   double s = 0.0;
-  for (int f0 = f_begin + tid; f0 < f_end; f0 += kStatThreads * U) {
-    float4 x[U];
 #pragma unroll
-    for (int k = 0; k < U; ++k) {
-      const int f = f0 + k * kStatThreads;
-      x[k] = (f < f_end) ? row4[f] : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
-    }
-    float cm = -INFINITY;
-#pragma unroll
-    for (int k = 0; k < U; ++k) {
-      const int y0 = (f0 + k * kStatThreads) * 4;
-      if (y0 + 3 >= vocab) {                       // the row's ragged end
-        if (y0 + 1 >= vocab) x[k].y = -INFINITY;
-        if (y0 + 2 >= vocab) x[k].z = -INFINITY;
-        if (y0 + 3 >= vocab) x[k].w = -INFINITY;
-      }
-      cm = fmaxf(cm, fmaxf(fmaxf(x[k].x, x[k].y), fmaxf(x[k].z, x[k].w)));
-    }
-    const double cmd = (double)cm * invT;
-    if (cmd > ref + 64.0) {                        // first values, or a much larger one
-      s = (ref == -INFINITY) ? 0.0 : s * exp_f64(ref - cmd, s_tab);
-      ref = cmd;
-    }
-#pragma unroll
-    for (int k = 0; k < U; ++k) {
-      s += exp_f64_flat(fma((double)x[k].x, invT, -ref), s_tab);
-      s += exp_f64_flat(fma((double)x[k].y, invT, -ref), s_tab);
-      s += exp_f64_flat(fma((double)x[k].z, invT, -ref), s_tab);
-      s += exp_f64_flat(fma((double)x[k].w, invT, -ref), s_tab);
-    }
+  for (int k = 0; k < kStatF4; ++k) {
+    s += exp_f64_clamped(fma((double)x[k].x, invT, -ref), s_tab);
+    s += exp_f64_clamped(fma((double)x[k].y, invT, -ref), s_tab);
+    s += exp_f64_clamped(fma((double)x[k].z, invT, -ref), s_tab);
+    s += exp_f64_clamped(fma((double)x[k].w, invT, -ref), s_tab);
   }
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1)
-    merge_ref(ref, s, __shfl_xor(ref, off, 64), __shfl_xor(s, off, 64), s_tab);
-  if (lane == 0) {
-    red_r[wave] = ref;
-    red_s[wave] = s;
-  }
+  s = wave_sum(s);
+  if (lane == 0) red_s[wave] = s;
   __syncthreads();
   if (tid == 0) {
-    for (int w = 1; w < kStatThreads / 64; ++w) merge_ref(ref, s, red_r[w], red_s[w], s_tab);
+    double tot = 0.0;
+    for (int w = 0; w < kStatThreads / 64; ++w) tot += red_s[w];
     ws.part_ref[slot] = ref;
-    ws.part_s[slot] = s;
+    ws.part_s[slot] = tot;
   }
 }
 
@@ -398,16 +389,18 @@ accept_stats_kernel(const int32_t* __restrict__ row_offsets, int B, int R,
 // One thread per (row, target|draft).
 SPEC_DEVICE void merged_ref_sum(const AcceptWs& ws, int rr, const double* tab, double& ref,
                                 double& s) {
-  ref = ws.part_ref[rr * kStatChunks];
-  s = ws.part_s[rr * kStatChunks];
-  for (int c = 1; c < kStatChunks; ++c)
-    merge_ref(ref, s, ws.part_ref[rr * kStatChunks + c], ws.part_s[rr * kStatChunks + c], tab);
+  const int nch = ws.nch;
+  ref = ws.part_ref[rr * nch];
+  s = ws.part_s[rr * nch];
+  for (int c = 1; c < nch; ++c)
+    merge_ref(ref, s, ws.part_ref[rr * nch + c], ws.part_s[rr * nch + c], tab);
 }
 SPEC_DEVICE int merged_argmax(const AcceptWs& ws, int r) {
-  float m = ws.part_m[r * kStatChunks];
-  int am = ws.part_am[r * kStatChunks];
-  for (int c = 1; c < kStatChunks; ++c)
-    merge_arg(m, am, ws.part_m[r * kStatChunks + c], ws.part_am[r * kStatChunks + c]);
+  const int nch = ws.nch;
+  float m = ws.part_m[r * nch];
+  int am = ws.part_am[r * nch];
+  for (int c = 1; c < nch; ++c)
+    merge_arg(m, am, ws.part_m[r * nch + c], ws.part_am[r * nch + c]);
   return am;
 }
 
@@ -1060,15 +1053,16 @@ hipError_t launch_accept(const LaunchCtx& cx, int R, const int32_t* parents, con
                          void* workspace, int slices_override) {
   static_assert(sizeof(WalkShared) < 20480, "walk LDS");
   const int nseg = segs_for(vocab);
-  AcceptWs ws = accept_ws(workspace, R, cx.B, nseg);
+  AcceptWs ws = accept_ws(workspace, R, cx.B, vocab);
+  const int nch = ws.nch;
   const bool greedy = temperature == 0.0f;
   const int rows = greedy ? R : 2 * R;
   if (greedy)
-    hipLaunchKernelGGL(accept_stats_kernel<true>, dim3(rows * kStatChunks), dim3(kStatThreads), 0,
+    hipLaunchKernelGGL(accept_stats_kernel<true>, dim3(rows * nch), dim3(kStatThreads), 0,
                        cx.stream, cx.row_offsets_d, cx.B, R, parents, p_logits, q_logits, ld, vocab,
                        temperature, ws);
   else
-    hipLaunchKernelGGL(accept_stats_kernel<false>, dim3(rows * kStatChunks), dim3(kStatThreads), 0,
+    hipLaunchKernelGGL(accept_stats_kernel<false>, dim3(rows * nch), dim3(kStatThreads), 0,
                        cx.stream, cx.row_offsets_d, cx.B, R, parents, p_logits, q_logits, ld, vocab,
                        temperature, ws);
   hipLaunchKernelGGL(accept_finalize_kernel, dim3((rows + 255) / 256), dim3(256), 0, cx.stream,
