@@ -96,14 +96,15 @@ kv_commit_kernel(const int32_t* __restrict__ row_offsets, const int32_t* __restr
   __shared__ int ok;
   __shared__ int pth[kMaxRows];
   const int a = accept_len[b];
+  // the path row is read together with accept_len (one memory round trip)
+  for (int k = threadIdx.x; k < path_stride && k < kMaxRows; k += blockDim.x)
+    pth[k] = path[(int64_t)b * path_stride + k];
   if (threadIdx.x == 0) ok = (a >= 0 && a < n && a < path_stride) ? 1 : 0;
   __syncthreads();
   if (!ok) {
     if (h == 0 && threadIdx.x == 0) new_len[b] = -1;
     return;
   }
-  for (int k = threadIdx.x; k <= a; k += blockDim.x) pth[k] = path[(int64_t)b * path_stride + k];
-  __syncthreads();
   if (threadIdx.x == 0) {
     int good = (pth[0] == 0);
     for (int k = 1; k <= a; ++k) good &= (pth[k] > pth[k - 1] && pth[k] < n);
