@@ -180,3 +180,27 @@ def test_error_string_is_thread_local():
     t.join()
     assert seen["msg"] == ""
     assert "row_offsets" in _err()
+
+
+def test_attention_rejects_requests_beyond_the_split_limit():
+    # 8192-key splits, at most 1024 of them per request: 8,388,608 keys
+    limit = 8192 * 1024
+    ok = _B([0, 3], [limit - 3])
+    kv = _kv(cap=limit)
+    assert L.LIB.spec_tree_attn_workspace_bytes(ctypes.byref(ok.c), ctypes.byref(kv), 4) > 0
+    big = _B([0, 3], [limit - 2])
+    kv = _kv(cap=limit + 1)
+    assert L.LIB.spec_tree_attn_workspace_bytes(ctypes.byref(big.c), ctypes.byref(kv), 4) == 0
+    assert "keys" in _err()
+    assert _attn(big, kv) == 7
+
+
+def test_attention_workspace_grows_with_splits_only():
+    # one short request: a single split, no partials to keep
+    small = _B([0, 5], [100])
+    kv = _kv(cap=256)
+    one = L.LIB.spec_tree_attn_workspace_bytes(ctypes.byref(small.c), ctypes.byref(kv), 4)
+    longer = _B([0, 5], [200000])
+    kv2 = _kv(cap=300000)
+    many = L.LIB.spec_tree_attn_workspace_bytes(ctypes.byref(longer.c), ctypes.byref(kv2), 4)
+    assert 0 < one < many

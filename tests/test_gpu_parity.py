@@ -88,6 +88,19 @@ def test_fp32_output_of_bf16_path(lib):
     log(f"[parity] fp32-out bf16 path max|d| = {worst:.3e}")
 
 
+def test_large_batch_in_request_order(lib):
+    """More than 512 requests: the attention grid keeps request order (no
+    longest-first phase), and one workspace holds every request's rows."""
+    w = make("dynamic", B=600, L=("uniform", 20, 400), V=1500)
+    vs = run_step(w, temperature=1.0, seed=3, step=2)
+    check_mask(w, vs)
+    req = [0, 1, 255, 511, 512, 598, 599]
+    worst = check_attention(w, vs, requests=req)
+    log(f"[parity] B=600: attention max|d| = {worst:.3e} on requests {req}")
+    check_accept(w, vs, 1.0, 3, 2)
+    check_commit(w, vs, requests=req, heads=[0, w.Hkv - 1])
+
+
 def test_deterministic(lib):
     w = make("dynamic", **SMALL["dynamic-small"])
     a = run_step(w, commit=False)

@@ -851,9 +851,9 @@ AttnPlan plan_attention(int B, const int32_t* row_offsets_h, const int32_t* pref
   // One workgroup per CU at a time: aim at ~4 workgroups per CU (256 CUs),
   // splits of at least 256 keys and at most kMaxSplitsCombine per request.
   const int64_t target = 1024;
-  int64_t split = (work + target - 1) / target;
-  split = std::max<int64_t>(split, (max_keys + kMaxSplitsCombine - 1) / kMaxSplitsCombine);
-  split = ((split + kTileKeys - 1) / kTileKeys) * kTileKeys;
+  auto round_up = [](int64_t x) { return ((x + kTileKeys - 1) / kTileKeys) * kTileKeys; };
+  int64_t split = std::min<int64_t>(round_up((work + target - 1) / target), kMaxSplit);
+  split = std::max<int64_t>(split, round_up((max_keys + kMaxSplitsCombine - 1) / kMaxSplitsCombine));
   if (split < 256) split = 256;
   p.units = units;
   p.items = 0;
