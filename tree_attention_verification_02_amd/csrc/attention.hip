@@ -649,16 +649,15 @@ __global__ void __launch_bounds__(kWaves * 64, 1) attn_bf16_kernel(AttnArgs a) {
 }
 
 // Merge split partials.  One workgroup per 32 query rows of one (request, KV
-// head, row block): 8 threads per row find the row's maximum and weighted sum
-// over the splits, then each thread accumulates float4 columns of four rows,
-// split after split (coalesced 512-byte rows of partials).
+// head, row block); each thread merges one float4 column of a row over the
+// splits in one pass with a running maximum (coalesced 512-byte rows of
+// partials; weights exp2(m_s - m)).
 template <int D>
 __global__ void __launch_bounds__(256) attn_combine_kernel(AttnArgs a) {
   constexpr int ROWS = kWaves * kRowsPerWave;
   constexpr int CHUNKS = ROWS / kCombineRows;
   constexpr int C4 = D / 4;                        // float4 per row
   constexpr int RPI = 256 / C4;                    // rows per pass of the block
-  __shared__ float s_m[kCombineRows], s_inv[kCombineRows];
   const int64_t unit = blockIdx.x / CHUNKS;
   const int chunk = blockIdx.x % CHUNKS;
   int b;
@@ -691,46 +690,32 @@ __global__ void __launch_bounds__(256) attn_combine_kernel(AttnArgs a) {
   }
   __syncthreads();
   const float2* ml = reinterpret_cast<const float2*>(a.part_ml);
-
-  {  // per-row maximum and weighted sum: 8 threads per row, splits strided
-    const int r = threadIdx.x >> 3, j = threadIdx.x & 7;
-    float mx = -INFINITY;
-    if (r < rows)
-      for (int s = j; s < ns; s += 8) mx = fmaxf(mx, ml[s_item[s] * ROWS + r0 + r].x);
-    mx = fmaxf(mx, __shfl_xor(mx, 1, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 2, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 4, 64));
-    const float ref = (mx == -INFINITY) ? 0.0f : mx;
-    float l = 0.0f;
-    if (r < rows)
-      for (int s = j; s < ns; s += 8) {
-        const float2 v = ml[s_item[s] * ROWS + r0 + r];
-        l += v.y * __builtin_amdgcn_exp2f(v.x - ref);
-      }
-    l += __shfl_xor(l, 1, 64);
-    l += __shfl_xor(l, 2, 64);
-    l += __shfl_xor(l, 4, 64);
-    if (j == 0 && r < kCombineRows) {
-      s_m[r] = ref;
-      s_inv[r] = 1.0f / l;
-    }
-  }
-  __syncthreads();
+  // One pass over the splits per (row, float4 column), with a running
+  // maximum: all of a thread's partial loads are independent.
   const int c4 = threadIdx.x % C4;
   const int rsub = threadIdx.x / C4;
 #pragma unroll
   for (int rp = 0; rp < kCombineRows / RPI; ++rp) {
     const int r = rp * RPI + rsub;
     if (r >= rows) break;
-    const float ref = s_m[r];
+    float mx = -INFINITY, l = 0.0f;
     float4 accv = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 4
     for (int s = 0; s < ns; ++s) {
       const int64_t pr = s_item[s] * ROWS + r0 + r;
-      const float wgt = __builtin_amdgcn_exp2f(ml[pr].x - ref);
+      const float2 v = ml[pr];
       const float4 pv = *reinterpret_cast<const float4*>(a.part + pr * D + c4 * 4);
+      if (v.x > mx) {                                // new maximum: rescale what is summed
+        const float sc = (mx == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mx - v.x);
+        accv.x *= sc; accv.y *= sc; accv.z *= sc; accv.w *= sc;
+        l *= sc;
+        mx = v.x;
+      }
+      const float wgt = (v.x == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(v.x - mx);
+      l += v.y * wgt;
       accv.x += pv.x * wgt; accv.y += pv.y * wgt; accv.z += pv.z * wgt; accv.w += pv.w * wgt;
     }
-    const float inv = s_inv[r];
+    const float inv = 1.0f / l;
     const int grow = rb * ROWS + r0 + r;
     const int ti = grow / a.G;
     const int hh = kvh * a.G + grow % a.G;
