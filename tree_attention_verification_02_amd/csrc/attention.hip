@@ -62,6 +62,9 @@ struct AttnArgs {
   int rows_per_block;
   float* part;       // [items][rows_per_block][D] unnormalised outputs
   float* part_ml;    // [items][rows_per_block][2]  (running max, running sum)
+  int* unit_desc;    // [units][8]: b, kvh, rb, ns, o, rows of the block (main kernel writes)
+  int* unit_items;   // [units][max_ns]: item of each split of the unit
+  int max_ns;
   int lpt;           // two-phase (longest-first) item order, see AttnPlan
   int64_t items_a;   // items of the first phase
   uint16_t order[kLptMax];
@@ -436,6 +439,20 @@ SPEC_DEVICE void compute_half(const uint16_t* ks, const uint16_t* vs, int hk, in
   }
 }
 
+// First (request, KV head, row block) unit of request b: units of all
+// earlier requests, in request order.  Wave-parallel; uniform.
+SPEC_DEVICE int64_t unit_base(const AttnArgs& a, int b) {
+  const int lane = threadIdx.x & 63;
+  int64_t cnt = 0;
+  for (int base = 0; base < b; base += 64) {
+    const int bq = base + lane;
+    if (bq < b)
+      cnt += (int64_t)a.addr.hkv *
+             attn_row_blocks(a.row_offsets[bq + 1] - a.row_offsets[bq], a.G, a.rows_per_block);
+  }
+  return wave_sum(cnt);
+}
+
 // Main kernel: one workgroup of 8 waves per (request, KV head, block of up
 // to 256 query rows, key split).  Query rows form groups of 32 (one wave's
 // MFMA columns).  With at most 4 groups, two waves share a group and each
@@ -472,6 +489,22 @@ __global__ void __launch_bounds__(kWaves * 64, 1) attn_bf16_kernel(AttnArgs a) {
   const int key_end = __builtin_amdgcn_readfirstlane(min(key_begin + a.split, total_keys));
   const int M = n * a.G;
 
+  if (a.max_ns > 1) {
+    // the combine finds each unit's splits here (no search over requests)
+    const int64_t unit = unit_base(a, b) + (int64_t)kvh * attn_row_blocks(n, a.G, ROWS) + rb;
+    if (tid == 0) {
+      a.unit_items[unit * a.max_ns + s] = (int)item;
+      if (s == 0) {
+        int* d = a.unit_desc + unit * 8;
+        d[0] = b;
+        d[1] = kvh;
+        d[2] = rb;
+        d[3] = ns;
+        d[4] = o;
+        d[5] = min(ROWS, M - rb * ROWS);
+      }
+    }
+  }
   const int groups = (min(ROWS, M - rb * ROWS) + kRowsPerWave - 1) / kRowsPerWave;
   const bool pair = groups <= kWaves / 2;
   const int g = pair ? (wave >> 1) : wave;
@@ -660,73 +693,70 @@ __global__ void __launch_bounds__(256) attn_combine_kernel(AttnArgs a) {
   constexpr int RPI = 256 / C4;                    // rows per pass of the block
   const int64_t unit = blockIdx.x / CHUNKS;
   const int chunk = blockIdx.x % CHUNKS;
-  int b;
-  int64_t ubase;
-  locate<true>(unit, a, b, ubase);
-  if (b < 0) return;
-  const int o = a.row_offsets[b];
-  const int n = a.row_offsets[b + 1] - o;
-  const int L = a.prefix_len[b];
-  const int ns = attn_splits(L + n, a.split);
+  const int4 d0 = *reinterpret_cast<const int4*>(a.unit_desc + unit * 8);
+  const int2 d1 = *reinterpret_cast<const int2*>(a.unit_desc + unit * 8 + 4);
+  const int kvh = d0.y, rb = d0.z, ns = d0.w, o = d1.x, m_blk = d1.y;
   if (ns == 1) return;
-  const int nrb = attn_row_blocks(n, a.G, ROWS);
-  const int M = n * a.G;
-  const int64_t u = unit - ubase;                  // kvh * nrb + rb
-  const int rb = (int)(u % nrb);
-  const int kvh = (int)(u / nrb);
   const int r0 = chunk * kCombineRows;             // first row (within the block)
-  const int rows = min(kCombineRows, min(ROWS, M - rb * ROWS) - r0);
+  const int rows = min(kCombineRows, m_blk - r0);
   if (rows <= 0) return;
-  // Item of each split of this unit, kept in LDS for the loops below.
-  __shared__ int64_t s_item[kMaxSplitsCombine];
-  if (ns > kMaxSplitsCombine) return;      // excluded by the planner
-  if (threadIdx.x < 64) {
-    const int64_t first = item_of(a, b, u, ns, 0);
-    for (int sp = threadIdx.x; sp < ns - a.lpt; sp += 64) s_item[sp] = first + sp;
-    if (a.lpt) {
-      const int64_t last = item_of(a, b, u, ns, ns - 1);
-      if (threadIdx.x == 0) s_item[ns - 1] = last;
-    }
-  }
+  // Item of each split of this unit, kept in LDS for the loop below.
+  __shared__ int s_item[kMaxSplitsCombine];
+  for (int sp = threadIdx.x; sp < ns; sp += blockDim.x) s_item[sp] = a.unit_items[unit * a.max_ns + sp];
   __syncthreads();
   const float2* ml = reinterpret_cast<const float2*>(a.part_ml);
   // One pass over the splits per (row, float4 column), with a running
-  // maximum: all of a thread's partial loads are independent.
+  // maximum.  A thread owns one column of kCombineRows / RPI rows; their
+  // loads are unconditional (row index clamped) so that all of them are in
+  // flight together.
+  constexpr int NP = kCombineRows / RPI;
   const int c4 = threadIdx.x % C4;
   const int rsub = threadIdx.x / C4;
+  float mx[NP], l[NP];
+  float4 accv[NP];
 #pragma unroll
-  for (int rp = 0; rp < kCombineRows / RPI; ++rp) {
-    const int r = rp * RPI + rsub;
-    if (r >= rows) break;
-    float mx = -INFINITY, l = 0.0f;
-    float4 accv = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll 4
-    for (int s = 0; s < ns; ++s) {
-      const int64_t pr = s_item[s] * ROWS + r0 + r;
+  for (int rp = 0; rp < NP; ++rp) {
+    mx[rp] = -INFINITY;
+    l[rp] = 0.0f;
+    accv[rp] = make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+#pragma unroll 2
+  for (int s = 0; s < ns; ++s) {
+    const int64_t base = (int64_t)s_item[s] * ROWS + r0;
+#pragma unroll
+    for (int rp = 0; rp < NP; ++rp) {
+      const int64_t pr = base + min(rp * RPI + rsub, rows - 1);
       const float2 v = ml[pr];
       const float4 pv = *reinterpret_cast<const float4*>(a.part + pr * D + c4 * 4);
-      if (v.x > mx) {                                // new maximum: rescale what is summed
-        const float sc = (mx == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mx - v.x);
-        accv.x *= sc; accv.y *= sc; accv.z *= sc; accv.w *= sc;
-        l *= sc;
-        mx = v.x;
+      if (v.x > mx[rp]) {                            // new maximum: rescale what is summed
+        const float sc = (mx[rp] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mx[rp] - v.x);
+        accv[rp].x *= sc; accv[rp].y *= sc; accv[rp].z *= sc; accv[rp].w *= sc;
+        l[rp] *= sc;
+        mx[rp] = v.x;
       }
-      const float wgt = (v.x == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(v.x - mx);
-      l += v.y * wgt;
-      accv.x += pv.x * wgt; accv.y += pv.y * wgt; accv.z += pv.z * wgt; accv.w += pv.w * wgt;
+      const float wgt = (v.x == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(v.x - mx[rp]);
+      l[rp] += v.y * wgt;
+      accv[rp].x += pv.x * wgt; accv[rp].y += pv.y * wgt;
+      accv[rp].z += pv.z * wgt; accv[rp].w += pv.w * wgt;
     }
-    const float inv = 1.0f / l;
+  }
+#pragma unroll
+  for (int rp = 0; rp < NP; ++rp) {
+    const int r = rp * RPI + rsub;
+    if (r >= rows) break;
+    const float inv = 1.0f / l[rp];
     const int grow = rb * ROWS + r0 + r;
     const int ti = grow / a.G;
     const int hh = kvh * a.G + grow % a.G;
     const int64_t obase = ((int64_t)(o + ti) * a.hq + hh) * D + c4 * 4;
+    const float4 v = accv[rp];
     if (a.out_f32) {
       *reinterpret_cast<float4*>((float*)a.out + obase) =
-          make_float4(accv.x * inv, accv.y * inv, accv.z * inv, accv.w * inv);
+          make_float4(v.x * inv, v.y * inv, v.z * inv, v.w * inv);
     } else {
       uint2 pk;
-      pk.x = f32_to_bf16_bits(accv.x * inv) | ((uint32_t)f32_to_bf16_bits(accv.y * inv) << 16);
-      pk.y = f32_to_bf16_bits(accv.z * inv) | ((uint32_t)f32_to_bf16_bits(accv.w * inv) << 16);
+      pk.x = f32_to_bf16_bits(v.x * inv) | ((uint32_t)f32_to_bf16_bits(v.y * inv) << 16);
+      pk.y = f32_to_bf16_bits(v.z * inv) | ((uint32_t)f32_to_bf16_bits(v.w * inv) << 16);
       *reinterpret_cast<uint2*>((uint16_t*)a.out + obase) = pk;
     }
   }
@@ -852,9 +882,11 @@ AttnPlan plan_attention(int B, const int32_t* row_offsets_h, const int32_t* pref
   }
   p.split_keys = (int)split;
   p.lpt = (B <= kLptMax) ? 1 : 0;
+  p.max_ns = 1;
   for (int b = 0; b < B; ++b) {
     const int n = row_offsets_h[b + 1] - row_offsets_h[b];
     const int ns = attn_splits(prefix_len_h[b] + n, p.split_keys);
+    p.max_ns = std::max(p.max_ns, ns);
     const int64_t per = (int64_t)hkv * attn_row_blocks(n, G, p.rows_per_block);
     p.items += per * ns;
     p.items_a += per * (ns - p.lpt);
@@ -878,7 +910,8 @@ AttnPlan plan_attention(int B, const int32_t* row_offsets_h, const int32_t* pref
 
 size_t attention_workspace_bytes(const AttnPlan& plan, int d) {
   if (plan.partial_items == 0) return 256;
-  return (size_t)plan.items * plan.rows_per_block * (d + 2) * sizeof(float) + 256;
+  return (size_t)plan.items * plan.rows_per_block * (d + 2) * sizeof(float) +
+         (size_t)plan.units * (8 + plan.max_ns) * sizeof(int) + 256;
 }
 
 hipError_t launch_attention_bf16(const LaunchCtx& cx, const AttnPlan& plan, const KvAddr& addr,
@@ -904,6 +937,9 @@ hipError_t launch_attention_bf16(const LaunchCtx& cx, const AttnPlan& plan, cons
   a.rows_per_block = plan.rows_per_block;
   a.part = (float*)workspace;
   a.part_ml = a.part + (size_t)plan.items * plan.rows_per_block * addr.d;
+  a.unit_desc = (int*)(a.part_ml + (size_t)plan.items * plan.rows_per_block * 2);
+  a.unit_items = a.unit_desc + (size_t)plan.units * 8;
+  a.max_ns = plan.max_ns;
   a.lpt = plan.lpt;
   a.items_a = plan.items_a;
   if (plan.lpt) std::copy(plan.order, plan.order + cx.B, a.order);

@@ -34,6 +34,7 @@ struct AttnPlan {
   int64_t items;        // total workgroups
   int64_t partial_items;// workgroups whose request needs more than one split
   int64_t units;        // (request, KV head, row block) triples
+  int max_ns;           // most splits of any request
   int lpt;              // two-phase order in use
   int64_t items_a;      // workgroups of the first phase
   uint16_t order[kLptMax];  // second phase: requests, longest last split first
