@@ -517,24 +517,6 @@ __global__ void __launch_bounds__(kWaves * 64, 1) attn_bf16_kernel(AttnArgs a) {
   const bool row_ok = wave_active && row < M;
   const int ti = row_ok ? row / a.G : 0;
   const int hh = kvh * a.G + (row_ok ? row % a.G : 0);
-  bf16x8 qf[NKS];
-  uint64_t mw0 = 0, mw1 = 0, mw2 = 0, mw3 = 0;
-  if (row_ok) {
-    const uint16_t* qp = a.q + ((int64_t)(o + ti) * a.hq + hh) * D + half * 8;
-#pragma unroll
-    for (int kk = 0; kk < NKS; ++kk)
-      qf[kk] = __builtin_bit_cast(bf16x8, gload16((gptr_u16)(qp + kk * 16)));
-    const uint64_t* mrow = a.mask + (int64_t)(o + ti) * a.words;
-    mw0 = mrow[0];
-    if (a.words > 1) mw1 = mrow[1];
-    if (a.words > 2) mw2 = mrow[2];
-    if (a.words > 3) mw3 = mrow[3];
-  } else {
-#pragma unroll
-    for (int kk = 0; kk < NKS; ++kk)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) qf[kk][e] = (__bf16)0.0f;
-  }
   f32x16 acc[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
@@ -565,23 +547,52 @@ __global__ void __launch_bounds__(kWaves * 64, 1) attn_bf16_kernel(AttnArgs a) {
   __syncthreads();
 
   // Ring of 4 stages: tile t lives in stage t % 4.  Step t waits for this
-  // wave's loads of tile t (tiles t+1 and t+2 stay in flight), meets the other
-  // waves -- after which all of them are done with tile t-1 -- refills that
-  // tile's stage with tile t+3, and computes tile t.
+  // wave's loads of tile t (tiles t+1 and t+2 stay in flight; loads complete
+  // in issue order), meets the other waves -- after which all of them are
+  // done with tile t-1 -- refills that tile's stage with tile t+3, and
+  // computes tile t.  No tile past the split is issued, and the last steps
+  // wait for correspondingly fewer loads in flight.
   const int ntiles = (key_end - key_begin + kTileKeys - 1) / kTileKeys;
   issue_tile<D>(k0, v0, gk, gv, key_begin, key_end, paged, s_blk, blk0, blk_stride, wave, lane);
-  issue_tile<D>(k1, v1, gk, gv, key_begin + kTileKeys, key_end, paged, s_blk, blk0, blk_stride,
-                wave, lane);
-  issue_tile<D>(k2, v2, gk, gv, key_begin + 2 * kTileKeys, key_end, paged, s_blk, blk0,
-                blk_stride, wave, lane);
+  if (ntiles > 1)
+    issue_tile<D>(k1, v1, gk, gv, key_begin + kTileKeys, key_end, paged, s_blk, blk0, blk_stride,
+                  wave, lane);
+  if (ntiles > 2)
+    issue_tile<D>(k2, v2, gk, gv, key_begin + 2 * kTileKeys, key_end, paged, s_blk, blk0,
+                  blk_stride, wave, lane);
+  // The query rows and mask words load while the first tiles stream in.
+  bf16x8 qf[NKS];
+  uint64_t mw0 = 0, mw1 = 0, mw2 = 0, mw3 = 0;
+  if (row_ok) {
+    const uint16_t* qp = a.q + ((int64_t)(o + ti) * a.hq + hh) * D + half * 8;
+#pragma unroll
+    for (int kk = 0; kk < NKS; ++kk)
+      qf[kk] = __builtin_bit_cast(bf16x8, gload16((gptr_u16)(qp + kk * 16)));
+    const uint64_t* mrow = a.mask + (int64_t)(o + ti) * a.words;
+    mw0 = mrow[0];
+    if (a.words > 1) mw1 = mrow[1];
+    if (a.words > 2) mw2 = mrow[2];
+    if (a.words > 3) mw3 = mrow[3];
+  } else {
+#pragma unroll
+    for (int kk = 0; kk < NKS; ++kk)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qf[kk][e] = (__bf16)0.0f;
+  }
 
 #define SPEC_ATTN_STEP(KC, VC, KN, VN, T)                                                       \
   {                                                                                              \
     const int t0_ = key_begin + (T) * kTileKeys;                                                 \
-    __builtin_amdgcn_s_waitcnt(SPEC_VMCNT(2 * PER_WAVE));                                        \
+    if ((T) + 2 < ntiles)                                                                        \
+      __builtin_amdgcn_s_waitcnt(SPEC_VMCNT(2 * PER_WAVE));                                      \
+    else if ((T) + 1 < ntiles)                                                                   \
+      __builtin_amdgcn_s_waitcnt(SPEC_VMCNT(PER_WAVE));                                          \
+    else                                                                                         \
+      __builtin_amdgcn_s_waitcnt(SPEC_VMCNT(0));                                                 \
     __builtin_amdgcn_s_barrier();                                                                \
-    issue_tile<D>(KN, VN, gk, gv, t0_ + 3 * kTileKeys, key_end, paged, s_blk, blk0, blk_stride,  \
-                  wave, lane);                                                                   \
+    if ((T) + 3 < ntiles)                                                                        \
+      issue_tile<D>(KN, VN, gk, gv, t0_ + 3 * kTileKeys, key_end, paged, s_blk, blk0,            \
+                    blk_stride, wave, lane);                                                     \
     if (wave_active) {                                                                           \
       for (int hk = h_lo; hk < h_hi; ++hk)                                                       \
         compute_half<D>(KC, VC, hk, t0_ + 32 * hk, lane, L, key_end, a.scale_log2, mw0, mw1,     \
