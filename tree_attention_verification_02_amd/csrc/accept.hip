@@ -42,11 +42,13 @@ namespace spec {
 constexpr int kStatThreads = 256;
 constexpr int kStatF4 = 16;                   // float4 per thread per statistics chunk
 constexpr int kStatChunkLen = kStatThreads * kStatF4 * 4;   // logits per chunk
-constexpr int kWalkThreads = 1024;
+constexpr int kWalkThreads = 256;
 constexpr int kWalkWaves = kWalkThreads / 64;
-constexpr int kSeg = kWalkThreads * 4;        // elements per segment
-constexpr int kMaxSegs = (1 << 20) / kSeg;    // vocab <= 2^20
-constexpr int kMaxSlices = 64;
+constexpr int kSeg = kWalkThreads * 4;        // elements per segment (one float4 per thread)
+constexpr int kPassF = 8;                     // segments per pass round (float4 in flight per row)
+constexpr int kPassChunk = 64;                // segments per partial-sum flush
+constexpr int kMaxSlices = 32;                // more pollers per counter cost more than they save
+constexpr int kSyncStride = 64;               // ints between barrier counters (own 256 B each)
 constexpr int kMaxSpins = 1 << 21;
 
 // ---------------------------------------------------------------------------
@@ -190,8 +192,8 @@ struct AcceptWs {
   int32_t* part_am; //                     and its first index
   double* cp;       // [R] P_parent(x_c) of each child row c (fp64, sampling)
   double* cq;       // [R] Q_parent(x_c)
-  int32_t* sync;    // [B]   walk barrier counters (zeroed by accept_stats)
-  double* seg;      // [B][2][kMaxSegs] per-pass segment sums (double-buffered)
+  int32_t* sync;    // [B][kSyncStride] walk barrier counters, [b][0] used (zeroed by accept_stats)
+  double* seg;      // [B][2][nseg] per-pass segment sums (double-buffered)
 };
 
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -222,7 +224,7 @@ __host__ __device__ inline AcceptWs accept_ws(void* base, int R, int B, int voca
   w.cq = (double*)p;
   p += align256((size_t)R * sizeof(double));
   w.sync = (int32_t*)p;
-  p += align256((size_t)B * sizeof(int32_t));
+  p += align256((size_t)B * kSyncStride * sizeof(int32_t));
   w.seg = (double*)p;
   return w;
 }
@@ -237,7 +239,8 @@ size_t accept_workspace_bytes(int R, int B, int vocab) {
          align256((size_t)R * nch * sizeof(float)) +
          align256((size_t)R * nch * sizeof(int32_t)) +
          2 * align256((size_t)R * sizeof(double)) +
-         align256((size_t)B * sizeof(int32_t)) + align256((size_t)B * 2 * nseg * sizeof(double));
+         align256((size_t)B * kSyncStride * sizeof(int32_t)) +
+         align256((size_t)B * 2 * nseg * sizeof(double));
 }
 
 // ---------------------------------------------------------------------------
@@ -288,7 +291,7 @@ accept_stats_kernel(const int32_t* __restrict__ row_offsets, int B, int R,
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int slot = rr * nch + chunk;
   if (blockIdx.x == 0)
-    for (int i = tid; i < B; i += kStatThreads) ws.sync[i] = 0;
+    for (int i = tid; i < B; i += kStatThreads) ws.sync[(int64_t)i * kSyncStride] = 0;
   if (!kGreedy) load_exp_table(s_tab);
   if (which == 1) {
     const int b = request_of_row(row_offsets, B, r);
@@ -469,8 +472,8 @@ struct WalkShared {
   double cp[kMaxRows];              // P_parent(x_c), Q_parent(x_c) of each child row
   double cq[kMaxRows];
   double tab[256];
-  double wave_tot[4][kWalkWaves];   // per wave (draw rescan)
-  double half_tot[kWalkWaves / 2][2];  // per segment of a pass round, per half
+  double wave_tot[kWalkWaves];      // per wave (draw rescan)
+  double part[kPassChunk][kWalkWaves];  // per segment and wave (pass)
   double lane_excl[64];             // prefix of the segment sums, per lane block
   double total;
   double c0;
@@ -558,45 +561,69 @@ struct WalkCtx {
   double* seg;        // this request's [2][nseg]
 };
 
-// One lane's share of half a segment: kF4 float4 of the target row (and of
-// the draft row when kQ), three float4 ahead in flight.  Indices past the row
-// are clamped (in-bounds loads) and masked to weight 0.
-template <bool kQ, int kF4>
-SPEC_DEVICE void pass_half(const WalkCtx& c, const float4* p4, const float4* q4, int f0, int v4,
-                           double t, const double* tab, double& acc) {
-  constexpr int kAhead = 3;                          // float4 loads in flight per row
-  float4 pb[kF4], qb[kF4];
+// Sum of the weights of 4 consecutive entries starting at y0: max(0, P - tQ)
+// (or P alone), entries past the row masked to weight 0.
+template <bool kQ>
+SPEC_DEVICE double weight4(const WalkCtx& c, float4 pv, float4 qv, int y0, double t,
+                           const double* tab) {
+  const float pa[4] = {pv.x, pv.y, pv.z, pv.w};
+  const float qa[4] = {qv.x, qv.y, qv.z, qv.w};
+  double acc = 0.0;
 #pragma unroll
-  for (int i = 0; i < kAhead && i < kF4; ++i) {
-    const int f = min(f0 + i * 64, v4 - 1);
+  for (int j = 0; j < 4; ++j) {
+    const bool in = y0 + j < c.vocab;                // the row's ragged end
+    const double P = exp_f64_clamped((double)(in ? pa[j] : -INFINITY) * c.invT - c.lse_p, tab);
+    if (kQ) {
+      const double Q = exp_f64_clamped((double)(in ? qa[j] : -INFINITY) * c.invT - c.lse_q, tab);
+      acc += fmax(0.0, fma(-t, Q, P));
+    } else {
+      acc += P;
+    }
+  }
+  return acc;
+}
+
+// NR consecutive segments from s0: thread tid takes float4 tid of each (all
+// loads in flight at once); each wave's sums go to sh.part[s0 - base + i].
+// Indices past the row are clamped (in-bounds loads) and masked.
+template <bool kQ, int NR>
+SPEC_DEVICE void pass_round(WalkShared& sh, const WalkCtx& c, int s0, int base, double t) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const float4* p4 = reinterpret_cast<const float4*>(c.p);
+  const float4* q4 = reinterpret_cast<const float4*>(c.q);
+  const int v4 = (c.vocab + 3) >> 2;
+  float4 pb[NR], qb[NR];
+#pragma unroll
+  for (int i = 0; i < NR; ++i) {
+    const int f = min((s0 + i) * (kSeg / 4) + tid, v4 - 1);
     pb[i] = p4[f];
-    if (kQ) qb[i] = q4[f];
+    qb[i] = kQ ? q4[f] : make_float4(0.f, 0.f, 0.f, 0.f);
   }
 #pragma unroll
-  for (int i = 0; i < kF4; ++i) {
-    if (i + kAhead < kF4) {
-      const int f = min(f0 + (i + kAhead) * 64, v4 - 1);
-      pb[i + kAhead] = p4[f];
-      if (kQ) qb[i + kAhead] = q4[f];
-    }
-    const int y0 = (f0 + i * 64) * 4;
-    const float pa[4] = {pb[i].x, pb[i].y, pb[i].z, pb[i].w};
-    float qa[4] = {0.f, 0.f, 0.f, 0.f};
-    if (kQ) {
-      qa[0] = qb[i].x; qa[1] = qb[i].y; qa[2] = qb[i].z; qa[3] = qb[i].w;
-    }
+  for (int i = 0; i < NR; ++i) {
+    const double w = wave_sum(weight4<kQ>(c, pb[i], qb[i], (s0 + i) * kSeg + 4 * tid, t, sh.tab));
+    if (lane == 0) sh.part[s0 - base + i][wave] = w;
+  }
+}
+
+template <bool kQ>
+SPEC_DEVICE void pass_segments(WalkShared& sh, const WalkCtx& c, double* seg, double t) {
+  const int tid = threadIdx.x;
+  for (int base = c.seg_lo; base < c.seg_hi; base += kPassChunk) {
+    const int end = min(c.seg_hi, base + kPassChunk);
+    int s0 = base;
+    for (; s0 + kPassF <= end; s0 += kPassF) pass_round<kQ, kPassF>(sh, c, s0, base, t);
+    if ((end - s0) & 4) { pass_round<kQ, 4>(sh, c, s0, base, t); s0 += 4; }
+    if ((end - s0) & 2) { pass_round<kQ, 2>(sh, c, s0, base, t); s0 += 2; }
+    if ((end - s0) & 1) pass_round<kQ, 1>(sh, c, s0, base, t);
+    __syncthreads();
+    if (tid < end - base) {
+      double tot = 0.0;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const bool in = y0 + j < c.vocab;              // the row's ragged end
-      const double P = exp_f64_clamped((double)(in ? pa[j] : -INFINITY) * c.invT - c.lse_p, tab);
-      if (kQ) {
-        const double Q =
-            exp_f64_clamped((double)(in ? qa[j] : -INFINITY) * c.invT - c.lse_q, tab);
-        acc += fmax(0.0, fma(-t, Q, P));
-      } else {
-        acc += P;
-      }
+      for (int w = 0; w < kWalkWaves; ++w) tot += sh.part[tid][w];
+      store_shared_d(&seg[base + tid], tot);
     }
+    __syncthreads();
   }
 }
 
@@ -605,33 +632,11 @@ SPEC_DEVICE void pass_half(const WalkCtx& c, const float4* p4, const float4* q4,
 SPEC_DEVICE double walk_pass(WalkShared& sh, const WalkCtx& c, int* ctr, int pass, double t,
                              bool need_q) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int buf = pass & 1;
-  double* seg = c.seg + buf * c.nseg;
-  const float4* p4 = reinterpret_cast<const float4*>(c.p);
-  const float4* q4 = reinterpret_cast<const float4*>(c.q);
-  // Two waves per segment, each a contiguous half of it: a lane sums its
-  // kHalf/64 weights in registers and the wave reduces once per half.
-  constexpr int kSegsPerRound = kWalkWaves / 2;
-  constexpr int kHalf = kSeg / 2;
-  constexpr int kF4 = kHalf / 256;                   // float4 per lane per half
-  const int v4 = (c.vocab + 3) >> 2;
-  for (int s0 = c.seg_lo; s0 < c.seg_hi; s0 += kSegsPerRound) {
-    const int sg = s0 + (wave >> 1);
-    double acc = 0.0;
-    if (sg < c.seg_hi) {                             // wave-uniform
-      const int f0 = (sg * kSeg + (wave & 1) * kHalf) / 4 + lane;
-      if (need_q)
-        pass_half<true, kF4>(c, p4, q4, f0, v4, t, sh.tab, acc);
-      else
-        pass_half<false, kF4>(c, p4, q4, f0, v4, t, sh.tab, acc);
-    }
-    const double tot = wave_sum(acc);
-    if (lane == 0) sh.half_tot[wave >> 1][wave & 1] = tot;
-    __syncthreads();
-    if (tid < kSegsPerRound && s0 + tid < c.seg_hi)
-      store_shared_d(&seg[s0 + tid], sh.half_tot[tid][0] + sh.half_tot[tid][1]);
-    __syncthreads();
-  }
+  double* seg = c.seg + (pass & 1) * c.nseg;
+  if (need_q)
+    pass_segments<true>(sh, c, seg, t);
+  else
+    pass_segments<false>(sh, c, seg, t);
   slice_barrier(sh, ctr, pass * c.S, c.S);
   if (wave == 0) {
     const int per = (c.nseg + 63) / 64;
@@ -715,11 +720,11 @@ SPEC_DEVICE int walk_draw(WalkShared& sh, const WalkCtx& c, int pass, double t, 
     }
   }
   const double incl = wave_incl_scan(acc, lane);
-  if (lane == 63) sh.wave_tot[0][wave] = incl;
+  if (lane == 63) sh.wave_tot[wave] = incl;
   if (tid == 0) sh.pick = 0x7fffffff;
   __syncthreads();
   double base = sh.c0;
-  for (int k = 0; k < wave; ++k) base += sh.wave_tot[0][k];
+  for (int k = 0; k < wave; ++k) base += sh.wave_tot[k];
   double cum = base + (incl - acc);
   int pick = -1, lastpos = -1;
   for (int j = 0; j < 4; ++j) {
@@ -887,7 +892,7 @@ SPEC_DEVICE void walk_decide(WalkShared& sh, WalkState& st, const float* p_logit
   }
 }
 
-__global__ void __launch_bounds__(kWalkThreads)
+__global__ void __launch_bounds__(kWalkThreads, 4)
 accept_walk_kernel(const int32_t* __restrict__ row_offsets, int R, int S,
                    const int32_t* __restrict__ parents, const int32_t* __restrict__ tokens,
                    const float* __restrict__ p_logits, const float* __restrict__ q_logits,
@@ -922,7 +927,7 @@ accept_walk_kernel(const int32_t* __restrict__ row_offsets, int R, int S,
   c.slice = slice;
   c.S = S;
   c.seg = ws.seg + (size_t)b * 2 * c.nseg;
-  int* ctr = ws.sync + b;
+  int* ctr = ws.sync + (int64_t)b * kSyncStride;
   if (tid == 0) {
     sh.len = 1;
     sh.ntok = 0;

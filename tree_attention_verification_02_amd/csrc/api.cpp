@@ -121,7 +121,7 @@ spec_status launched(hipError_t e, const char* what) {
 int esize(spec_dtype d) { return d == SPEC_BF16 ? 2 : 4; }
 
 // Test hook: SPEC_WALK_SLICES=<n> caps the workgroups per request of the
-// sampling walk (default: as many as fit, up to 64).
+// sampling walk (default: as many as fit, up to 32).
 int walk_slices_override() {
   const char* v = getenv("SPEC_WALK_SLICES");
   return v ? atoi(v) : 0;
