@@ -26,10 +26,16 @@ SMALL = {
     "dynamic-small": dict(B=6, L=("uniform", 30, 700), V=5000),
     "dynamic-contig": dict(B=5, L=("uniform", 0, 300), V=4004, kv_layout="contig"),
     "specinfer-empty-prefix": dict(B=2, L=0, Hq=8, Hkv=2, V=2048),
+    # more than 256 query rows per (request, KV head): the 4-wave wide kernel
+    "specinfer-wide-paged-d64": dict(B=2, L=900, Hq=16, Hkv=2, D=64, V=3000, kv_layout="paged"),
+    "dynamic-wide-mixed": dict(B=7, L=("uniform", 0, 900), Hq=32, Hkv=2, V=3000),
+    "medusa-wide-3blocks": dict(L=260, V=2000, Hq=16, Hkv=1, D=64, tree=("cartesian", (2, 3, 4))),
 }
 BASE = {"toy": "toy", "chain8-small": "chain8", "chain8-d64": "chain8", "medusa-small": "medusa",
         "medusa-256rows": "medusa", "specinfer-small": "specinfer", "dynamic-small": "dynamic",
-        "dynamic-contig": "dynamic", "specinfer-empty-prefix": "specinfer"}
+        "dynamic-contig": "dynamic", "specinfer-empty-prefix": "specinfer",
+        "specinfer-wide-paged-d64": "specinfer", "dynamic-wide-mixed": "dynamic",
+        "medusa-wide-3blocks": "medusa"}
 
 
 @pytest.fixture(scope="module")

@@ -345,16 +345,14 @@ SPEC_DEVICE uint32_t visible_bits(int kb0, int L, int key_end, uint64_t mw0, uin
   return ((uint32_t)tree | pre) & lim;
 }
 
-// One 32-key half (hk) of a staged tile for one wave's 32 query rows:
-// S^T = K Q^T (a 32x32 block), mask, online softmax in the exp2 domain,
-// O^T += V^T P^T.  kb0 is the absolute index of the half's first key.
+// Pieces of the per-wave tile computation, for one 32-key half (hk) of a
+// staged tile and one wave's 32 query rows.
+// S^T = K Q^T (a 32x32 block); sc[e] is the score of key
+// kb0 + half*4 + 8*(e/4) + e%4 (C layout of S^T).
 template <int D>
-SPEC_DEVICE void compute_half(const uint16_t* ks, const uint16_t* vs, int hk, int kb0, int lane,
-                              int L, int key_end, float scale_log2, uint64_t mw0, uint64_t mw1,
-                              uint64_t mw2, uint64_t mw3, const bf16x8 (&qf)[D / 16],
-                              f32x16 (&acc)[D / 32], float& m_run, float& l_run) {
+SPEC_DEVICE f32x16 half_scores(const uint16_t* ks, int hk, int lane,
+                               const bf16x8 (&qf)[D / 16]) {
   constexpr int NKS = D / 16;
-  constexpr int NDB = D / 32;
   const int col = lane & 31, half = lane >> 5;
   f32x16 sc;
 #pragma unroll
@@ -366,33 +364,30 @@ SPEC_DEVICE void compute_half(const uint16_t* ks, const uint16_t* vs, int hk, in
                                                        tile_slot_bytes(krow, kk * 2 + half));
     sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], sc, 0, 0, 0);
   }
-  // sc[e] is the score of key kb0 + half*4 + 8*(e/4) + e%4 (C layout of S^T).
-  if (kb0 + 32 > min(L, key_end)) {          // uniform: only tiles at the tree or split end
-    const uint32_t vis = visible_bits(kb0, L, key_end, mw0, mw1, mw2, mw3);
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int i = half * 4 + 8 * (e >> 2) + (e & 3);
-      sc[e] = ((vis >> i) & 1u) ? sc[e] : -INFINITY;
-    }
-  }
+  return sc;
+}
+
+// Online softmax in the exp2 domain with a lazily moved reference
+// (scale_log2 > 0, so the row maximum commutes with the scaling): a row's
+// reference m only moves when a score exceeds it by more than kLazyMax (log2
+// units), so p = 2^(s - m) stays <= 2^kLazyMax and the O/l rescale is rare.
+// O/l is unchanged by the choice of reference.  Returns whether this lane's
+// row moved with O != 0 (then O must be scaled by alpha before the next
+// P V^T).
+SPEC_DEVICE bool half_softmax(const f32x16& sc, float scale_log2, float& m_run, float& l_run,
+                              bf16x8 (&pb)[2], float& alpha) {
   float mx = sc[0];
 #pragma unroll
   for (int e = 1; e < 16; ++e) mx = fmaxf(mx, sc[e]);
   mx = row_pair_max(mx);
-  // Online softmax with a lazily moved reference (scale_log2 > 0, so the row
-  // maximum commutes with the scaling): a row's reference m only moves when
-  // a score exceeds it by more than kLazyMax (log2 units), so p = 2^(s - m)
-  // stays <= 2^kLazyMax and the O/l rescale is rare.  O/l is unchanged by
-  // the choice of reference.
   const float cand = mx * scale_log2;
   const bool move = cand > m_run + kLazyMax;          // false for a fully masked row
   const float m_new = move ? cand : m_run;
   // A row with no visible key yet keeps m = -inf; 0 as the reference then
   // gives alpha = 0 and p = 0 without a divergent branch.
   const float m_ref = (m_new == -INFINITY) ? 0.0f : m_new;
-  const float alpha = __builtin_amdgcn_exp2f(m_run - m_ref);
+  alpha = __builtin_amdgcn_exp2f(m_run - m_ref);
   float rs = 0.0f;
-  bf16x8 pb[2];
 #pragma unroll
   for (int e = 0; e < 16; ++e) {
     const float p = __builtin_amdgcn_exp2f(fmaf(sc[e], scale_log2, -m_ref));
@@ -402,17 +397,28 @@ SPEC_DEVICE void compute_half(const uint16_t* ks, const uint16_t* vs, int hk, in
   rs = row_pair_sum(rs);
   l_run = l_run * alpha + rs;
   // Rows seen for the first time have O = 0 and need no rescale.
-  if (__any(move && m_run != -INFINITY)) {
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[db][e] *= alpha;
-  }
+  const bool rescale = move && m_run != -INFINITY;
   m_run = m_new;
-  // V^T operand by transposed LDS reads: this lane supplies the address of 4
-  // dims of one key; lane 4q+c of each 16-lane group receives dim dbase+4q+c
-  // of 4 consecutive keys.  The k-slots of P^T (key half*4 + 8*(e/4) + e%4 of
-  // each 16-key step) and of V^T follow the same order.
+  return rescale;
+}
+
+template <int D>
+SPEC_DEVICE void scale_acc(f32x16 (&acc)[D / 32], float alpha) {
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[db][e] *= alpha;
+}
+
+// O^T += V^T P^T.  V^T operand by transposed LDS reads: this lane supplies
+// the address of 4 dims of one key; lane 4q+c of each 16-lane group receives
+// dim dbase+4q+c of 4 consecutive keys.  The k-slots of P^T (key
+// half*4 + 8*(e/4) + e%4 of each 16-key step) and of V^T follow the same
+// order.
+template <int D>
+SPEC_DEVICE void half_pv(const uint16_t* vs, int hk, int lane, const bf16x8 (&pb)[2],
+                         f32x16 (&acc)[D / 32]) {
+  constexpr int NDB = D / 32;
   const int grp = lane >> 4, j = lane & 15;
   const int h = grp >> 1;
   const int dsub = (grp & 1) * 16 + 4 * (j & 3);
@@ -437,6 +443,48 @@ SPEC_DEVICE void compute_half(const uint16_t* ks, const uint16_t* vs, int hk, in
       acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[mm], acc[db], 0, 0, 0);
     }
   }
+}
+
+// One 32-key half (hk) of a staged tile for one wave's 32 query rows:
+// scores, mask (tiles at the tree or split end), online softmax, P V^T.
+// kb0 is the absolute index of the half's first key.
+template <int D>
+SPEC_DEVICE void compute_half(const uint16_t* ks, const uint16_t* vs, int hk, int kb0, int lane,
+                              int L, int key_end, float scale_log2, uint64_t mw0, uint64_t mw1,
+                              uint64_t mw2, uint64_t mw3, const bf16x8 (&qf)[D / 16],
+                              f32x16 (&acc)[D / 32], float& m_run, float& l_run) {
+  const int half = lane >> 5;
+  f32x16 sc = half_scores<D>(ks, hk, lane, qf);
+  if (kb0 + 32 > min(L, key_end)) {          // uniform: only tiles at the tree or split end
+    const uint32_t vis = visible_bits(kb0, L, key_end, mw0, mw1, mw2, mw3);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int i = half * 4 + 8 * (e >> 2) + (e & 3);
+      sc[e] = ((vis >> i) & 1u) ? sc[e] : -INFINITY;
+    }
+  }
+  bf16x8 pb[2];
+  float alpha;
+  if (__any(half_softmax(sc, scale_log2, m_run, l_run, pb, alpha))) scale_acc<D>(acc, alpha);
+  half_pv<D>(vs, hk, lane, pb, acc);
+}
+
+// A whole tile of prefix keys (no mask) for one wave's 32 rows, pipelined
+// inside the wave: both halves' scores are issued first, so the second
+// half's MFMAs run while the first half's softmax occupies the vector ALUs,
+// and the first half's P V^T runs during the second half's softmax.
+template <int D>
+SPEC_DEVICE void compute_tile_full(const uint16_t* ks, const uint16_t* vs, int lane,
+                                   float scale_log2, const bf16x8 (&qf)[D / 16],
+                                   f32x16 (&acc)[D / 32], float& m_run, float& l_run) {
+  const f32x16 s0 = half_scores<D>(ks, 0, lane, qf);
+  const f32x16 s1 = half_scores<D>(ks, 1, lane, qf);
+  bf16x8 p0[2], p1[2];
+  float a0, a1;
+  if (__any(half_softmax(s0, scale_log2, m_run, l_run, p0, a0))) scale_acc<D>(acc, a0);
+  half_pv<D>(vs, 0, lane, p0, acc);
+  if (__any(half_softmax(s1, scale_log2, m_run, l_run, p1, a1))) scale_acc<D>(acc, a1);
+  half_pv<D>(vs, 1, lane, p1, acc);
 }
 
 // First (request, KV head, row block) unit of request b: units of all
@@ -594,9 +642,13 @@ __global__ void __launch_bounds__(kWaves * 64, 1) attn_bf16_kernel(AttnArgs a) {
       issue_tile<D>(KN, VN, gk, gv, t0_ + 3 * kTileKeys, key_end, paged, s_blk, blk0,            \
                     blk_stride, wave, lane);                                                     \
     if (wave_active) {                                                                           \
-      for (int hk = h_lo; hk < h_hi; ++hk)                                                       \
-        compute_half<D>(KC, VC, hk, t0_ + 32 * hk, lane, L, key_end, a.scale_log2, mw0, mw1,     \
-                        mw2, mw3, qf, acc, m_run, l_run);                                        \
+      if (!pair && t0_ + kTileKeys <= min(L, key_end)) {                                         \
+        compute_tile_full<D>(KC, VC, lane, a.scale_log2, qf, acc, m_run, l_run);                 \
+      } else {                                                                                   \
+        for (int hk = h_lo; hk < h_hi; ++hk)                                                     \
+          compute_half<D>(KC, VC, hk, t0_ + 32 * hk, lane, L, key_end, a.scale_log2, mw0, mw1,   \
+                          mw2, mw3, qf, acc, m_run, l_run);                                      \
+      }                                                                                          \
     }                                                                                            \
     __builtin_amdgcn_s_waitcnt(SPEC_LGKMCNT0);                                                   \
   }
