@@ -450,13 +450,13 @@ SPEC_DEVICE void half_pv(const uint16_t* vs, int hk, int lane, const bf16x8 (&pb
 // kb0 is the absolute index of the half's first key.
 template <int D>
 SPEC_DEVICE void compute_half(const uint16_t* ks, const uint16_t* vs, int hk, int kb0, int lane,
-                              int L, int key_end, float scale_log2, uint64_t mw0, uint64_t mw1,
-                              uint64_t mw2, uint64_t mw3, const bf16x8 (&qf)[D / 16],
+                              int L, int key_end, float scale_log2, const uint64_t* mw,
+                              const bf16x8 (&qf)[D / 16],
                               f32x16 (&acc)[D / 32], float& m_run, float& l_run) {
   const int half = lane >> 5;
   f32x16 sc = half_scores<D>(ks, hk, lane, qf);
   if (kb0 + 32 > min(L, key_end)) {          // uniform: only tiles at the tree or split end
-    const uint32_t vis = visible_bits(kb0, L, key_end, mw0, mw1, mw2, mw3);
+    const uint32_t vis = visible_bits(kb0, L, key_end, mw[0], mw[1], mw[2], mw[3]);
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const int i = half * 4 + 8 * (e >> 2) + (e & 3);
@@ -519,6 +519,7 @@ __global__ void __launch_bounds__(kWaves * 64, 1) attn_bf16_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t k0[TILE], k1[TILE], k2[TILE], k3[TILE];
   __shared__ __attribute__((aligned(16))) uint16_t v0[TILE], v1[TILE], v2[TILE], v3[TILE];
   __shared__ __attribute__((aligned(16))) int s_blk[kMaxSplit / kBlock + 4];
+  __shared__ uint64_t s_mask[ROWS * 4];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -610,6 +611,9 @@ __global__ void __launch_bounds__(kWaves * 64, 1) attn_bf16_kernel(AttnArgs a) {
                   blk_stride, wave, lane);
   // The query rows and mask words load while the first tiles stream in.
   bf16x8 qf[NKS];
+  // This lane's row's mask words go to LDS (read only at tiles that need
+  // them, by this wave alone; both waves of a pair write the same values).
+  uint64_t* mw = s_mask + 4 * (g * kRowsPerWave + col);
   uint64_t mw0 = 0, mw1 = 0, mw2 = 0, mw3 = 0;
   if (row_ok) {
     const uint16_t* qp = a.q + ((int64_t)(o + ti) * a.hq + hh) * D + half * 8;
@@ -626,6 +630,12 @@ __global__ void __launch_bounds__(kWaves * 64, 1) attn_bf16_kernel(AttnArgs a) {
     for (int kk = 0; kk < NKS; ++kk)
 #pragma unroll
       for (int e = 0; e < 8; ++e) qf[kk][e] = (__bf16)0.0f;
+  }
+  if (wave_active && half == 0) {
+    mw[0] = mw0;
+    mw[1] = mw1;
+    mw[2] = mw2;
+    mw[3] = mw3;
   }
 
 #define SPEC_ATTN_STEP(KC, VC, KN, VN, T)                                                       \
@@ -646,8 +656,8 @@ __global__ void __launch_bounds__(kWaves * 64, 1) attn_bf16_kernel(AttnArgs a) {
         compute_tile_full<D>(KC, VC, lane, a.scale_log2, qf, acc, m_run, l_run);                 \
       } else {                                                                                   \
         for (int hk = h_lo; hk < h_hi; ++hk)                                                     \
-          compute_half<D>(KC, VC, hk, t0_ + 32 * hk, lane, L, key_end, a.scale_log2, mw0, mw1,   \
-                          mw2, mw3, qf, acc, m_run, l_run);                                      \
+          compute_half<D>(KC, VC, hk, t0_ + 32 * hk, lane, L, key_end, a.scale_log2, mw, qf,     \
+                          acc, m_run, l_run);                                                    \
       }                                                                                          \
     }                                                                                            \
     __builtin_amdgcn_s_waitcnt(SPEC_LGKMCNT0);                                                   \
