@@ -928,19 +928,30 @@ AttnPlan plan_attention(int B, const int32_t* row_offsets_h, const int32_t* pref
   // 8 waves of 32 query rows: most (request, KV head) pairs fit in one
   // workgroup, so every KV tile is read once.
   p.rows_per_block = kWaves * kRowsPerWave;
-  int64_t work = 0, units = 0, max_keys = 0;
+  int64_t work = 0, units = 0, max_keys = 0, min_keys = INT64_MAX;
   for (int b = 0; b < B; ++b) {
     const int n = row_offsets_h[b + 1] - row_offsets_h[b];
     const int nrb = attn_row_blocks(n, G, p.rows_per_block);
     units += (int64_t)hkv * nrb;
     work += (int64_t)hkv * nrb * (prefix_len_h[b] + n);
     max_keys = std::max<int64_t>(max_keys, prefix_len_h[b] + n);
+    min_keys = std::min<int64_t>(min_keys, prefix_len_h[b] + n);
   }
-  // One workgroup per CU at a time: aim at ~4 workgroups per CU (256 CUs),
-  // splits of at least 256 keys and at most kMaxSplitsCombine per request.
-  const int64_t target = 1024;
+  // One workgroup per CU at a time (256 CUs).  Requests of (nearly) equal
+  // length: the fewest splits that give every CU one workgroup (each split
+  // costs a partial-result round trip).  Otherwise ~4 workgroups per CU, so
+  // that longest-first dispatch evens out the mixed lengths.  Splits are at
+  // least 256 keys and at most kMaxSplitsCombine per request.
+  constexpr int64_t kCUs = 256;
   auto round_up = [](int64_t x) { return ((x + kTileKeys - 1) / kTileKeys) * kTileKeys; };
-  int64_t split = std::min<int64_t>(round_up((work + target - 1) / target), kMaxSplit);
+  int64_t split;
+  if (B > 0 && max_keys <= min_keys + min_keys / 8) {
+    const int64_t ns = std::max<int64_t>(1, (kCUs + units - 1) / std::max<int64_t>(units, 1));
+    split = std::min<int64_t>(round_up((max_keys + ns - 1) / ns), kMaxSplit);
+  } else {
+    const int64_t target = 4 * kCUs;
+    split = std::min<int64_t>(round_up((work + target - 1) / target), kMaxSplit);
+  }
   split = std::max<int64_t>(split, round_up((max_keys + kMaxSplitsCombine - 1) / kMaxSplitsCombine));
   if (split < 256) split = 256;
   p.units = units;
