@@ -477,8 +477,13 @@ template <int D>
 SPEC_DEVICE void compute_tile_full(const uint16_t* ks, const uint16_t* vs, int lane,
                                    float scale_log2, const bf16x8 (&qf)[D / 16],
                                    f32x16 (&acc)[D / 32], float& m_run, float& l_run) {
+  // Raised priority while the scores are issued: of the two waves sharing a
+  // SIMD, the first to get here finishes its MFMAs first and moves on to
+  // its softmax while the other one's MFMAs run.
+  __builtin_amdgcn_s_setprio(1);
   const f32x16 s0 = half_scores<D>(ks, 0, lane, qf);
   const f32x16 s1 = half_scores<D>(ks, 1, lane, qf);
+  __builtin_amdgcn_s_setprio(0);
   bf16x8 p0[2], p1[2];
   float a0, a1;
   if (__any(half_softmax(s0, scale_log2, m_run, l_run, p0, a0))) scale_acc<D>(acc, a0);
