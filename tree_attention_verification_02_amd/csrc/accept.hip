@@ -15,16 +15,17 @@
 // and the final draw after the last rejection reuses that pass's sums.
 //
 // Kernels:
-//  * accept_stats: one workgroup per (row, {target, draft}) streams the row
-//    once (16-byte loads) and produces the fp64 log-sum-exp of logits/T, the
-//    first argmax, and the child probabilities P_u(x_c), Q_u(x_c).  Draft rows
+//  * accept_stats: one workgroup per (row, {target, draft}, 16K-logit chunk)
+//    streams its chunk once (16-byte loads) into fp64 partial sums (or the
+//    first argmax); accept_finalize merges them into each row's log-sum-exp
+//    of logits/T and the child probabilities P_u(x_c), Q_u(x_c).  Draft rows
 //    of leaves are never read.
-//  * accept_walk (cooperative launch): S workgroups per request.  Each pass
-//    is split over the S workgroups by 4096-element segments; segment sums go
-//    to global memory and the S workgroups meet at a per-request counter
-//    barrier (bounded spin).  Every workgroup then sums the segments in the
-//    same order and replays the same scalar decisions, so no further
-//    broadcast is needed; the owner of the drawn segment rescans it.
+//  * accept_walk: S workgroups ("slices", taken by ticket in start order) per
+//    request.  Each pass is split over the S slices by 1024-element
+//    segments; segment sums go to global memory and the S slices meet at a
+//    per-request counter barrier (bounded spin).  Every slice then sums the
+//    segments in the same order and replays the same scalar decisions, so no
+//    further broadcast is needed; the owner of the drawn segment rescans it.
 //  * accept_greedy: temperature 0, one workgroup per request.
 //
 // Every quantity that decides an integer (accept tests, residual masses,
@@ -32,6 +33,8 @@
 // exponential, so decisions agree with a float64 reference except within
 // ~1e-11 of a threshold.
 #include <math.h>
+
+#include <atomic>
 
 #include "common.hpp"
 #include "launch.hpp"
@@ -48,6 +51,7 @@ constexpr int kSeg = kWalkThreads * 4;        // elements per segment (one float
 constexpr int kPassF = 8;                     // segments per pass round (float4 in flight per row)
 constexpr int kPassChunk = 64;                // segments per partial-sum flush
 constexpr int kMaxSlices = 32;                // more pollers per counter cost more than they save
+constexpr int kMaxDevices = 64;
 constexpr int kSyncStride = 64;               // ints between barrier counters (own 256 B each)
 constexpr int kMaxSpins = 1 << 21;
 
@@ -192,7 +196,8 @@ struct AcceptWs {
   int32_t* part_am; //                     and its first index
   double* cp;       // [R] P_parent(x_c) of each child row c (fp64, sampling)
   double* cq;       // [R] Q_parent(x_c)
-  int32_t* sync;    // [B][kSyncStride] walk barrier counters, [b][0] used (zeroed by accept_stats)
+  int32_t* sync;    // [B+1][kSyncStride]: [0][0] walk ticket counter, [b+1][0] barrier counter
+                    // of request b (zeroed by accept_stats)
   double* seg;      // [B][2][nseg] per-pass segment sums (double-buffered)
 };
 
@@ -224,7 +229,7 @@ __host__ __device__ inline AcceptWs accept_ws(void* base, int R, int B, int voca
   w.cq = (double*)p;
   p += align256((size_t)R * sizeof(double));
   w.sync = (int32_t*)p;
-  p += align256((size_t)B * kSyncStride * sizeof(int32_t));
+  p += align256((size_t)(B + 1) * kSyncStride * sizeof(int32_t));
   w.seg = (double*)p;
   return w;
 }
@@ -239,7 +244,7 @@ size_t accept_workspace_bytes(int R, int B, int vocab) {
          align256((size_t)R * nch * sizeof(float)) +
          align256((size_t)R * nch * sizeof(int32_t)) +
          2 * align256((size_t)R * sizeof(double)) +
-         align256((size_t)B * kSyncStride * sizeof(int32_t)) +
+         align256((size_t)(B + 1) * kSyncStride * sizeof(int32_t)) +
          align256((size_t)B * 2 * nseg * sizeof(double));
 }
 
@@ -291,7 +296,7 @@ accept_stats_kernel(const int32_t* __restrict__ row_offsets, int B, int R,
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int slot = rr * nch + chunk;
   if (blockIdx.x == 0)
-    for (int i = tid; i < B; i += kStatThreads) ws.sync[(int64_t)i * kSyncStride] = 0;
+    for (int i = tid; i <= B; i += kStatThreads) ws.sync[(int64_t)i * kSyncStride] = 0;
   if (!kGreedy) load_exp_table(s_tab);
   if (which == 1) {
     const int b = request_of_row(row_offsets, B, r);
@@ -900,8 +905,18 @@ accept_walk_kernel(const int32_t* __restrict__ row_offsets, int R, int S,
                    AcceptWs ws, WalkOut out) {
   __shared__ WalkShared sh;
   __shared__ WalkState st;
-  const int b = blockIdx.x / S;
-  const int slice = blockIdx.x % S;
+  // (request, slice) by ticket, in the order the workgroups start running:
+  // the lowest unfinished request then always has all its slices running
+  // or next in line, so the per-request barriers make progress whenever S
+  // workgroups fit on the device at once (no cooperative launch needed).
+  __shared__ int s_ticket;
+  if (threadIdx.x == 0)
+    s_ticket = (S == 1) ? (int)blockIdx.x
+                        : __hip_atomic_fetch_add(ws.sync, 1, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  const int b = s_ticket / S;
+  const int slice = s_ticket % S;
   const int o = row_offsets[b];
   const int n = row_offsets[b + 1] - o;
   const int tid = threadIdx.x;
@@ -927,7 +942,7 @@ accept_walk_kernel(const int32_t* __restrict__ row_offsets, int R, int S,
   c.slice = slice;
   c.S = S;
   c.seg = ws.seg + (size_t)b * 2 * c.nseg;
-  int* ctr = ws.sync + (int64_t)b * kSyncStride;
+  int* ctr = ws.sync + (int64_t)(b + 1) * kSyncStride;
   if (tid == 0) {
     sh.len = 1;
     sh.ntok = 0;
@@ -1040,6 +1055,29 @@ accept_greedy_kernel(const int32_t* __restrict__ row_offsets, const int32_t* __r
   write_outputs(sh, out, b, o, n, -1);
 }
 
+// Walk workgroups that fit on device `dev` at once (CUs x occupancy),
+// queried once per device.
+static hipError_t walk_capacity(int dev, int* capacity) {
+  static std::atomic<int> cached[kMaxDevices];
+  if (dev >= 0 && dev < kMaxDevices) {
+    const int c = cached[dev].load(std::memory_order_relaxed);
+    if (c > 0) {
+      *capacity = c;
+      return hipSuccess;
+    }
+  }
+  int cus = 0, per_cu = 0;
+  hipError_t e;
+  if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess)
+    return e;
+  if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, accept_walk_kernel, kWalkThreads,
+                                                        0)) != hipSuccess)
+    return e;
+  *capacity = cus * per_cu;
+  if (dev >= 0 && dev < kMaxDevices) cached[dev].store(*capacity, std::memory_order_relaxed);
+  return hipSuccess;
+}
+
 int walk_slices(int B, int vocab, int capacity_blocks) {
   const int nseg = segs_for(vocab);
   int S = capacity_blocks / (B > 0 ? B : 1);
@@ -1081,32 +1119,17 @@ hipError_t launch_accept(const LaunchCtx& cx, int R, const int32_t* parents, con
                        cx.row_offsets_d, parents, tokens, ws, out);
     return hipGetLastError();
   }
-  int dev = 0, cus = 0, per_cu = 0;
+  int dev = 0;
   if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
-  if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess)
-    return e;
-  if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, accept_walk_kernel, kWalkThreads,
-                                                        0)) != hipSuccess)
-    return e;
-  const int capacity = cus * per_cu;
+  int capacity = 0;
+  if ((e = walk_capacity(dev, &capacity)) != hipSuccess) return e;
   int S = walk_slices(cx.B, vocab, capacity);
   if (slices_override > 0) S = slices_override < S ? slices_override : S;
-  if (S == 1) {
-    // one workgroup per request: no cross-workgroup waiting, any grid size
-    WalkOut o1 = out;
-    hipLaunchKernelGGL(accept_walk_kernel, dim3(cx.B), dim3(kWalkThreads), 0, cx.stream,
-                       cx.row_offsets_d, R, 1, parents, tokens, p_logits, q_logits, ld, vocab,
-                       temperature, seed, step, ws, o1);
-    return hipGetLastError();
-  }
-  const int32_t* ro = cx.row_offsets_d;
-  int S_arg = S;
-  void* args[] = {(void*)&ro,         (void*)&R,     (void*)&S_arg,    (void*)&parents,
-                  (void*)&tokens,     (void*)&p_logits, (void*)&q_logits, (void*)&ld,
-                  (void*)&vocab,      (void*)&temperature, (void*)&seed, (void*)&step,
-                  (void*)&ws,         (void*)&out};
-  return hipLaunchCooperativeKernel((const void*)accept_walk_kernel, dim3(cx.B * S),
-                                    dim3(kWalkThreads), args, 0, cx.stream);
+  // S > 1: B * S <= capacity workgroups, which take tickets (see the kernel).
+  hipLaunchKernelGGL(accept_walk_kernel, dim3(cx.B * S), dim3(kWalkThreads), 0, cx.stream,
+                     cx.row_offsets_d, R, S, parents, tokens, p_logits, q_logits, ld, vocab,
+                     temperature, seed, step, ws, out);
+  return hipGetLastError();
 }
 
 }  // namespace spec
