@@ -187,15 +187,12 @@ SPEC_DEVICE void load_exp_table(double* s_tab) {
 // ---------------------------------------------------------------------------
 // Workspace.
 struct AcceptWs {
-  double* lse;      // [2][R] log-sum-exp of logits / T (target rows, draft rows)
   int32_t* am;      // [R]   first argmax of the target row (greedy)
   int nch;          // statistics chunks per row
   double* part_ref; // [2][R][nch] chunk partials: reference
   double* part_s;   //                     and sum of exp(z - reference)
   float* part_m;    // [R][nch]    chunk max (greedy)
   int32_t* part_am; //                     and its first index
-  double* cp;       // [R] P_parent(x_c) of each child row c (fp64, sampling)
-  double* cq;       // [R] Q_parent(x_c)
   int32_t* sync;    // [B+1][kSyncStride]: [0][0] walk ticket counter, [b+1][0] barrier counter
                     // of request b (zeroed by accept_stats)
   double* seg;      // [B][2][nseg] per-pass segment sums (double-buffered)
@@ -212,8 +209,6 @@ __host__ __device__ inline AcceptWs accept_ws(void* base, int R, int B, int voca
   char* p = (char*)base;
   AcceptWs w;
   w.nch = nch;
-  w.lse = (double*)p;
-  p += align256(2 * (size_t)R * sizeof(double));
   w.am = (int32_t*)p;
   p += align256((size_t)R * sizeof(int32_t));
   w.part_ref = (double*)p;
@@ -224,10 +219,6 @@ __host__ __device__ inline AcceptWs accept_ws(void* base, int R, int B, int voca
   p += align256((size_t)R * nch * sizeof(float));
   w.part_am = (int32_t*)p;
   p += align256((size_t)R * nch * sizeof(int32_t));
-  w.cp = (double*)p;
-  p += align256((size_t)R * sizeof(double));
-  w.cq = (double*)p;
-  p += align256((size_t)R * sizeof(double));
   w.sync = (int32_t*)p;
   p += align256((size_t)(B + 1) * kSyncStride * sizeof(int32_t));
   w.seg = (double*)p;
@@ -239,11 +230,11 @@ static int segs_for(int vocab) { return (vocab + kSeg - 1) / kSeg; }
 size_t accept_workspace_bytes(int R, int B, int vocab) {
   const int nseg = segs_for(vocab);
   const int nch = stat_chunks(vocab);
-  return align256(2 * (size_t)R * sizeof(double)) + align256((size_t)R * sizeof(int32_t)) +
+  // the layout of accept_ws, field by field
+  return align256((size_t)R * sizeof(int32_t)) +
          2 * align256(2 * (size_t)R * nch * sizeof(double)) +
          align256((size_t)R * nch * sizeof(float)) +
          align256((size_t)R * nch * sizeof(int32_t)) +
-         2 * align256((size_t)R * sizeof(double)) +
          align256((size_t)(B + 1) * kSyncStride * sizeof(int32_t)) +
          align256((size_t)B * 2 * nseg * sizeof(double));
 }
@@ -391,10 +382,10 @@ accept_stats_kernel(const int32_t* __restrict__ row_offsets, int B, int R,
 }
 
 // Per-row results from the chunk partials, merged in chunk order (so every
-// run gives the same bits): the log-sum-exp of each row (or the target
-// argmax when greedy), and each child's probability under its parent's
-// distributions, P_u(x_c) and Q_u(x_c) (greedy: 1 if x_c is the argmax).
-// One thread per (row, target|draft).
+// run gives the same bits): (reference, sum) of a row (its log-sum-exp is
+// ref + log(sum); the sampling walk merges its own rows), or the target
+// argmax.  accept_finalize (greedy): one thread per row writes the argmax
+// and, per child, 1 if its token is the parent's argmax.
 SPEC_DEVICE void merged_ref_sum(const AcceptWs& ws, int rr, const double* tab, double& ref,
                                 double& s) {
   const int nch = ws.nch;
@@ -415,53 +406,20 @@ SPEC_DEVICE int merged_argmax(const AcceptWs& ws, int r) {
 __global__ void __launch_bounds__(256)
 accept_finalize_kernel(const int32_t* __restrict__ row_offsets, int B, int R,
                        const int32_t* __restrict__ parents, const int32_t* __restrict__ tokens,
-                       const float* __restrict__ p_logits, const float* __restrict__ q_logits,
-                       int64_t ld, int vocab, float temperature, AcceptWs ws,
-                       float* __restrict__ child_p, float* __restrict__ child_q) {
-  __shared__ double s_tab[256];
-  const bool greedy = temperature == 0.0f;
-  if (!greedy) load_exp_table(s_tab);
-  __syncthreads();
-  const int t = blockIdx.x * 256 + threadIdx.x;
-  if (t >= (greedy ? R : 2 * R)) return;
-  const int which = t >= R ? 1 : 0;
-  const int r = t - which * R;
+                       AcceptWs ws, float* __restrict__ child_p) {
+  const int r = blockIdx.x * 256 + threadIdx.x;
+  if (r >= R) return;
   const int b = request_of_row(row_offsets, B, r);
   const int o = row_offsets[b];
   const int u = r - o;
-  const double invT = greedy ? 1.0 : 1.0 / (double)temperature;
-  if (greedy) {
-    ws.am[r] = merged_argmax(ws, r);
-  } else {
-    double ref, s;
-    merged_ref_sum(ws, which * R + r, s_tab, ref, s);
-    ws.lse[which * R + r] = ref + log(s);
-  }
-  float* dst = which ? child_q : child_p;
-  if (u == 0) {                                    // the root has no draft
-    if (dst) dst[r] = __int_as_float(0x7fc00000);
-    return;
-  }
+  ws.am[r] = merged_argmax(ws, r);
+  if (!child_p) return;
   const int pu = parents[r];
-  const int x = tokens[r];
-  if (pu < 0 || pu >= u) {                         // invalid tree (reported by the walk)
-    if (dst) dst[r] = __int_as_float(0x7fc00000);
+  if (u == 0 || pu < 0 || pu >= u) {              // root, or invalid tree (reported by the walk)
+    child_p[r] = __int_as_float(0x7fc00000);
     return;
   }
-  if (greedy) {
-    if (dst) dst[r] = (x == merged_argmax(ws, o + pu)) ? 1.0f : 0.0f;
-    return;
-  }
-  double val = 0.0;
-  if (x >= 0 && x < vocab) {
-    double ref, s;
-    merged_ref_sum(ws, which * R + o + pu, s_tab, ref, s);
-    const double lse = ref + log(s);
-    const float* prow = (which ? q_logits : p_logits) + (int64_t)(o + pu) * ld;
-    val = exp_f64((double)prow[x] * invT - lse, s_tab);
-  }
-  (which ? ws.cq : ws.cp)[r] = val;
-  if (dst) dst[r] = (float)val;
+  child_p[r] = (tokens[r] == merged_argmax(ws, o + pu)) ? 1.0f : 0.0f;
 }
 
 // ---------------------------------------------------------------------------
@@ -476,6 +434,7 @@ struct WalkShared {
   int toks[kMaxRows + 1];
   double cp[kMaxRows];              // P_parent(x_c), Q_parent(x_c) of each child row
   double cq[kMaxRows];
+  double lse[2][kMaxRows];          // log-sum-exp of logits / T: target, draft rows
   double tab[256];
   double wave_tot[kWalkWaves];      // per wave (draw rescan)
   double part[kPassChunk][kWalkWaves];  // per segment and wave (pass)
@@ -795,6 +754,8 @@ struct WalkOut {
   uint8_t* accept_mask;
   int32_t* flags;
   int path_stride;
+  float* child_p;     // optional fp32 copies of P_u(x_c), Q_u(x_c) (sampling walk)
+  float* child_q;
 };
 
 // Writes path, tokens (except index `skip`, written by the slice that drew
@@ -846,9 +807,7 @@ struct WalkState {
 // Thread 0: run sibling tests and moves until a vocabulary pass (or a draw)
 // is needed.  Coins: purpose 0 for the accept test of child c, purpose 1 for
 // the draw at the node where the walk stops.
-SPEC_DEVICE void walk_decide(WalkShared& sh, WalkState& st, const float* p_logits,
-                             const float* q_logits, int64_t ld, int o, int vocab, double invT,
-                             const double* lse, int R, uint64_t seed, uint64_t step, int b,
+SPEC_DEVICE void walk_decide(WalkShared& sh, WalkState& st, uint64_t seed, uint64_t step, int b,
                              int path_stride) {
   while (true) {
     const int u = st.u;
@@ -923,17 +882,43 @@ accept_walk_kernel(const int32_t* __restrict__ row_offsets, int R, int S,
   load_exp_table(sh.tab);
   if (tid == 0) sh.timeout = 0;
   load_tree(sh, parents, tokens, o, n);
+  // This request's row statistics: each row's log-sum-exp from its chunk
+  // partials (in chunk order), then each child's P_u(x_c), Q_u(x_c) in fp64.
+  // Every slice computes them; slice 0 writes the fp32 outputs (NaN at roots
+  // and at rows whose parent is invalid).
+  const double invT = 1.0 / (double)temperature;
+  for (int k = tid; k < 2 * n; k += blockDim.x) {
+    const int which = k >= n ? 1 : 0;
+    const int i = k - which * n;
+    double ref, s;
+    merged_ref_sum(ws, which * R + o + i, sh.tab, ref, s);
+    sh.lse[which][i] = ref + log(s);
+  }
+  __syncthreads();
+  for (int k = tid; k < 2 * n; k += blockDim.x) {
+    const int which = k >= n ? 1 : 0;
+    const int i = k - which * n;
+    float* dst = which ? out.child_q : out.child_p;
+    const int pu = sh.par[i];
+    double val = __longlong_as_double(0x7ff8000000000000LL);
+    if (i > 0 && pu >= 0 && pu < i) {
+      const int x = sh.tok[i];
+      val = 0.0;
+      if (x >= 0 && x < vocab) {
+        const float* prow = (which ? q_logits : p_logits) + (int64_t)(o + pu) * ld;
+        val = exp_f64((double)prow[x] * invT - sh.lse[which][pu], sh.tab);
+      }
+      (which ? sh.cq : sh.cp)[i] = val;
+    }
+    if (dst && slice == 0) dst[o + i] = (float)val;
+  }
+  __syncthreads();
   if (sh.bad) {
     if (slice == 0) write_bad_tree(out, b, o, n);
     return;
   }
-  for (int i = tid; i < n; i += blockDim.x) {
-    sh.cp[i] = ws.cp[o + i];
-    sh.cq[i] = ws.cq[o + i];
-  }
-  __syncthreads();
   WalkCtx c;
-  c.invT = 1.0 / (double)temperature;
+  c.invT = invT;
   c.vocab = vocab;
   c.nseg = (vocab + kSeg - 1) / kSeg;
   const int per = (c.nseg + S - 1) / S;
@@ -959,16 +944,15 @@ accept_walk_kernel(const int32_t* __restrict__ row_offsets, int R, int S,
   bool final_here = false;
   while (true) {
     if (tid == 0)
-      walk_decide(sh, st, p_logits, q_logits, ld, o, vocab, c.invT, ws.lse, R, seed, step, b,
-                  out.path_stride);
+      walk_decide(sh, st, seed, step, b, out.path_stride);
     __syncthreads();
     const int action = st.action;
     if (action == 3) break;
     const int u = st.u;
     c.p = p_logits + (int64_t)(o + u) * ld;
     c.q = q_logits + (int64_t)(o + u) * ld;
-    c.lse_p = ws.lse[o + u];
-    c.lse_q = st.act_q ? ws.lse[R + o + u] : 0.0;
+    c.lse_p = sh.lse[0][u];
+    c.lse_q = st.act_q ? sh.lse[1][u] : 0.0;
     const double act_t = st.act_t;
     const bool act_q = st.act_q != 0;
     if (action != 2) {
@@ -1108,13 +1092,12 @@ hipError_t launch_accept(const LaunchCtx& cx, int R, const int32_t* parents, con
     hipLaunchKernelGGL(accept_stats_kernel<false>, dim3(rows * nch), dim3(kStatThreads), 0,
                        cx.stream, cx.row_offsets_d, cx.B, R, parents, p_logits, q_logits, ld, vocab,
                        temperature, ws);
-  hipLaunchKernelGGL(accept_finalize_kernel, dim3((rows + 255) / 256), dim3(256), 0, cx.stream,
-                     cx.row_offsets_d, cx.B, R, parents, tokens, p_logits, q_logits, ld, vocab,
-                     temperature, ws, child_p, child_q);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  WalkOut out{accept_len, path, tokens_out, accept_mask, flags, path_stride};
+  WalkOut out{accept_len, path, tokens_out, accept_mask, flags, path_stride, child_p, child_q};
   if (temperature == 0.0f) {
+    hipLaunchKernelGGL(accept_finalize_kernel, dim3((R + 255) / 256), dim3(256), 0, cx.stream,
+                       cx.row_offsets_d, cx.B, R, parents, tokens, ws, child_p);
     hipLaunchKernelGGL(accept_greedy_kernel, dim3(cx.B), dim3(kWalkThreads), 0, cx.stream,
                        cx.row_offsets_d, parents, tokens, ws, out);
     return hipGetLastError();
