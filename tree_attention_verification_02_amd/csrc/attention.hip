@@ -78,133 +78,76 @@ __host__ __device__ inline int attn_splits(int keys, int split) {
   return (keys + split - 1) / split;
 }
 
-// Wave-parallel search: which request holds item `x`, given per-request
-// counts.  Returns b and the first item of b.  Uniform across the wave.
-template <bool kUnits>
-SPEC_DEVICE void locate(int64_t x, const AttnArgs& a, int& b_out, int64_t& base_out) {
-  const int lane = threadIdx.x & 63;
-  int64_t running = 0;
-  for (int base = 0; base < a.B; base += 64) {
-    const int b = base + lane;
-    int64_t cnt = 0;
-    if (b < a.B) {
-      const int n = a.row_offsets[b + 1] - a.row_offsets[b];
-      const int nrb = attn_row_blocks(n, a.G, a.rows_per_block);
-      cnt = (int64_t)a.addr.hkv * nrb;
-      if (!kUnits) cnt *= attn_splits(a.prefix_len[b] + n, a.split);
-    }
-    int64_t incl = cnt;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      int64_t t = __shfl_up(incl, o, 64);
-      if (lane >= o) incl += t;
-    }
-    const int64_t total = __shfl(incl, 63, 64);
-    if (x < running + total) {
-      const uint64_t hit = __ballot(running + incl > x);
-      const int first = __ffsll((long long)hit) - 1;
-      const int64_t excl = __shfl(incl - cnt, first, 64);
-      b_out = base + first;
-      base_out = running + excl;
-      return;
-    }
-    running += total;
-  }
-  b_out = -1;
-  base_out = 0;
-}
-
-
 // Workgroup index -> (request, KV head, row block, split).  Phase A: every
 // split but the last of each request when `lpt` is set (every split
 // otherwise), request by request, then (KV head, row block, split).  Phase B
 // (`lpt` only): the last split of each request, requests in `order`, then
 // (KV head, row block).  Wave-parallel over requests; uniform results;
-// b = -1 past the end.
-SPEC_DEVICE void locate_item(int64_t x, const AttnArgs& a, int& b, int& kvh, int& rb, int& s) {
+// b = -1 past the end.  Also returns the request's first row o, rows n and
+// prefix length L from the same loads, and (batches of at most 64 requests)
+// its first (KV head, row block) unit `ubase` among all requests in request
+// order; ubase = -1 otherwise.
+struct ItemLoc {
+  int b, kvh, rb, s, o, n, L;
+  int64_t ubase;
+};
+SPEC_DEVICE ItemLoc locate_item(int64_t x, const AttnArgs& a) {
   const int lane = threadIdx.x & 63;
   const int tail = a.lpt;
   const int rpb = a.rows_per_block;
-  b = -1;
-  kvh = rb = s = 0;
+  ItemLoc r;
+  r.b = -1;
+  r.kvh = r.rb = r.s = r.o = r.n = r.L = 0;
+  r.ubase = -1;
   const bool phase_a = x < a.items_a;
   if (!phase_a) x -= a.items_a;
   int64_t running = 0;
   for (int base = 0; base < a.B; base += 64) {
-    int bq = -1, nrb = 0, ns = 0;
+    int bq = -1, nrb = 0, ns = 0, o = 0, n = 0, L = 0;
     int64_t cnt = 0;
     if (base + lane < a.B) {
       bq = phase_a ? base + lane : (int)a.order[base + lane];
-      const int n = a.row_offsets[bq + 1] - a.row_offsets[bq];
+      o = a.row_offsets[bq];
+      n = a.row_offsets[bq + 1] - o;
+      L = a.prefix_len[bq];
       nrb = attn_row_blocks(n, a.G, rpb);
-      ns = attn_splits(a.prefix_len[bq] + n, a.split);
+      ns = attn_splits(L + n, a.split);
       cnt = (int64_t)a.addr.hkv * nrb * (phase_a ? ns - tail : 1);
     }
     int64_t incl = cnt;
 #pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int64_t t = __shfl_up(incl, o, 64);
-      if (lane >= o) incl += t;
+    for (int off = 1; off < 64; off <<= 1) {
+      const int64_t t = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += t;
     }
     const int64_t total = __shfl(incl, 63, 64);
     if (x < running + total) {
       const uint64_t hit = __ballot(running + incl > x);
       const int f = __ffsll((long long)hit) - 1;
       const int64_t local = x - running - __shfl(incl - cnt, f, 64);
-      b = __shfl(bq, f, 64);
+      r.b = __shfl(bq, f, 64);
+      r.o = __shfl(o, f, 64);
+      r.n = __shfl(n, f, 64);
+      r.L = __shfl(L, f, 64);
       const int nrb_b = __shfl(nrb, f, 64);
       const int ns_b = __shfl(ns, f, 64);
       if (phase_a) {
         const int nsa = ns_b - tail;
-        s = (int)(local % nsa);
-        rb = (int)((local / nsa) % nrb_b);
-        kvh = (int)(local / ((int64_t)nsa * nrb_b));
+        r.s = (int)(local % nsa);
+        r.rb = (int)((local / nsa) % nrb_b);
+        r.kvh = (int)(local / ((int64_t)nsa * nrb_b));
       } else {
-        s = ns_b - 1;
-        rb = (int)(local % nrb_b);
-        kvh = (int)(local / nrb_b);
+        r.s = ns_b - 1;
+        r.rb = (int)(local % nrb_b);
+        r.kvh = (int)(local / nrb_b);
       }
-      return;
+      if (a.B <= 64)      // every request is in this chunk (any order)
+        r.ubase = wave_sum(bq >= 0 && bq < r.b ? (int64_t)a.addr.hkv * nrb : (int64_t)0);
+      return r;
     }
     running += total;
   }
-}
-
-// Item index of split s of unit u = kvh * nrb + rb of request b (inverse of
-// locate_item).  Wave-parallel; uniform.
-SPEC_DEVICE int64_t item_of(const AttnArgs& a, int b, int64_t u, int ns, int s) {
-  const int lane = threadIdx.x & 63;
-  const int tail = a.lpt;
-  const int rpb = a.rows_per_block;
-  if (s < ns - tail) {
-    int64_t cnt = 0;
-    for (int base = 0; base < b; base += 64) {
-      const int bq = base + lane;
-      if (bq < b) {
-        const int n = a.row_offsets[bq + 1] - a.row_offsets[bq];
-        cnt += (int64_t)a.addr.hkv * attn_row_blocks(n, a.G, rpb) *
-               (attn_splits(a.prefix_len[bq] + n, a.split) - tail);
-      }
-    }
-    return wave_sum(cnt) + u * (ns - tail) + s;
-  }
-  int64_t running = 0;
-  for (int base = 0; base < a.B; base += 64) {
-    int bq = -1;
-    int64_t cnt = 0;
-    if (base + lane < a.B) {
-      bq = a.order[base + lane];
-      const int n = a.row_offsets[bq + 1] - a.row_offsets[bq];
-      cnt = (int64_t)a.addr.hkv * attn_row_blocks(n, a.G, rpb);
-    }
-    const uint64_t hit = __ballot(bq == b);
-    if (hit) {
-      const int f = __ffsll((long long)hit) - 1;
-      return a.items_a + running + wave_sum(lane < f ? cnt : (int64_t)0) + u;
-    }
-    running += wave_sum(cnt);
-  }
-  return -1;
+  return r;
 }
 
 typedef const __attribute__((address_space(1))) uint16_t* gptr_u16;
@@ -531,12 +474,13 @@ __global__ void __launch_bounds__(kWaves * 64, 1) attn_bf16_kernel(AttnArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
   const int64_t item = blockIdx.x;
-  int b, kvh, rb, s;
-  locate_item(item, a, b, kvh, rb, s);
+  const ItemLoc loc = locate_item(item, a);
+  const int b = loc.b;
   if (b < 0) return;
-  const int o = a.row_offsets[b];
-  const int n = a.row_offsets[b + 1] - o;
-  const int L = __builtin_amdgcn_readfirstlane(a.prefix_len[b]);
+  const int kvh = loc.kvh, rb = loc.rb, s = loc.s;
+  const int o = __builtin_amdgcn_readfirstlane(loc.o);
+  const int n = __builtin_amdgcn_readfirstlane(loc.n);
+  const int L = __builtin_amdgcn_readfirstlane(loc.L);
   const int total_keys = L + n;
   const int ns = attn_splits(total_keys, a.split);
   const int key_begin = __builtin_amdgcn_readfirstlane(s * a.split);
@@ -545,7 +489,8 @@ __global__ void __launch_bounds__(kWaves * 64, 1) attn_bf16_kernel(AttnArgs a) {
 
   if (a.max_ns > 1) {
     // the combine finds each unit's splits here (no search over requests)
-    const int64_t unit = unit_base(a, b) + (int64_t)kvh * attn_row_blocks(n, a.G, ROWS) + rb;
+    const int64_t ub = loc.ubase >= 0 ? loc.ubase : unit_base(a, b);
+    const int64_t unit = ub + (int64_t)kvh * attn_row_blocks(n, a.G, ROWS) + rb;
     if (tid == 0) {
       a.unit_items[unit * a.max_ns + s] = (int)item;
       if (s == 0) {
