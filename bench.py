@@ -31,6 +31,8 @@ WORKLOAD_TEXT = {
                  "contiguous KV 8192, bf16, vocab 128256",
     "dynamic": "dynamic: EAGLE-2 top-5 trees under ECHO budget Kmax=1024 rows, B=64, "
                "paged KV (block 16) prefixes U[512,16384], GQA 32/8, D=128, bf16, vocab 128256",
+    "lookahead": "lookahead: W=5 N=4 G=5 pass (30 rows, two causal branches, caller mask), B=1, "
+                 "MHA 32x128, contiguous KV 2048, bf16, vocab 32000",
 }
 
 
@@ -46,11 +48,15 @@ def algorithmic(w):
         o, n = int(w.row_offsets[b]), w.rows(b)
         L = int(w.prefix_len[b])
         a_attn += w.Hkv * (L + n) * w.D * 2 * e + 2 * n * w.Hq * w.D * e + n * words * 8
-        par = w.parents[o:o + n]
-        depth = np.zeros(n, dtype=np.int64)
-        for i in range(1, n):
-            depth[i] = depth[par[i]] + 1
-        f_attn += w.Hq * w.D * 4 * int(np.sum(L + depth + 1))
+        if getattr(w, "visibility", None) is not None:
+            seen = np.asarray(w.visibility[b], dtype=bool).sum(axis=1)   # new rows each row sees
+        else:
+            par = w.parents[o:o + n]
+            depth = np.zeros(n, dtype=np.int64)
+            for i in range(1, n):
+                depth[i] = depth[par[i]] + 1
+            seen = depth + 1
+        f_attn += w.Hq * w.D * 4 * int(np.sum(L + seen))
         a_acc += n * w.V * 4 + int(w.nonleaf[o:o + n].sum()) * w.V * 4
     return a_attn, f_attn, a_acc
 

@@ -149,7 +149,13 @@ spec_status spec_kv_append(const spec_batch *batch, const spec_kv *kv,
  * Query head h reads KV head h / (Hq / Hkv) (grouped-query attention).
  *
  *   q_d        [R][Hq][D], same dtype as the cache
- *   mask_d     uint64 [R][W] from spec_tree_build_mask
+ *   mask_d     uint64 [R][W]: bit j of row i's words = row i sees new row j of
+ *              its request.  Usually from spec_tree_build_mask (the ancestor
+ *              mask); any other visibility of the new rows may be passed,
+ *              such as the survey page's lookahead decoding mask (section
+ *              8.2.3: causal branches that do not see each other) or rows
+ *              seeing later rows.  Bits at or past N_b are ignored; a row
+ *              must see at least one key (a prefix token or one bit).
  *   out_d      [R][Hq][D] of out_dtype (bf16 or f32)
  *   workspace  >= spec_tree_attn_workspace_bytes(batch, kv, Hq) bytes
  *              (split-KV partial results; contents need no initialisation)

@@ -36,6 +36,19 @@ def tree_attention(q, k_prefix, v_prefix, k_tree, v_tree, parents, scale=None):
     parents  [N]          local parent array
     Returns float64 [N][Hq][D].
     """
+    return masked_attention(q, k_prefix, v_prefix, k_tree, v_tree, ancestor_mask(parents),
+                            scale)
+
+
+def masked_attention(q, k_prefix, v_prefix, k_tree, v_tree, visible, scale=None):
+    """The same attention under any visibility of the new rows.
+
+    visible [N][N] bool: row i sees new row j.  Every row sees the whole
+    prefix.  The pages' lookahead decoding (section 8.2.3 of the survey page)
+    combines two branches in one pass with such a mask: causal inside each
+    branch, no branch seeing the other; tree_attention is the case
+    visible = the ancestor mask.
+    """
     q = np.asarray(q, dtype=np.float64)
     k_prefix = np.asarray(k_prefix, dtype=np.float64)
     v_prefix = np.asarray(v_prefix, dtype=np.float64)
@@ -46,7 +59,8 @@ def tree_attention(q, k_prefix, v_prefix, k_tree, v_tree, parents, scale=None):
     G = Hq // Hkv
     if scale is None:
         scale = 1.0 / np.sqrt(D)
-    M = ancestor_mask(parents)
+    M = np.asarray(visible, dtype=bool)
+    assert M.shape == (N, N)
     visible = np.concatenate([np.ones((N, L), dtype=bool), M], axis=1)
     out = np.empty((N, Hq, D), dtype=np.float64)
     for h in range(Hq):

@@ -66,7 +66,8 @@ def check_mask(w, vs):
     for b in range(w.B):
         o, e = request_slice(w, b)
         par = w.parents[o:e]
-        M = OT.ancestor_mask(par)
+        # a caller-supplied visibility replaces the ancestor mask
+        M = w.visibility[b] if w.visibility is not None else OT.ancestor_mask(par)
         exp = OT.pack_words(M, words)
         assert np.array_equal(got[o:e], exp), f"mask mismatch in request {b}"
         d = OT.depth(par)
@@ -81,6 +82,8 @@ def oracle_attention(w, b):
     q = w.q[o:e].detach().to("cpu", torch.float64).numpy()
     kt = w.k_new[o:e].detach().to("cpu", torch.float64).numpy()
     vt = w.v_new[o:e].detach().to("cpu", torch.float64).numpy()
+    if w.visibility is not None:
+        return OAt.masked_attention(q, kp, vp, kt, vt, w.visibility[b], scale=1.0 / np.sqrt(w.D))
     return OAt.tree_attention(q, kp, vp, kt, vt, w.parents[o:e], scale=1.0 / np.sqrt(w.D))
 
 

@@ -204,3 +204,19 @@ def test_attention_workspace_grows_with_splits_only():
     kv2 = _kv(cap=300000)
     many = L.LIB.spec_tree_attn_workspace_bytes(ctypes.byref(longer.c), ctypes.byref(kv2), 4)
     assert 0 < one < many
+
+
+def test_binding_packs_caller_masks_like_the_oracle():
+    """The binding's packing of a caller-supplied visibility (host marshalling)
+    gives the oracle's mask words, for the lookahead mask and random bits."""
+    from oracle import tree as OT
+    from tree_attention_verification_02_amd.pipeline import pack_visibility
+    from workloads import masks
+    rng = np.random.default_rng(3)
+    vis = [masks.lookahead_visibility(5, 4, 5), masks.random_visibility(rng, 130, 0.5),
+           masks.random_visibility(rng, 7, 0.3)]
+    ro = np.concatenate([[0], np.cumsum([v.shape[0] for v in vis])])
+    words = (max(v.shape[0] for v in vis) + 63) // 64
+    got = pack_visibility(vis, ro, words).view(np.uint64)
+    for b, v in enumerate(vis):
+        assert np.array_equal(got[ro[b]:ro[b + 1]], OT.pack_words(v, words))

@@ -13,8 +13,9 @@ import torch
 
 pytestmark = pytest.mark.gpu
 
-from parity import (bits_equal, check_accept, check_attention, check_commit, check_mask,  # noqa: E402
-                    log, make, run_step)
+from oracle import attention as OAt  # noqa: E402
+from parity import (ATTN_TOL, bits_equal, check_accept, check_attention, check_commit,  # noqa: E402
+                    check_mask, log, make, request_slice, run_step)
 
 SMALL = {
     "toy": dict(),
@@ -189,9 +190,9 @@ def test_commit_adversarial_paths(lib):
     del L
 
 
-FULL = ["toy", "chain8", "medusa", "specinfer", "dynamic"]
+FULL = ["toy", "chain8", "medusa", "specinfer", "dynamic", "lookahead"]
 SAMPLE_REQ = {"toy": None, "chain8": None, "medusa": None, "specinfer": [0, 5],
-              "dynamic": "pick"}
+              "dynamic": "pick", "lookahead": None}
 
 
 @pytest.mark.parametrize("name", FULL)
@@ -219,3 +220,47 @@ def test_full_size_greedy_and_seed1(lib, name):
     check_accept(w, vs, 0.0, 0, 0)
     vs = run_step(w, temperature=1.0, seed=1, step=0, commit=False)
     check_accept(w, vs, 1.0, 1, 0)
+
+
+@pytest.mark.parametrize("kind", ["lookahead", "random"])
+def test_caller_supplied_masks(lib, kind):
+    """Any visibility of the new rows, packed by the caller: the survey page's
+    lookahead decoding mask (two causal branches sharing the current token,
+    W=5, N=4, G=5: 30 rows) and arbitrary bits (rows may see later rows)."""
+    from oracle import tree as OTr
+    from workloads import masks
+    from tree_attention_verification_02_amd.pipeline import VerifyStep
+    if kind == "lookahead":
+        w = make("chain8", B=3, tree=("chain", 29), L=("uniform", 0, 400), V=2000, Hq=16, Hkv=2)
+    else:
+        w = make("dynamic", **SMALL["dynamic-small"])
+    vs = VerifyStep(w)
+    vs.build_mask()
+    rng = np.random.default_rng(7)
+    words = vs.batch.words
+    new = np.zeros((w.R, words), dtype=np.uint64)
+    vis = {}
+    for b in range(w.B):
+        o, e = request_slice(w, b)
+        n = e - o
+        vis[b] = (masks.lookahead_visibility(5, 4, 5) if kind == "lookahead"
+                  else masks.random_visibility(rng, n, 0.3))
+        assert vis[b].shape == (n, n)
+        new[o:e] = OTr.pack_words(vis[b], words)
+    vs.mask.copy_(torch.from_numpy(new.view(np.int64)).to(vs.mask.device))
+    vs.append()
+    vs.attention()
+    torch.cuda.synchronize()
+    out = vs.attn_out.detach().to("cpu", torch.float64).numpy()
+    worst = 0.0
+    for b in range(w.B):
+        o, e = request_slice(w, b)
+        kp, vp = w.prefix_kv(b)
+        q = w.q[o:e].detach().to("cpu", torch.float64).numpy()
+        kt = w.k_new[o:e].detach().to("cpu", torch.float64).numpy()
+        vt = w.v_new[o:e].detach().to("cpu", torch.float64).numpy()
+        ref = OAt.masked_attention(q, kp, vp, kt, vt, vis[b], scale=1.0 / np.sqrt(w.D))
+        err = float(np.abs(out[o:e] - ref).max())
+        worst = max(worst, err)
+        assert err <= ATTN_TOL, f"{kind} request {b}: max |d| = {err}"
+    log(f"[parity] {kind} masks: attention max|d| = {worst:.3e}")

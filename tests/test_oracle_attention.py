@@ -100,3 +100,61 @@ def test_gqa_head_mapping():
     q2 = q[:, [2, 3, 0, 1]]
     out2 = A.tree_attention(q2, kp[::-1], vp[::-1], kt[:, ::-1], vt[:, ::-1], parents)
     np.testing.assert_allclose(out2[:, [2, 3, 0, 1]], out, atol=1e-13)
+
+
+# -- arbitrary visibility of the new rows (lookahead-style and random masks) --
+from workloads import masks  # noqa: E402
+
+
+def test_lookahead_mask_counts():
+    """Survey page, lookahead decoding 8.2.3 and 8.3.2: with W=5, N=4, G=5 the
+    lookahead branch adds W(N-1)-1 rows to "0" and the verify branch G(N-1),
+    W(N-1) + G(N-1) = 30 rows in one pass."""
+    m = masks.lookahead_visibility(5, 4, 5)
+    assert m.shape == (30, 30)
+    assert m[:, 0].all()                          # everyone sees "0"
+    la = list(range(1, 15))
+    ve = list(range(15, 30))
+    assert not m[np.ix_(la, ve)].any() and not m[np.ix_(ve, la)].any()
+    assert not np.triu(m, 1).any()                # causal
+
+
+def test_lookahead_mask_equals_two_causal_branches():
+    """Each branch, run as its own causal sequence "0", b_1, b_2, ... after the
+    prefix, gives the masked outputs at its rows (torch SDPA, float64)."""
+    vis = masks.lookahead_visibility(3, 3, 2)     # "0" + 5 lookahead + 4 verify rows
+    n = vis.shape[0]
+    rng = np.random.default_rng(11)
+    Hq, Hkv, D, L = 4, 2, 8, 9
+    q, kp, vp = _rand(rng, n, Hq, D), _rand(rng, Hkv, L, D), _rand(rng, Hkv, L, D)
+    kt, vt = _rand(rng, n, Hkv, D), _rand(rng, n, Hkv, D)
+    out = A.masked_attention(q, kp, vp, kt, vt, vis)
+    for rows in ([0, 1, 2, 3, 4, 5], [0, 6, 7, 8, 9]):
+        for h in range(Hq):
+            kvh = h // (Hq // Hkv)
+            keys = np.concatenate([kp[kvh], kt[rows, kvh]], axis=0)
+            vals = np.concatenate([vp[kvh], vt[rows, kvh]], axis=0)
+            np.testing.assert_allclose(out[rows, h], _sdpa_causal(q[rows, h], keys, vals),
+                                       rtol=0, atol=1e-12)
+
+
+def test_random_mask_zero_query_and_single_key():
+    rng = np.random.default_rng(12)
+    n, Hq, Hkv, D = 7, 2, 1, 4
+    vis = masks.random_visibility(rng, n, 0.4)
+    q, kp, vp = np.zeros((n, Hq, D)), _rand(rng, Hkv, 5, D), _rand(rng, Hkv, 5, D)
+    kt, vt = _rand(rng, n, Hkv, D), _rand(rng, n, Hkv, D)
+    out = A.masked_attention(q, kp, vp, kt, vt, vis)
+    for i in range(n):
+        visv = np.concatenate([vp[0], vt[vis[i], 0]], axis=0)
+        for h in range(Hq):
+            np.testing.assert_allclose(out[i, h], visv.mean(axis=0), atol=1e-13)
+    # empty prefix, each row seeing exactly one (possibly later) row
+    pick = rng.integers(0, n, n)
+    one = np.zeros((n, n), dtype=bool)
+    one[np.arange(n), pick] = True
+    q2 = _rand(rng, n, Hq, D)
+    out2 = A.masked_attention(q2, kp[:, :0], vp[:, :0], kt, vt, one)
+    for i in range(n):
+        for h in range(Hq):
+            np.testing.assert_allclose(out2[i, h], vt[pick[i], 0], atol=1e-15)

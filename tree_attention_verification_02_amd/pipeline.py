@@ -15,6 +15,19 @@ import torch
 from . import _lib as L
 
 
+def pack_visibility(visibility, row_offsets, words):
+    """Mask words [R][words] (int64 view of uint64) from per-request bool
+    [n][n] visibility: bit j of row i's words set iff row i sees row j."""
+    R = int(row_offsets[-1])
+    out = np.zeros((R, words * 8), dtype=np.uint8)
+    for b, vis in enumerate(visibility):
+        o = int(row_offsets[b])
+        vis = np.asarray(vis, dtype=bool)
+        packed = np.packbits(vis, axis=1, bitorder="little")
+        out[o:o + vis.shape[0], :packed.shape[1]] = packed
+    return out.view(np.int64)
+
+
 class VerifyStep:
     def __init__(self, w, path_stride=None, out_dtype=None, temperature=None, seed=None, step=None):
         """``w`` is any object with the workload fields (see workloads.gen.Workload)."""
@@ -28,6 +41,12 @@ class VerifyStep:
                        layout="paged" if w.kv_layout == "paged" else "contig",
                        capacity=getattr(w, "capacity", 0), block_table=w.block_table)
         self.mask = torch.empty((R, self.batch.words), dtype=torch.int64, device=dev)
+        # A caller-supplied visibility of the new rows (not a tree mask):
+        # packed once here, it replaces the ancestor mask after build_mask.
+        self.caller_mask = None
+        if getattr(w, "visibility", None) is not None:
+            self.caller_mask = torch.from_numpy(
+                pack_visibility(w.visibility, w.row_offsets, self.batch.words)).to(dev)
         self.depth = torch.empty(R, dtype=torch.int32, device=dev)
         self.position = torch.empty(R, dtype=torch.int32, device=dev)
         self.err_row = torch.empty(B, dtype=torch.int32, device=dev)
@@ -58,6 +77,10 @@ class VerifyStep:
     def build_mask(self, stream=None):
         L.spec_tree_build_mask(self.batch, self.parents, self.mask, self.depth, self.position,
                                self.err_row, stream)
+        if self.caller_mask is not None:
+            s = stream if stream is not None else torch.cuda.current_stream(self.mask.device)
+            with torch.cuda.stream(s):
+                self.mask.copy_(self.caller_mask, non_blocking=True)
 
     def append(self, stream=None):
         L.spec_kv_append(self.batch, self.kv, self.w.k_new, self.w.v_new, stream)

@@ -25,7 +25,7 @@ import hashlib
 import numpy as np
 import torch
 
-from . import trees
+from . import masks, trees
 
 # ----------------------------------------------------------------------------
 # The five workloads.  Sizes, dtypes and distributions follow the stated
@@ -44,6 +44,12 @@ CONFIGS = {
     "specinfer": dict(index=3, B=8, tree=("kschedule", (3, 2, 2, 1, 1)),
                       Hq=64, Hkv=8, D=128, L=8192, dtype="bf16", V=128256,
                       p_sigma=3.0, q_sigma=1.0, kv_layout="contig"),
+    # Not one of the five: a lookahead-decoding pass (survey page, 8.2.3) with
+    # W=5, N=4, G=5 -- "0" + 14 lookahead rows + 15 verify rows = 30 rows whose
+    # attention mask is not a tree mask; shaped like chain8's layer.
+    "lookahead": dict(index=5, B=1, tree=("chain", 29), Hq=32, Hkv=32, D=128, L=2048,
+                      dtype="bf16", V=32000, p_sigma=3.0, q_sigma=1.0, kv_layout="contig",
+                      visibility=("lookahead", 5, 4, 5)),
     "dynamic": dict(index=4, B=64, tree=("eagle2", 5, 8), kmax_per_req=16,
                     Hq=32, Hkv=8, D=128, L=("uniform", 512, 16384),
                     dtype="bf16", V=128256, p_sigma=3.0, q_sigma=1.0,
@@ -92,6 +98,9 @@ class Workload:
     seed: int = 0              # Philox key for the acceptance uniforms
     step: int = 0
     temperature: float = 1.0
+    # per request: visibility of the new rows when the attention mask is not
+    # the tree's ancestor mask (bool [n][n]); None for tree masks
+    visibility: list | None = None
     block_size: int = BLOCK
 
     @property
@@ -261,10 +270,16 @@ def make(name: str, device: str = "cpu", **over) -> Workload:
     root_rows = row_offsets[:-1]
     tokens[root_rows] = rng.integers(0, V, size=B)
 
+    visibility = None
+    if cfg.get("visibility") is not None:
+        kind, *args = cfg["visibility"]
+        assert kind == "lookahead"
+        visibility = [masks.lookahead_visibility(*args) for _ in range(B)]
+        assert all(v.shape[0] == sizes[b] for b, v in enumerate(visibility))
     return Workload(name=name, B=B, Hq=Hq, Hkv=Hkv, D=D, V=V, dtype=cfg["dtype"],
                     kv_layout=layout, parents=parents, row_offsets=row_offsets,
                     prefix_len=prefix_len, tokens=tokens, device=device, q=q,
                     k_new=k_new, v_new=v_new, k_cache=k_cache, v_cache=v_cache,
                     capacity=capacity, block_table=block_table, p_logits=p_logits,
                     q_logits=q_logits, nonleaf=nonleaf, seed=seed, step=step,
-                    temperature=temperature)
+                    temperature=temperature, visibility=visibility)
