@@ -46,6 +46,13 @@ Readings taken where the pages are silent or garbled:
    purpose); purpose 0 = accept coin of draft row c, 1 = sampling coin of the
    node where the walk stops.  This layout is a convention (parity unpinned
    beyond GPU = oracle; the statistics it must produce are pinned).
+10. Deterministic children (top-k drafts, as in Medusa or expansion trees;
+   the pages give no rule): child c of u is taken as a draft from the point
+   mass at its token x, so reading 2 with Q = delta_x accepts c iff r < R(x),
+   and a rejection removes x from R (max(0, R - delta_x) / Z).  This is
+   sampling from P_u without replacement, so the emitted token still follows
+   P_u; no draft logits are used.  A sibling repeating a rejected token has
+   R(x) = 0 and is never accepted.
 
 Decisions whose outcome is within rounding of its threshold are reported as
 flagged: |r - R(x)/Q_u(x)| < FLAG_EPS (1e-6) for a child test, and a sampling
@@ -173,6 +180,61 @@ def walk_sampling(parents, tokens, P, Q, coin_accept, coin_sample) -> WalkResult
             res.decisions.append(("sample", u, m))
             res.tokens.append(t)
             return res
+
+
+def walk_topk(parents, tokens, P, coin_accept, coin_sample) -> WalkResult:
+    """Acceptance walk for deterministic children (reading 10)."""
+    validate(parents)
+    kids = tree_children(parents)
+    res = WalkResult()
+    u = 0
+    while True:
+        if not kids[u]:
+            t, m = sample_inverse_cdf(P[u], coin_sample[u])
+            res.decisions.append(("sample", u, m))
+            res.tokens.append(t)
+            return res
+        R = np.array(P[u], dtype=np.float64)
+        moved = False
+        for c in kids[u]:
+            x = int(tokens[c])
+            r = float(coin_accept[c])
+            res.decisions.append(("accept", c, abs(r - R[x])))
+            if r < R[x]:
+                res.path.append(c)
+                res.tokens.append(x)
+                u = c
+                moved = True
+                break
+            w = R.copy()
+            w[x] = max(0.0, R[x] - 1.0)
+            Z = float(np.sum(w))
+            if Z > 0:
+                R = w / Z
+            else:
+                res.zero_residual = True
+                res.decisions.append(("residual", c, 0.0))
+        if not moved:
+            t, m = sample_inverse_cdf(R, coin_sample[u])
+            res.decisions.append(("sample", u, m))
+            res.tokens.append(t)
+            return res
+
+
+def accept_request_topk(parents, tokens, p_logits, temperature, seed, step, request):
+    """Acceptance of one request whose children are deterministic drafts
+    (reading 10); temperature > 0.  Returns the same dict as accept_request
+    (child_q is NaN everywhere)."""
+    parents = np.asarray(parents)
+    n = len(parents)
+    P = distributions(p_logits, temperature)
+    ca, cs = request_coins(seed, step, request, n)
+    res = walk_topk(parents, tokens, P, ca, cs)
+    child_p = np.full(n, np.nan)
+    for c in range(1, n):
+        child_p[c] = P[int(parents[c]), int(tokens[c])]
+    return dict(path=list(res.path), tokens=list(res.tokens), accept_len=res.accept_len,
+                child_p=child_p, child_q=np.full(n, np.nan), result=res)
 
 
 def walk_greedy(parents, tokens, p_logits) -> WalkResult:
