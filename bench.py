@@ -4,8 +4,8 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config dynamic]
 
 One step = the whole verify path over one batch: spec_tree_build_mask ->
-spec_kv_append -> spec_tree_attn_verify -> spec_accept_sample ->
-spec_kv_commit, on synthetic inputs already resident in HBM.  Prints one JSON
+spec_kv_append -> spec_tree_attn_verify -> spec_accept_sample (or
+spec_accept_topk with --acceptance topk) -> spec_kv_commit, on synthetic inputs already resident in HBM.  Prints one JSON
 line: verified tree tokens/s (all verify rows, roots included, per second of
 wall-clock over K steps), the roofline of the dominant kernel (tree
 attention) from live HIP-event timing, and the CPU oracle timed on a bounded
@@ -36,8 +36,10 @@ WORKLOAD_TEXT = {
 }
 
 
-def algorithmic(w):
-    """Algorithmic bytes / flops of one step (what the method must move)."""
+def algorithmic(w, topk=False):
+    """Algorithmic bytes / flops of one step (what the method must move).
+    Acceptance reads every target row once, and the draft rows of nodes with
+    children unless the children are deterministic (topk)."""
     import numpy as np
     e = 2 if w.dtype == "bf16" else 4
     words = (w.max_rows + 63) // 64
@@ -57,7 +59,7 @@ def algorithmic(w):
                 depth[i] = depth[par[i]] + 1
             seen = depth + 1
         f_attn += w.Hq * w.D * 4 * int(np.sum(L + seen))
-        a_acc += n * w.V * 4 + int(w.nonleaf[o:o + n].sum()) * w.V * 4
+        a_acc += n * w.V * 4 + (0 if topk else int(w.nonleaf[o:o + n].sum()) * w.V * 4)
     return a_attn, f_attn, a_acc
 
 
@@ -85,7 +87,7 @@ def measured_traffic(config):
     return rec["traffic_bytes_per_call"]
 
 
-def cpu_baseline(w, budget_s):
+def cpu_baseline(w, budget_s, topk=False):
     """Time the oracle on the requests of the workload, in order (and again
     from the first request when one pass over the batch takes less than the
     budget), until about budget_s seconds of CPU time are spent."""
@@ -118,7 +120,12 @@ def cpu_baseline(w, budget_s):
         t0 = time.perf_counter()
         OT.pack_words(OT.ancestor_mask(par), (w.max_rows + 63) // 64)
         OAt.tree_attention(q, kp, vp, kt, vt, par, scale=1.0 / np.sqrt(w.D))
-        r = OA.accept_request(par, w.tokens[o:o + n], pl, ql, w.temperature, w.seed, w.step, b)
+        if topk:
+            r = OA.accept_request_topk(par, w.tokens[o:o + n], pl, w.temperature, w.seed,
+                                       w.step, b)
+        else:
+            r = OA.accept_request(par, w.tokens[o:o + n], pl, ql, w.temperature, w.seed,
+                                  w.step, b)
         for h in range(w.Hkv):
             OK.commit(np.concatenate([kp[h], kt[:, h]]), L, r["path"])
             OK.commit(np.concatenate([vp[h], vt[:, h]]), L, r["path"])
@@ -140,6 +147,9 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="dynamic", choices=list(WORKLOAD_TEXT))
+    ap.add_argument("--acceptance", default="sample", choices=["sample", "topk"],
+                    help="children drawn from the draft rows (spec_accept_sample) or the "
+                         "drafter's top-k tokens (spec_accept_topk)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--calib-copy-gib", type=float, default=0.0,
@@ -154,9 +164,10 @@ def main():
     import workloads as W
     from tree_attention_verification_02_amd.pipeline import VerifyStep
 
-    w = W.make(args.config, device="cuda")
-    vs = VerifyStep(w)
-    a_attn, f_attn, a_acc = algorithmic(w)
+    topk = args.acceptance == "topk"
+    w = W.make(args.config, device="cuda", **({"draft": "topk"} if topk else {}))
+    vs = VerifyStep(w, acceptance=args.acceptance)
+    a_attn, f_attn, a_acc = algorithmic(w, topk)
     for _ in range(args.warmup):
         vs.run()
     torch.cuda.synchronize()
@@ -210,7 +221,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": WORKLOAD_TEXT[args.config], "name": args.config,
                    "batch": w.B, "verify_rows": R, "draft_tokens": R - w.B,
-                   "kv_tokens": int(w.prefix_len.sum()) + R, "vocab": w.V},
+                   "kv_tokens": int(w.prefix_len.sum()) + R, "vocab": w.V,
+                   "acceptance": args.acceptance},
         "roofline": {"bound": "hbm", "kernel": "spec_tree_attn_verify (split-KV main + combine)",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(args.config),
@@ -227,7 +239,7 @@ def main():
         "mean_accepted_drafts": float(vs.acc.accept_len.float().mean()),
     }
     if not args.no_cpu:
-        out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, topk)
     print(json.dumps(out), flush=True)
 
 

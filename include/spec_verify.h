@@ -9,6 +9,7 @@
  *   spec_kv_append         tree rows' K/V -> cache slots [L_b, L_b + N_b)
  *   spec_tree_attn_verify  tree attention: prefix + ancestors only
  *   spec_accept_sample     lossless acceptance walk + final token
+ *   spec_accept_topk       the same for deterministic (top-k) children
  *   spec_kv_commit         compact the accepted path's K/V, roll back the rest
  *
  * Pages this interface restates (title, section):
@@ -237,6 +238,33 @@ spec_status spec_accept_sample(const spec_batch *batch, const int32_t *parents_d
                                float temperature, uint64_t seed, uint64_t step,
                                int32_t path_stride, const spec_accept_out *out,
                                void *workspace_d, size_t workspace_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * spec_accept_topk -- acceptance when the children are the drafter's top-k
+ * choices (deterministic, as in Medusa heads and expansion or EAGLE trees:
+ * [SURV] 5.2 and 6.2, [TREE] tree generation).  The pages give no rule for
+ * this case; the one taken here treats child c as a draft from the point
+ * mass at its token x, so [MATH] 7.1's test and residual become:
+ * child c is accepted iff r < R(x), and a rejection removes x from R,
+ * where R starts as P_u and is kept normalised (R = P_u on the tokens not
+ * yet rejected at u, divided by N = 1 - their P_u mass).  A sibling that
+ * repeats a rejected token is never accepted.  When every child of u is
+ * rejected, the final token is drawn from R; at a leaf, from P_leaf.  This
+ * is sampling from P_u without replacement, so the emitted tokens follow
+ * the target distribution exactly; no draft logits are needed.
+ *
+ * Arguments, outputs, coins (purpose 0 = accept coin of child c, 1 = draw
+ * at the stopping node), flags and workspace are those of
+ * spec_accept_sample without q_logits_d; child_q_d, when given, is set to
+ * NaN.  temperature == 0 is the greedy walk of spec_accept_sample.  A
+ * rejection that would leave no mass (N <= 0) keeps R and sets
+ * SPEC_FLAG_ZERO_RESIDUAL.
+ */
+spec_status spec_accept_topk(const spec_batch *batch, const int32_t *parents_d,
+                             const int32_t *tokens_d, const float *p_logits_d, int64_t logits_ld,
+                             int32_t vocab, float temperature, uint64_t seed, uint64_t step,
+                             int32_t path_stride, const spec_accept_out *out, void *workspace_d,
+                             size_t workspace_bytes, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
  * spec_kv_commit -- [SD] KV-cache management: keep accepted tokens' K/V,

@@ -42,10 +42,10 @@ def make(name, **kw):
 
 
 def run_step(w, temperature=None, seed=None, step=None, commit=True, out_dtype=None,
-             path_stride=None):
+             path_stride=None, acceptance="sample"):
     from tree_attention_verification_02_amd.pipeline import VerifyStep
     vs = VerifyStep(w, temperature=temperature, seed=seed, step=step, out_dtype=out_dtype,
-                    path_stride=path_stride)
+                    path_stride=path_stride, acceptance=acceptance)
     vs.run(commit=commit)
     torch.cuda.synchronize()
     return vs
@@ -102,11 +102,17 @@ def check_attention(w, vs, requests=None, tol=None):
 
 
 # -- acceptance ----------------------------------------------------------------
-def oracle_accept(w, temperature, seed, step, requests=None):
+def oracle_accept(w, temperature, seed, step, requests=None, topk=False):
+    # the library takes T as a 32-bit float: the oracle divides by that value
+    temperature = float(np.float32(temperature))
     res = {}
     for b in (range(w.B) if requests is None else requests):
         o, e = request_slice(w, b)
         pl = w.p_logits[o:e].detach().to("cpu", torch.float64).numpy()
+        if topk and temperature > 0:
+            res[b] = OA.accept_request_topk(w.parents[o:e], w.tokens[o:e], pl, temperature, seed,
+                                            step, b)
+            continue
         ql = None
         if temperature > 0:
             ql = w.q_logits[o:e].detach().to("cpu", torch.float64).numpy()
@@ -114,8 +120,8 @@ def oracle_accept(w, temperature, seed, step, requests=None):
     return res
 
 
-def check_accept(w, vs, temperature, seed, step, requests=None, max_flagged=1):
-    ref = oracle_accept(w, temperature, seed, step, requests)
+def check_accept(w, vs, temperature, seed, step, requests=None, max_flagged=1, topk=False):
+    ref = oracle_accept(w, temperature, seed, step, requests, topk=topk)
     acc = vs.acc
     alen = acc.accept_len.cpu().numpy()
     path = acc.path.cpu().numpy()
@@ -138,10 +144,14 @@ def check_accept(w, vs, temperature, seed, step, requests=None, max_flagged=1):
             assert (rel <= PROB_RTOL).all(), f"request {b}: child_p rel err {rel.max()}"
             ref_q = r["child_q"][1:]
             got_q = cq[o + 1:e]
+            if topk:                      # no draft distribution: NaN everywhere
+                assert np.isnan(got_q).all() and np.isnan(cq[o]), f"request {b}: child_q"
+                ref_q = got_q = np.zeros(0)
             relq = np.abs(got_q - ref_q) / np.maximum(np.abs(ref_q), 1e-30)
             assert (relq <= PROB_RTOL).all(), f"request {b}: child_q rel err {relq.max()}"
             # the library evaluates these in fp64; only the fp32 output rounds
-            assert max(rel.max(initial=0), relq.max(initial=0)) <= 3e-7, (rel.max(), relq.max())
+            worst = (rel.max(initial=0), relq.max(initial=0))
+            assert max(worst) <= 3e-7, worst
         else:
             assert np.array_equal(got_p, ref_p), f"request {b}: greedy child_p"
         res = r["result"]

@@ -29,7 +29,7 @@ def _declared():
 
 def test_header_declarations_are_all_exported():
     names = _declared()
-    assert "spec_tree_attn_verify" in names and len(names) == 10
+    assert "spec_tree_attn_verify" in names and len(names) == 11
     assert sorted(L.EXPORTS) == names
     lib = ctypes.CDLL(L.LIB_PATH)
     for n in names:
@@ -153,6 +153,28 @@ def test_greedy_needs_no_draft_logits():
     b = _B([0, 3, 9], [20, 30])
     # T = 0 with q NULL passes that check and fails later on the workspace size
     assert _acc(b, T=0.0, q=None, ws_bytes=16) == 8
+
+
+def _topk(b, T=1.0, vocab=1000, ld=1000, stride=8, ws_bytes=1 << 30, p=FAKE):
+    o = L.CAcceptOut(FAKE, FAKE, FAKE, None, None, None, None)
+    return L.LIB.spec_accept_topk(ctypes.byref(b.c), FAKE, FAKE, p, ld, vocab, T, 0, 0, stride,
+                                  ctypes.byref(o), FAKE, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(T=-1.0), 2, "temperature"),
+    (dict(p=None), 1, "p_logits_d"),
+    (dict(vocab=0), 7, "vocab"),
+    (dict(ld=1002), 2, "logits_ld"),
+    (dict(stride=0), 2, "path_stride"),
+    (dict(ws_bytes=16), 8, "workspace"),
+    (dict(p=FAKE + 8), 2, "aligned"),
+])
+def test_accept_topk_validation(kw, status, msg):
+    b = _B([0, 3, 9], [20, 30])
+    assert _topk(b, **kw) == status
+    assert msg in _err()
+    assert "spec_accept_topk" in L.EXPORTS
 
 
 def test_commit_and_append_validation():

@@ -7,5 +7,5 @@ the five calls of one verify step on torch-owned device buffers.
 from . import _lib  # noqa: F401  (fails loudly when the library is not built)
 from ._lib import (SpecError, Batch, Kv, AcceptOut, spec_tree_build_mask,  # noqa: F401
                    spec_kv_append, spec_tree_attn_workspace_bytes, spec_tree_attn_verify,
-                   spec_accept_workspace_bytes, spec_accept_sample, spec_kv_commit,
+                   spec_accept_workspace_bytes, spec_accept_sample, spec_accept_topk, spec_kv_commit,
                    spec_abi_version, spec_status_string)

@@ -30,7 +30,7 @@ STATUS_NAMES = {0: "SPEC_OK", 1: "SPEC_ERR_NULL", 2: "SPEC_ERR_SHAPE", 3: "SPEC_
 
 EXPORTS = ["spec_tree_build_mask", "spec_kv_append", "spec_tree_attn_workspace_bytes",
            "spec_tree_attn_verify", "spec_accept_workspace_bytes", "spec_accept_sample",
-           "spec_kv_commit", "spec_status_string", "spec_last_error", "spec_abi_version"]
+           "spec_accept_topk", "spec_kv_commit", "spec_status_string", "spec_last_error", "spec_abi_version"]
 
 
 class SpecError(RuntimeError):
@@ -77,6 +77,8 @@ def _load():
         "spec_accept_workspace_bytes": ([P(CBatch), i32], sz),
         "spec_accept_sample": ([P(CBatch), vp, vp, vp, vp, i64, i32, f32, u64, u64, i32,
                                 P(CAcceptOut), vp, sz, vp], ctypes.c_int),
+        "spec_accept_topk": ([P(CBatch), vp, vp, vp, i64, i32, f32, u64, u64, i32,
+                              P(CAcceptOut), vp, sz, vp], ctypes.c_int),
         "spec_kv_commit": ([P(CBatch), P(CKv), vp, vp, i32, vp, vp, vp], ctypes.c_int),
         "spec_status_string": ([ctypes.c_int], ctypes.c_char_p),
         "spec_last_error": ([], ctypes.c_char_p),
@@ -222,6 +224,17 @@ def spec_accept_sample(batch, parents, tokens, p_logits, q_logits, vocab, temper
                                   _ptr(p_logits), _ptr(q_logits), int(logits_ld), int(vocab),
                                   float(temperature), int(seed), int(step), out.path_stride,
                                   ctypes.byref(out.c), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def spec_accept_topk(batch, parents, tokens, p_logits, vocab, temperature, seed, step, out,
+                     workspace, logits_ld=None, stream=None):
+    if logits_ld is None:
+        logits_ld = p_logits.stride(0)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(LIB.spec_accept_topk(ctypes.byref(batch.c), _ptr(parents), _ptr(tokens),
+                                _ptr(p_logits), int(logits_ld), int(vocab), float(temperature),
+                                int(seed), int(step), out.path_stride, ctypes.byref(out.c),
+                                _ptr(workspace), ws_bytes, _stream(stream)))
 
 
 def spec_kv_commit(batch, kv, accept_len, path, new_len, freed_blocks=None, stream=None):

@@ -28,6 +28,14 @@
 //    further broadcast is needed; the owner of the drawn segment rescans it.
 //  * accept_greedy: temperature 0, one workgroup per request.
 //
+// Deterministic children (no draft rows): each child is a draft from the
+// point mass at its token, so a rejection removes that token from the
+// residual: R = P restricted to the tokens not yet rejected, divided by
+// N = 1 - (their P mass).  The sibling tests then need no vocabulary pass;
+// the one pass left is the final draw (P without the rejected tokens, or
+// P_leaf).  The emitted token follows P exactly (sampling without
+// replacement).
+//
 // Every quantity that decides an integer (accept tests, residual masses,
 // inverse-CDF boundaries) is evaluated in fp64, with a table-driven fp64
 // exponential, so decisions agree with a float64 reference except within
@@ -432,6 +440,7 @@ struct WalkShared {
   int kid_list[kMaxRows];
   int path[kMaxRows];
   int toks[kMaxRows + 1];
+  int rej[kMaxRows];                // deterministic children: tokens rejected at the current node
   double cp[kMaxRows];              // P_parent(x_c), Q_parent(x_c) of each child row
   double cq[kMaxRows];
   double lse[2][kMaxRows];          // log-sum-exp of logits / T: target, draft rows
@@ -446,7 +455,7 @@ struct WalkShared {
   int bad;
   int timeout;
   // walk state (broadcast from thread 0)
-  int u, len, ntok, done, accept, flags;
+  int u, len, ntok, done, accept, flags, nrej;
 };
 
 // Unnormalised weight of entry y: max(0, P_y - t Q_y), or P_y alone when
@@ -523,19 +532,33 @@ struct WalkCtx {
   double invT, lse_p, lse_q;
   int vocab, nseg, seg_lo, seg_hi, slice, S;
   double* seg;        // this request's [2][nseg]
+  const int* rej;     // tokens whose weight is 0 (LDS), nrej of them
+  int nrej;
 };
 
+// Bit j set iff entry y0 + j is one of the excluded tokens.
+SPEC_DEVICE int excluded4(const WalkCtx& c, int y0) {
+  int ex = 0;
+  for (int k = 0; k < c.nrej; ++k) {
+    const unsigned d = (unsigned)(c.rej[k] - y0);
+    if (d < 4u) ex |= 1 << d;
+  }
+  return ex;
+}
+
 // Sum of the weights of 4 consecutive entries starting at y0: max(0, P - tQ)
-// (or P alone), entries past the row masked to weight 0.
+// (or P alone, without the excluded tokens), entries past the row masked to
+// weight 0.
 template <bool kQ>
 SPEC_DEVICE double weight4(const WalkCtx& c, float4 pv, float4 qv, int y0, double t,
                            const double* tab) {
   const float pa[4] = {pv.x, pv.y, pv.z, pv.w};
   const float qa[4] = {qv.x, qv.y, qv.z, qv.w};
+  const int ex = kQ ? 0 : excluded4(c, y0);
   double acc = 0.0;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const bool in = y0 + j < c.vocab;                // the row's ragged end
+    const bool in = y0 + j < c.vocab && !((ex >> j) & 1);   // ragged end, excluded tokens
     const double P = exp_f64_clamped((double)(in ? pa[j] : -INFINITY) * c.invT - c.lse_p, tab);
     if (kQ) {
       const double Q = exp_f64_clamped((double)(in ? qa[j] : -INFINITY) * c.invT - c.lse_q, tab);
@@ -673,11 +696,12 @@ SPEC_DEVICE int walk_draw(WalkShared& sh, const WalkCtx& c, int pass, double t, 
   if (fs < c.seg_lo || fs >= c.seg_hi) return -1;
   // rescan the segment with the same arithmetic as the pass
   const int y0 = fs * kSeg + 4 * tid;
+  const int ex = need_q ? 0 : excluded4(c, y0);
   double w[4] = {0.0, 0.0, 0.0, 0.0};
   double acc = 0.0;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    if (y0 + j < c.vocab) {
+    if (y0 + j < c.vocab && !((ex >> j) & 1)) {
       w[j] = walk_weight(c.p[y0 + j], need_q ? c.q[y0 + j] : 0.f, c.invT, c.lse_p, c.lse_q, t,
                          need_q, sh.tab);
       acc += w[j];
@@ -808,11 +832,17 @@ struct WalkState {
 // is needed.  Coins: purpose 0 for the accept test of child c, purpose 1 for
 // the draw at the node where the walk stops.
 SPEC_DEVICE void walk_decide(WalkShared& sh, WalkState& st, uint64_t seed, uint64_t step, int b,
-                             int path_stride) {
+                             int path_stride, bool topk) {
   while (true) {
     const int u = st.u;
     const int k0 = sh.kid_start[u], k1 = sh.kid_start[u + 1];
     if (k1 == k0) {                      // leaf: bonus token from P_u
+      st.action = 1;
+      st.act_t = 0.0;
+      st.act_q = 0;
+      return;
+    }
+    if (st.kidx >= k1 && topk) {         // every child rejected: P without the rejected tokens
       st.action = 1;
       st.act_t = 0.0;
       st.act_q = 0;
@@ -832,8 +862,11 @@ SPEC_DEVICE void walk_decide(WalkShared& sh, WalkState& st, uint64_t seed, uint6
     const int x = sh.tok[ch];
     const double Px = sh.cp[ch], Qx = sh.cq[ch];
     const double r = verify_uniform(seed, step, (uint64_t)b, (uint64_t)ch, 0);
-    const double Rx = fmax(0.0, fma(-st.t, Qx, Px)) / st.N;
-    if (r * Qx < Rx) {                   // accept: move to the child
+    bool seen = false;                   // deterministic children: x rejected before has R(x) = 0
+    if (topk)
+      for (int k = 0; k < sh.nrej; ++k) seen |= (sh.rej[k] == x);
+    const double Rx = topk ? (seen ? 0.0 : Px / st.N) : fmax(0.0, fma(-st.t, Qx, Px)) / st.N;
+    if (topk ? (r < Rx) : (r * Qx < Rx)) {   // accept: move to the child
       if (sh.len >= path_stride) {
         sh.flags |= kFlagPathTruncated;
         st.action = 3;
@@ -846,6 +879,19 @@ SPEC_DEVICE void walk_decide(WalkShared& sh, WalkState& st, uint64_t seed, uint6
       st.t = 0.0;
       st.N = 1.0;
       st.pass_t = -1.0;
+      sh.nrej = 0;
+      continue;
+    }
+    if (topk) {                          // reject: drop x from the residual
+      st.kidx += 1;
+      if (seen || Px == 0.0) continue;   // (out-of-range tokens have Px = 0)
+      const double N2 = st.N - Px;
+      if (N2 > 0.0) {
+        st.N = N2;
+        sh.rej[sh.nrej++] = x;
+      } else {
+        sh.flags |= kFlagZeroResidual;
+      }
       continue;
     }
     // reject: the next residual needs G(t + N)
@@ -885,9 +931,11 @@ accept_walk_kernel(const int32_t* __restrict__ row_offsets, int R, int S,
   // This request's row statistics: each row's log-sum-exp from its chunk
   // partials (in chunk order), then each child's P_u(x_c), Q_u(x_c) in fp64.
   // Every slice computes them; slice 0 writes the fp32 outputs (NaN at roots
-  // and at rows whose parent is invalid).
+  // and at rows whose parent is invalid; Q is NaN everywhere without draft
+  // rows).
+  const bool topk = q_logits == nullptr;
   const double invT = 1.0 / (double)temperature;
-  for (int k = tid; k < 2 * n; k += blockDim.x) {
+  for (int k = tid; k < (topk ? n : 2 * n); k += blockDim.x) {
     const int which = k >= n ? 1 : 0;
     const int i = k - which * n;
     double ref, s;
@@ -901,7 +949,7 @@ accept_walk_kernel(const int32_t* __restrict__ row_offsets, int R, int S,
     float* dst = which ? out.child_q : out.child_p;
     const int pu = sh.par[i];
     double val = __longlong_as_double(0x7ff8000000000000LL);
-    if (i > 0 && pu >= 0 && pu < i) {
+    if (i > 0 && pu >= 0 && pu < i && !(which && topk)) {
       const int x = sh.tok[i];
       val = 0.0;
       if (x >= 0 && x < vocab) {
@@ -933,6 +981,7 @@ accept_walk_kernel(const int32_t* __restrict__ row_offsets, int R, int S,
     sh.ntok = 0;
     sh.flags = 0;
     sh.path[0] = 0;
+    sh.nrej = 0;
     st.u = 0;
     st.kidx = sh.kid_start[0];
     st.t = 0.0;
@@ -944,15 +993,17 @@ accept_walk_kernel(const int32_t* __restrict__ row_offsets, int R, int S,
   bool final_here = false;
   while (true) {
     if (tid == 0)
-      walk_decide(sh, st, seed, step, b, out.path_stride);
+      walk_decide(sh, st, seed, step, b, out.path_stride, topk);
     __syncthreads();
     const int action = st.action;
     if (action == 3) break;
     const int u = st.u;
     c.p = p_logits + (int64_t)(o + u) * ld;
-    c.q = q_logits + (int64_t)(o + u) * ld;
+    c.q = topk ? nullptr : q_logits + (int64_t)(o + u) * ld;
     c.lse_p = sh.lse[0][u];
     c.lse_q = st.act_q ? sh.lse[1][u] : 0.0;
+    c.rej = sh.rej;
+    c.nrej = topk ? sh.nrej : 0;
     const double act_t = st.act_t;
     const bool act_q = st.act_q != 0;
     if (action != 2) {
@@ -1083,7 +1134,8 @@ hipError_t launch_accept(const LaunchCtx& cx, int R, const int32_t* parents, con
   AcceptWs ws = accept_ws(workspace, R, cx.B, vocab);
   const int nch = ws.nch;
   const bool greedy = temperature == 0.0f;
-  const int rows = greedy ? R : 2 * R;
+  // q_logits == nullptr at T > 0: deterministic children, target rows only
+  const int rows = (greedy || !q_logits) ? R : 2 * R;
   if (greedy)
     hipLaunchKernelGGL(accept_stats_kernel<true>, dim3(rows * nch), dim3(kStatThreads), 0,
                        cx.stream, cx.row_offsets_d, cx.B, R, parents, p_logits, q_logits, ld, vocab,

@@ -239,17 +239,18 @@ size_t spec_accept_workspace_bytes(const spec_batch* batch, int32_t vocab) {
   return spec::accept_workspace_bytes(R, batch->batch, vocab);
 }
 
-spec_status spec_accept_sample(const spec_batch* batch, const int32_t* parents_d, const int32_t* tokens_d,
-                               const float* p_logits_d, const float* q_logits_d, int64_t logits_ld,
+static spec_status accept_call(const spec_batch* batch, const int32_t* parents_d,
+                               const int32_t* tokens_d, const float* p_logits_d,
+                               const float* q_logits_d, bool topk, int64_t logits_ld,
                                int32_t vocab, float temperature, uint64_t seed, uint64_t step,
                                int32_t path_stride, const spec_accept_out* out, void* workspace_d,
-                               size_t workspace_bytes, hipStream_t stream) {
+                               size_t workspace_bytes, hipStream_t stream, const char* name) {
   int R = 0;
   spec_status st = check_batch(batch, &R);
   if (st != SPEC_OK) return st;
   if (!parents_d || !tokens_d || !p_logits_d) return fail(SPEC_ERR_NULL, "parents_d, tokens_d and p_logits_d are required");
   if (!(temperature >= 0.0f) || temperature > 1e30f) return fail(SPEC_ERR_SHAPE, "temperature must be finite and >= 0");
-  if (temperature > 0.0f && !q_logits_d) return fail(SPEC_ERR_NULL, "q_logits_d is required when temperature > 0");
+  if (!topk && temperature > 0.0f && !q_logits_d) return fail(SPEC_ERR_NULL, "q_logits_d is required when temperature > 0");
   if (vocab < 1 || vocab > kMaxVocab) return fail(SPEC_ERR_UNSUPPORTED, "vocab = %d, supported 1..%d", vocab, kMaxVocab);
   if (logits_ld < vocab || logits_ld % 4) return fail(SPEC_ERR_SHAPE, "logits_ld = %lld must be >= vocab and a multiple of 4", (long long)logits_ld);
   if (!aligned16(p_logits_d) || (q_logits_d && !aligned16(q_logits_d)))
@@ -262,11 +263,32 @@ spec_status spec_accept_sample(const spec_batch* batch, const int32_t* parents_d
     return fail(SPEC_ERR_WORKSPACE, "accept workspace %zu bytes < required %zu", workspace_bytes, need);
   if (!aligned16(workspace_d)) return fail(SPEC_ERR_SHAPE, "workspace must be 16-byte aligned");
   return launched(spec::launch_accept(ctx(batch, stream), R, parents_d, tokens_d, p_logits_d,
-                                      temperature > 0.0f ? q_logits_d : nullptr, logits_ld, vocab,
-                                      temperature, seed, step, path_stride, out->accept_len_d,
-                                      out->path_d, out->tokens_d, out->accept_mask_d, out->child_p_d,
-                                      out->child_q_d, out->flags_d, workspace_d, walk_slices_override()),
-                  "spec_accept_sample");
+                                      (temperature > 0.0f && !topk) ? q_logits_d : nullptr,
+                                      logits_ld, vocab, temperature, seed, step, path_stride,
+                                      out->accept_len_d, out->path_d, out->tokens_d,
+                                      out->accept_mask_d, out->child_p_d, out->child_q_d,
+                                      out->flags_d, workspace_d, walk_slices_override()),
+                  name);
+}
+
+spec_status spec_accept_sample(const spec_batch* batch, const int32_t* parents_d, const int32_t* tokens_d,
+                               const float* p_logits_d, const float* q_logits_d, int64_t logits_ld,
+                               int32_t vocab, float temperature, uint64_t seed, uint64_t step,
+                               int32_t path_stride, const spec_accept_out* out, void* workspace_d,
+                               size_t workspace_bytes, hipStream_t stream) {
+  return accept_call(batch, parents_d, tokens_d, p_logits_d, q_logits_d, false, logits_ld, vocab,
+                     temperature, seed, step, path_stride, out, workspace_d, workspace_bytes, stream,
+                     "spec_accept_sample");
+}
+
+spec_status spec_accept_topk(const spec_batch* batch, const int32_t* parents_d, const int32_t* tokens_d,
+                             const float* p_logits_d, int64_t logits_ld, int32_t vocab,
+                             float temperature, uint64_t seed, uint64_t step, int32_t path_stride,
+                             const spec_accept_out* out, void* workspace_d, size_t workspace_bytes,
+                             hipStream_t stream) {
+  return accept_call(batch, parents_d, tokens_d, p_logits_d, nullptr, true, logits_ld, vocab,
+                     temperature, seed, step, path_stride, out, workspace_d, workspace_bytes, stream,
+                     "spec_accept_topk");
 }
 
 spec_status spec_kv_commit(const spec_batch* batch, const spec_kv* kv, const int32_t* accept_len_d,

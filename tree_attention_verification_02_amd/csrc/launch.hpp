@@ -60,7 +60,8 @@ hipError_t launch_attention_f32(const LaunchCtx& cx, int R, const KvAddr& addr, 
                                 const float* q, const uint64_t* mask, int words, float scale,
                                 const float* k_cache, const float* v_cache, void* out, int out_f32);
 
-// Acceptance.
+// Acceptance.  At temperature > 0, q_logits == nullptr selects deterministic
+// children (each child a point-mass draft; no draft rows are read).
 size_t accept_workspace_bytes(int R, int B, int vocab);
 hipError_t launch_accept(const LaunchCtx& cx, int R, const int32_t* parents, const int32_t* tokens,
                          const float* p_logits, const float* q_logits, int64_t ld, int vocab,

@@ -29,8 +29,14 @@ def pack_visibility(visibility, row_offsets, words):
 
 
 class VerifyStep:
-    def __init__(self, w, path_stride=None, out_dtype=None, temperature=None, seed=None, step=None):
-        """``w`` is any object with the workload fields (see workloads.gen.Workload)."""
+    def __init__(self, w, path_stride=None, out_dtype=None, temperature=None, seed=None, step=None,
+                 acceptance="sample"):
+        """``w`` is any object with the workload fields (see workloads.gen.Workload).
+        ``acceptance``: "sample" (children drawn from the draft rows) or "topk"
+        (deterministic children: spec_accept_topk, draft rows unused)."""
+        if acceptance not in ("sample", "topk"):
+            raise ValueError(f"acceptance must be 'sample' or 'topk', not {acceptance!r}")
+        self.acceptance = acceptance
         dev = w.q.device
         self.w = w
         self.batch = L.Batch(w.row_offsets, w.prefix_len, dev)
@@ -90,6 +96,11 @@ class VerifyStep:
                                 self.attn_out, self.attn_ws, stream)
 
     def accept(self, stream=None):
+        if self.acceptance == "topk":
+            L.spec_accept_topk(self.batch, self.parents, self.tokens, self.w.p_logits, self.w.V,
+                               self.temperature, self.seed, self.step, self.acc, self.acc_ws,
+                               stream=stream)
+            return
         q = self.w.q_logits if self.temperature > 0 else None
         L.spec_accept_sample(self.batch, self.parents, self.tokens, self.w.p_logits, q,
                              self.w.V, self.temperature, self.seed, self.step, self.acc,

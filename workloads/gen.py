@@ -15,7 +15,10 @@ tensors are drawn with a seeded ``torch.Generator`` on the requested device
 
 Draft tokens are sampled the way a drafter would: child ``c`` of row ``u`` is
 a draw from softmax(q_logits[u] / T) with T = 1, taken with the Gumbel-max
-trick (argmax of logits plus Gumbel noise), independently per child.
+trick (argmax of logits plus Gumbel noise), independently per child.  With
+``draft="topk"`` the children are the drafter's top choices instead: the
+i-th child of ``u`` (in row order) gets the i-th largest entry of
+q_logits[u] (a stable sort, so equal logits keep vocabulary order).
 """
 from __future__ import annotations
 
@@ -269,6 +272,19 @@ def make(name: str, device: str = "cpu", **over) -> Workload:
         tokens[child_rows[s:s + CH]] = pick.cpu().numpy().astype(np.int32)
     root_rows = row_offsets[:-1]
     tokens[root_rows] = rng.integers(0, V, size=B)
+    if cfg.get("draft", "sample") == "topk":
+        kids = {}
+        for c, u in zip(child_rows, par_rows):
+            kids.setdefault(int(u), []).append(int(c))
+        us = sorted(kids)
+        kmax = max(len(v) for v in kids.values())
+        for s in range(0, len(us), CH):
+            blk = us[s:s + CH]
+            order = torch.sort(q_logits[torch.tensor(blk, device=device)], dim=1,
+                               descending=True, stable=True).indices[:, :kmax].cpu().numpy()
+            for j, u in enumerate(blk):
+                for i, c in enumerate(kids[u]):
+                    tokens[c] = int(order[j, i])
 
     visibility = None
     if cfg.get("visibility") is not None:
