@@ -22,10 +22,13 @@ Pages followed (title, section):
 * "万字综述 10+ 种 LLM 投机采样推理加速方案" -- section 5.2 (tree-based
   parallel decoding equals sequence-based decoding), section 4.3 / 8.1
   (argmax sampling at temperature 0, longest matching prefix).
+* "投机推理算法的常见优化手段" (cnblogs) -- draft-tree generation (EAGLE-2
+  expansion of the most probable leaves) and dynamic draft length (ECHO's
+  global budget and checkpoints).  -> ``draft``.
 
 Readings of the pages where they are silent or garbled are listed in the
 module that takes them.  Every function here is pinned by the CPU tests
 against printed values, closed forms, library routines or brute force,
 except where a module header says "parity unpinned".
 """
-from . import philox, tree, attention, accept, kv  # noqa: F401
+from . import philox, tree, attention, accept, kv, draft  # noqa: F401
