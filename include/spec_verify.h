@@ -10,6 +10,8 @@
  *   spec_tree_attn_verify  tree attention: prefix + ancestors only
  *   spec_accept_sample     lossless acceptance walk + final token
  *   spec_accept_topk       the same for deterministic (top-k) children
+ *   spec_draft_begin / spec_draft_expand / spec_draft_select
+ *                          build dynamic draft trees under a batch budget
  *   spec_kv_commit         compact the accepted path's K/V, roll back the rest
  *
  * Pages this interface restates (title, section):
@@ -283,6 +285,88 @@ spec_status spec_kv_commit(const spec_batch *batch, const spec_kv *kv,
                            const int32_t *accept_len_d, const int32_t *path_d,
                            int32_t path_stride, int32_t *new_len_d,
                            int32_t *freed_blocks_d, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Dynamic draft trees -- [TREE] draft-tree generation (EAGLE-2: each round
+ * expands only the K most probable bottom-layer leaves, a leaf's
+ * probability being the product of the node probabilities on its path) and
+ * dynamic draft length (ECHO: one budget of verify rows shared by the batch,
+ * checkpoints at fixed depths that cut low-confidence branches, budget that
+ * weak requests leave going to confident ones).  These calls build, on the
+ * device, the parents/tokens/row_offsets that the verify calls above take.
+ *
+ * spec_draft_tree holds each request's nodes in creation order (node 0 is
+ * the root).  All arrays are device memory owned by the caller:
+ *   parent_d, token_d, depth_d  int32 [batch][capacity]
+ *   score_d                     f32   [batch][capacity]  product of the path's
+ *                               probabilities, each step rounded to f32
+ *   count_d                     int32 [batch]  nodes so far
+ *   frontier_d                  int32 [batch][topk]  nodes the next round
+ *                               expands, -1 padded
+ *   flags_d                     int32 [batch]  SPEC_DRAFT_FLAG_* bits
+ * Limits: 1 <= topk <= 16, 1 <= capacity <= 4096.
+ *
+ * spec_draft_begin: every request gets its root (token root_tokens_d[b],
+ * score 1) as the only node and the only frontier entry; flags cleared.
+ *
+ * spec_draft_expand: one round.  cand_tokens_d int32 / cand_probs_d f32
+ * [batch][topk][topk]: row i holds the drafter's topk candidates (token,
+ * probability) for the request's i-th frontier node (rows past the frontier
+ * are ignored).  Each frontier node gets topk children in that order, ids
+ * continuing the count; a child's score is f32(score(parent) * p) with p
+ * clamped to [0, 1] (NaN -> 0).  The next frontier is the topk
+ * highest-scoring new nodes (ties: lower id), skipping, when the new depth
+ * equals gate_depth_h[g], nodes scoring below gate_score_h[g]
+ * (checkpoints; n_gates <= 8, host arrays).  An empty frontier ends the
+ * request's growth.  A round that does not fit in `capacity` appends
+ * nothing, ends growth and sets SPEC_DRAFT_FLAG_CAPACITY; a count outside
+ * 1..capacity or a frontier entry that is not an existing node (state not
+ * made by these calls) ends growth with SPEC_DRAFT_FLAG_BAD_STATE, never a
+ * fault.  cand arrays must hold batch * topk * topk entries.
+ *
+ * spec_draft_select: keeps every root plus the budget_rows - batch
+ * highest-scoring non-root nodes of the whole batch (ties: lower request,
+ * then lower id), taken among each request's max_rows - 1 best nodes (score
+ * descending, id ascending).  A child never outscores its parent and has
+ * the larger id, so each request's kept nodes form a tree.  Outputs:
+ *   row_offsets_d  int32 [batch + 1]
+ *   parents_d, tokens_d, node_of_row_d (optional)  int32 [rows_capacity]:
+ *     request b's rows are its root, then its kept nodes in id order
+ *     (breadth-first); parents are local rows (-1 at the root);
+ *     node_of_row gives each row's node id.
+ * Requires budget_rows >= batch, 1 <= max_rows <= min(SPEC_MAX_TREE_ROWS,
+ * capacity), batch <= 4096, batch * (max_rows - 1) <= 16384 and
+ * rows_capacity >= min(budget_rows, batch * max_rows).  The verify calls
+ * need row_offsets on the host too: copy the batch + 1 entries back.
+ * workspace >= spec_draft_select_workspace_bytes(batch, max_rows).
+ */
+#define SPEC_DRAFT_FLAG_CAPACITY 1   /* a round did not fit; growth ended */
+#define SPEC_DRAFT_FLAG_BAD_STATE 2  /* count/frontier not made by begin/expand; growth ended */
+
+typedef struct {
+  int32_t batch;
+  int32_t topk;
+  int32_t capacity;
+  int32_t *parent_d;
+  int32_t *token_d;
+  float *score_d;
+  int32_t *depth_d;
+  int32_t *count_d;
+  int32_t *frontier_d;
+  int32_t *flags_d;
+} spec_draft_tree;
+
+spec_status spec_draft_begin(const spec_draft_tree *tree, const int32_t *root_tokens_d,
+                             hipStream_t stream);
+spec_status spec_draft_expand(const spec_draft_tree *tree, const int32_t *cand_tokens_d,
+                              const float *cand_probs_d, int32_t n_gates,
+                              const int32_t *gate_depth_h, const float *gate_score_h,
+                              hipStream_t stream);
+size_t spec_draft_select_workspace_bytes(int32_t batch, int32_t max_rows);
+spec_status spec_draft_select(const spec_draft_tree *tree, int32_t budget_rows, int32_t max_rows,
+                              int32_t *row_offsets_d, int32_t *parents_d, int32_t *tokens_d,
+                              int32_t *node_of_row_d, int32_t rows_capacity, void *workspace_d,
+                              size_t workspace_bytes, hipStream_t stream);
 
 const char *spec_status_string(spec_status status);
 const char *spec_last_error(void);

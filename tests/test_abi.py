@@ -29,7 +29,7 @@ def _declared():
 
 def test_header_declarations_are_all_exported():
     names = _declared()
-    assert "spec_tree_attn_verify" in names and len(names) == 11
+    assert "spec_tree_attn_verify" in names and len(names) == 15
     assert sorted(L.EXPORTS) == names
     lib = ctypes.CDLL(L.LIB_PATH)
     for n in names:
@@ -242,3 +242,54 @@ def test_binding_packs_caller_masks_like_the_oracle():
     got = pack_visibility(vis, ro, words).view(np.uint64)
     for b, v in enumerate(vis):
         assert np.array_equal(got[ro[b]:ro[b + 1]], OT.pack_words(v, words))
+
+
+def _tree(batch=4, topk=5, capacity=64, null=None):
+    arr = [FAKE] * 7
+    if null is not None:
+        arr[null] = None
+    return L.CDraftTree(batch, topk, capacity, *arr)
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(batch=0), 2, "batch"),
+    (dict(topk=0), 7, "topk"),
+    (dict(topk=17), 7, "topk"),
+    (dict(capacity=4097), 7, "capacity"),
+    (dict(null=3), 1, "spec_draft_tree"),
+])
+def test_draft_tree_validation(kw, status, msg):
+    t = _tree(**kw)
+    assert L.LIB.spec_draft_begin(ctypes.byref(t), FAKE, None) == status
+    assert msg in _err()
+
+
+def test_draft_expand_and_select_validation():
+    t = _tree()
+    gd = np.array([2] * 9, dtype=np.int32)
+    gs = np.array([0.1] * 9, dtype=np.float32)
+    ex = L.LIB.spec_draft_expand
+    assert ex(ctypes.byref(t), FAKE, FAKE, 9, gd.ctypes.data, gs.ctypes.data, None) == 7
+    assert ex(ctypes.byref(t), FAKE, FAKE, 1, None, None, None) == 1
+    gs[0] = -1.0
+    assert ex(ctypes.byref(t), FAKE, FAKE, 1, gd.ctypes.data, gs.ctypes.data, None) == 2
+    gd[0] = 0
+    assert ex(ctypes.byref(t), FAKE, FAKE, 1, gd.ctypes.data, gs.ctypes.data, None) == 2
+    assert ex(ctypes.byref(t), None, FAKE, 0, None, None, None) == 1
+    sel = L.LIB.spec_draft_select
+    need = L.LIB.spec_draft_select_workspace_bytes(4, 16)
+    assert need > 0
+    ok = dict(budget=40, max_rows=16, cap=64, ws=need)
+
+    def s(**kw):
+        a = dict(ok, **kw)
+        return sel(ctypes.byref(t), a["budget"], a["max_rows"], FAKE, FAKE, FAKE, None, a["cap"],
+                   FAKE, a["ws"], None)
+    assert s(budget=3) == 2 and "budget_rows" in _err()
+    assert s(max_rows=0) == 2
+    assert s(max_rows=65) == 2 and "max_rows" in _err()        # above capacity 64
+    assert s(cap=39) == 4 and "rows_capacity" in _err()
+    assert s(ws=need - 1) == 8
+    big = _tree(batch=4096, capacity=256)
+    assert sel(ctypes.byref(big), 5000, 8, FAKE, FAKE, FAKE, None, 5000, FAKE, 1 << 30, None) == 7
+    assert "batch * (max_rows - 1)" in _err()

@@ -24,13 +24,15 @@ SPEC_KV_CONTIGUOUS, SPEC_KV_PAGED = 0, 1
 SPEC_MAX_TREE_ROWS = 256
 SPEC_FLAG_ZERO_RESIDUAL, SPEC_FLAG_PATH_TRUNCATED, SPEC_FLAG_BAD_TREE = 1, 2, 4
 SPEC_FLAG_SYNC_TIMEOUT = 8
+SPEC_DRAFT_FLAG_CAPACITY = 1
 STATUS_NAMES = {0: "SPEC_OK", 1: "SPEC_ERR_NULL", 2: "SPEC_ERR_SHAPE", 3: "SPEC_ERR_TREE",
                 4: "SPEC_ERR_CAPACITY", 5: "SPEC_ERR_DTYPE", 6: "SPEC_ERR_HIP",
                 7: "SPEC_ERR_UNSUPPORTED", 8: "SPEC_ERR_WORKSPACE"}
 
 EXPORTS = ["spec_tree_build_mask", "spec_kv_append", "spec_tree_attn_workspace_bytes",
            "spec_tree_attn_verify", "spec_accept_workspace_bytes", "spec_accept_sample",
-           "spec_accept_topk", "spec_kv_commit", "spec_status_string", "spec_last_error", "spec_abi_version"]
+           "spec_accept_topk", "spec_kv_commit", "spec_draft_begin", "spec_draft_expand",
+           "spec_draft_select_workspace_bytes", "spec_draft_select", "spec_status_string", "spec_last_error", "spec_abi_version"]
 
 
 class SpecError(RuntimeError):
@@ -60,6 +62,14 @@ class CAcceptOut(ctypes.Structure):
                 ("flags_d", ctypes.c_void_p)]
 
 
+class CDraftTree(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("topk", ctypes.c_int32), ("capacity", ctypes.c_int32),
+                ("parent_d", ctypes.c_void_p), ("token_d", ctypes.c_void_p),
+                ("score_d", ctypes.c_void_p), ("depth_d", ctypes.c_void_p),
+                ("count_d", ctypes.c_void_p), ("frontier_d", ctypes.c_void_p),
+                ("flags_d", ctypes.c_void_p)]
+
+
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with "
@@ -80,6 +90,11 @@ def _load():
         "spec_accept_topk": ([P(CBatch), vp, vp, vp, i64, i32, f32, u64, u64, i32,
                               P(CAcceptOut), vp, sz, vp], ctypes.c_int),
         "spec_kv_commit": ([P(CBatch), P(CKv), vp, vp, i32, vp, vp, vp], ctypes.c_int),
+        "spec_draft_begin": ([P(CDraftTree), vp, vp], ctypes.c_int),
+        "spec_draft_expand": ([P(CDraftTree), vp, vp, i32, vp, vp, vp], ctypes.c_int),
+        "spec_draft_select_workspace_bytes": ([i32, i32], sz),
+        "spec_draft_select": ([P(CDraftTree), i32, i32, vp, vp, vp, vp, i32, vp, sz, vp],
+                              ctypes.c_int),
         "spec_status_string": ([ctypes.c_int], ctypes.c_char_p),
         "spec_last_error": ([], ctypes.c_char_p),
         "spec_abi_version": ([], ctypes.c_int),
@@ -241,6 +256,54 @@ def spec_kv_commit(batch, kv, accept_len, path, new_len, freed_blocks=None, stre
     _check(LIB.spec_kv_commit(ctypes.byref(batch.c), ctypes.byref(kv.c), _ptr(accept_len),
                               _ptr(path), int(path.shape[1]), _ptr(new_len), _ptr(freed_blocks),
                               _stream(stream)))
+
+
+class DraftTree:
+    """Device state of a batch of growing draft trees (torch-owned arrays)."""
+
+    def __init__(self, batch, topk, capacity, device):
+        i32 = dict(dtype=torch.int32, device=device)
+        self.parent = torch.empty((batch, capacity), **i32)
+        self.token = torch.empty((batch, capacity), **i32)
+        self.score = torch.empty((batch, capacity), dtype=torch.float32, device=device)
+        self.depth = torch.empty((batch, capacity), **i32)
+        self.count = torch.empty(batch, **i32)
+        self.frontier = torch.empty((batch, topk), **i32)
+        self.flags = torch.empty(batch, **i32)
+        self.c = CDraftTree(int(batch), int(topk), int(capacity), _ptr(self.parent),
+                            _ptr(self.token), _ptr(self.score), _ptr(self.depth),
+                            _ptr(self.count), _ptr(self.frontier), _ptr(self.flags))
+
+    @property
+    def batch(self):
+        return int(self.c.batch)
+
+
+def spec_draft_begin(tree, root_tokens, stream=None):
+    _check(LIB.spec_draft_begin(ctypes.byref(tree.c), _ptr(root_tokens), _stream(stream)))
+
+
+def spec_draft_expand(tree, cand_tokens, cand_probs, gates=(), stream=None):
+    n = len(gates)
+    gd = np.ascontiguousarray([int(d) for d, _ in gates] or [0], dtype=np.int32)
+    gs = np.ascontiguousarray([float(t) for _, t in gates] or [0.0], dtype=np.float32)
+    _check(LIB.spec_draft_expand(ctypes.byref(tree.c), _ptr(cand_tokens), _ptr(cand_probs), n,
+                                 _ptr(gd), _ptr(gs), _stream(stream)))
+
+
+def spec_draft_select_workspace_bytes(batch, max_rows):
+    n = LIB.spec_draft_select_workspace_bytes(int(batch), int(max_rows))
+    if n == 0:
+        raise SpecError(2, LIB.spec_last_error().decode())
+    return int(n)
+
+
+def spec_draft_select(tree, budget_rows, max_rows, row_offsets, parents, tokens, workspace,
+                      node_of_row=None, stream=None):
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(LIB.spec_draft_select(ctypes.byref(tree.c), int(budget_rows), int(max_rows),
+                                 _ptr(row_offsets), _ptr(parents), _ptr(tokens), _ptr(node_of_row),
+                                 int(parents.numel()), _ptr(workspace), ws_bytes, _stream(stream)))
 
 
 def spec_abi_version():

@@ -18,6 +18,8 @@ static_assert(SPEC_FLAG_ZERO_RESIDUAL == spec::kFlagZeroResidual, "flag");
 static_assert(SPEC_FLAG_PATH_TRUNCATED == spec::kFlagPathTruncated, "flag");
 static_assert(SPEC_FLAG_BAD_TREE == spec::kFlagBadTree, "flag");
 static_assert(SPEC_FLAG_SYNC_TIMEOUT == spec::kFlagSyncTimeout, "flag");
+static_assert(SPEC_DRAFT_FLAG_CAPACITY == spec::kDraftFlagCapacity, "flag");
+static_assert(SPEC_DRAFT_FLAG_BAD_STATE == spec::kDraftFlagBadState, "flag");
 
 namespace {
 
@@ -304,6 +306,89 @@ spec_status spec_kv_commit(const spec_batch* batch, const spec_kv* kv, const int
                                          path_d, path_stride, kv->k, kv->v, new_len_d,
                                          kv->layout == SPEC_KV_PAGED ? freed_blocks_d : nullptr),
                   "spec_kv_commit");
+}
+
+static spec_status check_draft(const spec_draft_tree* t) {
+  if (!t) return fail(SPEC_ERR_NULL, "tree is NULL");
+  if (t->batch < 1) return fail(SPEC_ERR_SHAPE, "batch = %d, need >= 1", t->batch);
+  if (t->topk < 1 || t->topk > spec::kDraftMaxK)
+    return fail(SPEC_ERR_UNSUPPORTED, "topk = %d, supported 1..%d", t->topk, spec::kDraftMaxK);
+  if (t->capacity < 1 || t->capacity > spec::kDraftMaxNodes)
+    return fail(SPEC_ERR_UNSUPPORTED, "capacity = %d, supported 1..%d", t->capacity, spec::kDraftMaxNodes);
+  if ((int64_t)t->batch * t->capacity >= (1ll << 32))
+    return fail(SPEC_ERR_SHAPE, "batch * capacity must stay below 2^32");
+  if (!t->parent_d || !t->token_d || !t->score_d || !t->depth_d || !t->count_d || !t->frontier_d || !t->flags_d)
+    return fail(SPEC_ERR_NULL, "every spec_draft_tree array is required");
+  return SPEC_OK;
+}
+
+static spec::DraftTree draft_of(const spec_draft_tree* t) {
+  return spec::DraftTree{t->batch, t->topk, t->capacity, t->parent_d, t->token_d, t->score_d,
+                         t->depth_d, t->count_d, t->frontier_d, t->flags_d};
+}
+
+spec_status spec_draft_begin(const spec_draft_tree* tree, const int32_t* root_tokens_d, hipStream_t stream) {
+  spec_status st = check_draft(tree);
+  if (st != SPEC_OK) return st;
+  if (!root_tokens_d) return fail(SPEC_ERR_NULL, "root_tokens_d is required");
+  return launched(spec::launch_draft_begin(draft_of(tree), root_tokens_d, stream), "spec_draft_begin");
+}
+
+spec_status spec_draft_expand(const spec_draft_tree* tree, const int32_t* cand_tokens_d,
+                              const float* cand_probs_d, int32_t n_gates, const int32_t* gate_depth_h,
+                              const float* gate_score_h, hipStream_t stream) {
+  spec_status st = check_draft(tree);
+  if (st != SPEC_OK) return st;
+  if (!cand_tokens_d || !cand_probs_d) return fail(SPEC_ERR_NULL, "cand_tokens_d and cand_probs_d are required");
+  if (n_gates < 0 || n_gates > spec::kDraftMaxGates)
+    return fail(SPEC_ERR_UNSUPPORTED, "n_gates = %d, supported 0..%d", n_gates, spec::kDraftMaxGates);
+  if (n_gates > 0 && (!gate_depth_h || !gate_score_h)) return fail(SPEC_ERR_NULL, "gate arrays are required when n_gates > 0");
+  spec::DraftGates g{};
+  g.n = n_gates;
+  for (int i = 0; i < n_gates; ++i) {
+    if (gate_depth_h[i] < 1) return fail(SPEC_ERR_SHAPE, "gate_depth[%d] = %d, need >= 1", i, gate_depth_h[i]);
+    if (!(gate_score_h[i] >= 0.0f) || gate_score_h[i] > 1e30f)
+      return fail(SPEC_ERR_SHAPE, "gate_score[%d] must be finite and >= 0", i);
+    g.depth[i] = gate_depth_h[i];
+    g.score[i] = gate_score_h[i];
+  }
+  return launched(spec::launch_draft_expand(draft_of(tree), cand_tokens_d, cand_probs_d, g, stream),
+                  "spec_draft_expand");
+}
+
+size_t spec_draft_select_workspace_bytes(int32_t batch, int32_t max_rows) {
+  if (batch < 1 || max_rows < 1) {
+    fail(SPEC_ERR_SHAPE, "batch and max_rows must be >= 1");
+    return 0;
+  }
+  return spec::draft_select_workspace_bytes(batch, max_rows);
+}
+
+spec_status spec_draft_select(const spec_draft_tree* tree, int32_t budget_rows, int32_t max_rows,
+                              int32_t* row_offsets_d, int32_t* parents_d, int32_t* tokens_d,
+                              int32_t* node_of_row_d, int32_t rows_capacity, void* workspace_d,
+                              size_t workspace_bytes, hipStream_t stream) {
+  spec_status st = check_draft(tree);
+  if (st != SPEC_OK) return st;
+  const int B = tree->batch;
+  if (B > spec::kDraftSelMaxB) return fail(SPEC_ERR_UNSUPPORTED, "batch = %d, selection supports up to %d", B, spec::kDraftSelMaxB);
+  if (max_rows < 1 || max_rows > SPEC_MAX_TREE_ROWS || max_rows > tree->capacity)
+    return fail(SPEC_ERR_SHAPE, "max_rows = %d, need 1..min(%d, capacity %d)", max_rows, SPEC_MAX_TREE_ROWS, tree->capacity);
+  if ((int64_t)B * (max_rows - 1) > spec::kDraftSelMax)
+    return fail(SPEC_ERR_UNSUPPORTED, "batch * (max_rows - 1) = %lld, supported up to %d",
+                (long long)B * (max_rows - 1), spec::kDraftSelMax);
+  if (budget_rows < B) return fail(SPEC_ERR_SHAPE, "budget_rows = %d < batch %d (every root takes a row)", budget_rows, B);
+  if (!row_offsets_d || !parents_d || !tokens_d) return fail(SPEC_ERR_NULL, "row_offsets_d, parents_d and tokens_d are required");
+  const int64_t most = std::min<int64_t>(budget_rows, (int64_t)B * max_rows);
+  if (rows_capacity < most)
+    return fail(SPEC_ERR_CAPACITY, "rows_capacity = %d < %lld rows the selection may emit", rows_capacity, (long long)most);
+  const size_t need = spec::draft_select_workspace_bytes(B, max_rows);
+  if (!workspace_d || workspace_bytes < need)
+    return fail(SPEC_ERR_WORKSPACE, "select workspace %zu bytes < required %zu", workspace_bytes, need);
+  if (!aligned16(workspace_d)) return fail(SPEC_ERR_SHAPE, "workspace must be 16-byte aligned");
+  return launched(spec::launch_draft_select(draft_of(tree), budget_rows, max_rows, row_offsets_d, parents_d,
+                                            tokens_d, node_of_row_d, workspace_d, stream),
+                  "spec_draft_select");
 }
 
 }  // extern "C"

@@ -70,4 +70,39 @@ hipError_t launch_accept(const LaunchCtx& cx, int R, const int32_t* parents, con
                          uint8_t* accept_mask, float* child_p, float* child_q, int32_t* flags,
                          void* workspace, int slices_override);
 
+// Dynamic draft trees (EAGLE-2 rounds, global row budget).
+constexpr int kDraftMaxK = 16;          // children per expanded node, nodes expanded per round
+constexpr int kDraftMaxNodes = 4096;    // nodes per request (capacity), root included
+constexpr int kDraftMaxGates = 8;       // checkpoints
+constexpr int kDraftSelPer = 16;        // compact candidates per selection thread
+constexpr int kDraftSelMax = 1024 * kDraftSelPer;   // B * (max_rows - 1) limit
+constexpr int kDraftSelMaxB = 4096;     // requests per selection
+constexpr int kDraftFlagCapacity = 1;
+constexpr int kDraftFlagBadState = 2;
+
+struct DraftTree {
+  int batch, topk, capacity;
+  int32_t* parent;    // [batch][capacity]
+  int32_t* token;
+  float* score;
+  int32_t* depth;
+  int32_t* count;     // [batch]
+  int32_t* frontier;  // [batch][topk]
+  int32_t* flags;     // [batch]
+};
+
+struct DraftGates {
+  int n;
+  int depth[kDraftMaxGates];
+  float score[kDraftMaxGates];
+};
+
+hipError_t launch_draft_begin(const DraftTree& t, const int32_t* root_tokens, hipStream_t stream);
+hipError_t launch_draft_expand(const DraftTree& t, const int32_t* cand_tokens,
+                               const float* cand_probs, const DraftGates& g, hipStream_t stream);
+size_t draft_select_workspace_bytes(int B, int max_rows);
+hipError_t launch_draft_select(const DraftTree& t, int budget_rows, int max_rows,
+                               int32_t* row_offsets, int32_t* parents, int32_t* tokens,
+                               int32_t* node_of_row, void* workspace, hipStream_t stream);
+
 }  // namespace spec

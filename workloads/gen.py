@@ -153,6 +153,8 @@ def _tree_for(cfg, rng, B):
         return [trees.cartesian(cfg["tree"][1]) for _ in range(B)]
     if kind == "kschedule":
         return [trees.k_schedule(cfg["tree"][1]) for _ in range(B)]
+    if kind == "given":                 # trees supplied by the caller (e.g. a tree builder)
+        return [np.asarray(t, dtype=np.int32) for t in cfg["tree"][1]]
     if kind == "eagle2":
         topk, max_depth = cfg["tree"][1], cfg["tree"][2]
         sizes = trees.echo_budget(rng, B, cfg.get("kmax_per_req", 16) * B)
@@ -272,6 +274,9 @@ def make(name: str, device: str = "cpu", **over) -> Workload:
         tokens[child_rows[s:s + CH]] = pick.cpu().numpy().astype(np.int32)
     root_rows = row_offsets[:-1]
     tokens[root_rows] = rng.integers(0, V, size=B)
+    if cfg.get("given_tokens") is not None:      # the tree builder's tokens
+        tokens = np.asarray(cfg["given_tokens"], dtype=np.int32).copy()
+        assert tokens.shape == (R,)
     if cfg.get("draft", "sample") == "topk":
         kids = {}
         for c, u in zip(child_rows, par_rows):
