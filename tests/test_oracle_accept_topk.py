@@ -151,12 +151,3 @@ def test_planted_mistakes_fail_the_chi_square(old, new):
     res = _run(mut, parents, tokens, P, 100000, seed=41)
     assert _chi2_pvalue(np.array([r.tokens[0] for r in res]), P) < 1e-6
 
-
-def test_topk_workload_children_are_the_drafters_top_choices():
-    import workloads as W
-    w = W.make("medusa", L=64, V=300, Hq=2, Hkv=2, draft="topk")
-    q = w.host("q_logits")
-    for u in np.nonzero(w.nonleaf)[0]:
-        kids = [c for c in range(len(w.parents)) if c > 0 and w.parents[c] == u]
-        order = np.argsort(-q[u], kind="stable")
-        assert list(w.tokens[kids]) == list(order[:len(kids)])

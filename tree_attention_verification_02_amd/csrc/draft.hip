@@ -166,17 +166,22 @@ draft_rank_kernel(DraftTree t, int max_rows, SelectWs ws) {
   }
 }
 
-// One workgroup: the take-th smallest key over all compact lists (radix
-// select, 8 bits per round), then kept[b] = how many of list b's keys are
-// <= it.  Keys are unique, so exactly `take` keys are kept.
+// One workgroup: the (take + 1)-th smallest key over all compact lists
+// (radix select, 8 bits per round: an LDS histogram, then one wave scans
+// the 256 bins), then kept[b] = how many of list b's keys are below it.
+// Keys are unique, so exactly `take` keys are kept; once the current digit
+// holds a single key, that key is the answer and the rounds stop.
 __global__ void __launch_bounds__(kSelThreads)
 draft_threshold_kernel(int B, int max_rows, int take, SelectWs ws) {
   __shared__ int hist[256];
-  __shared__ int s_digit, s_need;
+  __shared__ int s_digit, s_need, s_count, s_total;
+  __shared__ uint64_t s_kth;
   __shared__ int s_kept[kDraftSelMaxB];
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63;
   const int lim = max_rows - 1;
   const int slots = B * lim;
+  if (tid == 0) s_total = 0;
+  for (int i = tid; i < B; i += kSelThreads) s_kept[i] = 0;
   uint64_t key[kDraftSelPer];
 #pragma unroll
   for (int k = 0; k < kDraftSelPer; ++k) {
@@ -184,12 +189,18 @@ draft_threshold_kernel(int B, int max_rows, int take, SelectWs ws) {
     key[k] = ~0ull;                              // empty slot: never selected
     if (f < slots) {
       const int bb = f / lim, r = f - bb * lim;
-      if (r < ws.n_el[bb]) key[k] = ws.cand[f];
+      const uint64_t c = ws.cand[f];             // in bounds; used only when r < n_el
+      if (r < ws.n_el[bb]) key[k] = c;
     }
   }
-  for (int i = tid; i < B; i += kSelThreads) s_kept[i] = 0;
-  int total = 0;
-  for (int i = 0; i < B; ++i) total += ws.n_el[i];
+  int nv = 0;
+#pragma unroll
+  for (int k = 0; k < kDraftSelPer; ++k) nv += key[k] != ~0ull;
+  nv = wave_sum(nv);
+  __syncthreads();                               // s_total cleared
+  if (lane == 0) atomicAdd(&s_total, nv);
+  __syncthreads();
+  const int total = s_total;
   uint64_t kth = ~0ull;                          // keep all
   if (take < total) {
     uint64_t prefix = 0;
@@ -203,17 +214,43 @@ draft_threshold_kernel(int B, int max_rows, int take, SelectWs ws) {
         if (key[k] != ~0ull && ((key[k] ^ prefix) & hi_mask) == 0)
           atomicAdd(&hist[(int)((key[k] >> shift) & 255)], 1);
       __syncthreads();
-      if (tid == 0) {
-        int need = s_need, dgt = 0;
-        for (; dgt < 256; ++dgt) {
-          if (need <= hist[dgt]) break;
-          need -= hist[dgt];
+      if (tid < 64) {
+        const int h0 = hist[4 * lane], h1 = hist[4 * lane + 1];
+        const int h2 = hist[4 * lane + 2], h3 = hist[4 * lane + 3];
+        const int sum = h0 + h1 + h2 + h3;
+        int incl = sum;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+          const int x = __shfl_up(incl, o, 64);
+          if (lane >= o) incl += x;
         }
-        s_digit = dgt;
-        s_need = need;
+        const int excl = incl - sum;
+        const int need = s_need;
+        if (excl < need && need <= incl) {       // exactly one lane
+          int n2 = need - excl, d = 4 * lane, hs = h0;
+          if (n2 > h0) {
+            n2 -= h0; ++d; hs = h1;
+            if (n2 > h1) {
+              n2 -= h1; ++d; hs = h2;
+              if (n2 > h2) { n2 -= h2; ++d; hs = h3; }
+            }
+          }
+          s_digit = d;
+          s_need = n2;
+          s_count = hs;
+        }
       }
       __syncthreads();
       prefix |= (uint64_t)s_digit << shift;
+      if (s_count == 1) {                        // one key left under this prefix
+        const uint64_t m = ~0ull << shift;
+#pragma unroll
+        for (int k = 0; k < kDraftSelPer; ++k)
+          if (key[k] != ~0ull && ((key[k] ^ prefix) & m) == 0) s_kth = key[k];
+        __syncthreads();
+        prefix = s_kth;
+        break;
+      }
     }
     kth = prefix;                                // the (take + 1)-th smallest key
   }

@@ -162,6 +162,26 @@ def _tree_for(cfg, rng, B):
     raise ValueError(kind)
 
 
+def prefix_lengths(name: str, **over) -> np.ndarray:
+    """The prefix lengths ``make(name, **over)`` draws, without building the
+    tensors (same seed, same order of draws)."""
+    cfg = dict(CONFIGS[name])
+    for k in ("seed", "step", "temperature"):
+        over.pop(k, None)
+    tag = over.pop("tag", 0)
+    cfg.update(over)
+    base = (1000 + cfg["index"], tag, tuple(sorted((k, repr(v)) for k, v in over.items())))
+    rng = np.random.default_rng(_seed(*base, "host"))
+    B = cfg["B"]
+    _tree_for(cfg, rng, B)
+    Lspec = cfg["L"]
+    if isinstance(Lspec, tuple):
+        return rng.integers(Lspec[1], Lspec[2], size=B, endpoint=True).astype(np.int32)
+    if isinstance(Lspec, (list, np.ndarray)):
+        return np.asarray(Lspec, dtype=np.int32)
+    return np.full(B, int(Lspec), dtype=np.int32)
+
+
 def make(name: str, device: str = "cpu", **over) -> Workload:
     """Build workload ``name`` (one of CONFIGS) on ``device``.
 
