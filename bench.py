@@ -228,15 +228,15 @@ def main():
     w = W.make(args.config, device="cuda", **over)
     vs = VerifyStep(w, acceptance=args.acceptance)
     a_attn, f_attn, a_acc = algorithmic(w, topk)
-    for _ in range(args.warmup):
-        vs.run()
-    torch.cuda.synchronize()
-
     names = ["mask", "append", "attention", "accept", "commit"]
     calls = [vs.build_mask, vs.append, vs.attention, vs.accept, vs.commit]
     if builder is not None:
         names = ["draft_build"] + names
         calls = [builder.run] + calls
+    for _ in range(args.warmup):
+        for fn in calls:
+            fn()
+    torch.cuda.synchronize()
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)]
           for _ in range(args.steps)]
     torch.cuda.synchronize()
