@@ -66,6 +66,7 @@ struct AttnArgs {
   int* unit_items;   // [units][max_ns]: item of each split of the unit
   int max_ns;
   int lpt;           // two-phase (longest-first) item order, see AttnPlan
+  int weighted;      // heavy units get shorter splits (attn_split_for)
   int64_t items_a;   // items of the first phase
   uint16_t order[kLptMax];
 };
@@ -74,8 +75,26 @@ struct AttnArgs {
 __host__ __device__ inline int attn_row_blocks(int n, int G, int rpb) {
   return (n * G + rpb - 1) / rpb;
 }
+// Splits of a request with `keys` keys: a last piece shorter than a quarter
+// split joins the one before it (a tiny workgroup pays its start-up and its
+// partial write for little work), unless that piece would exceed kMaxSplit.
+// The last split ends at `keys`; every other one is `split` long.
 __host__ __device__ inline int attn_splits(int keys, int split) {
-  return (keys + split - 1) / split;
+  int ns = (keys + split - 1) / split;
+  if (ns > 1 && keys - (ns - 1) * split < split / 4 && keys - (ns - 2) * split <= kMaxSplit) --ns;
+  return ns;
+}
+// Keys per split of a request with n tree rows.  With `weighted`, a unit
+// (KV head, row block) of more than kWaves / 2 row groups runs one wave per
+// group instead of two, and is compute-bound: per-item timing on the
+// batched dynamic trees gave ~32 keys/us for such units against ~48 for the
+// HBM-bound pair-mode units.  Its splits are 2/3 as long, so that every full
+// split takes about the same time.
+__host__ __device__ inline int attn_split_for(int split, int n, int G, int rpb, int weighted) {
+  const int rows = n * G < rpb ? n * G : rpb;
+  if (!weighted || (rows + kRowsPerWave - 1) / kRowsPerWave <= kWaves / 2) return split;
+  const int s2 = (split * 2 / 3) / kTileKeys * kTileKeys;
+  return s2 > kTileKeys ? s2 : kTileKeys;
 }
 
 // Workgroup index -> (request, KV head, row block, split).  Phase A: every
@@ -111,7 +130,7 @@ SPEC_DEVICE ItemLoc locate_item(int64_t x, const AttnArgs& a) {
       n = a.row_offsets[bq + 1] - o;
       L = a.prefix_len[bq];
       nrb = attn_row_blocks(n, a.G, rpb);
-      ns = attn_splits(L + n, a.split);
+      ns = attn_splits(L + n, attn_split_for(a.split, n, a.G, rpb, a.weighted));
       cnt = (int64_t)a.addr.hkv * nrb * (phase_a ? ns - tail : 1);
     }
     int64_t incl = cnt;
@@ -482,9 +501,10 @@ __global__ void __launch_bounds__(kWaves * 64, 1) attn_bf16_kernel(AttnArgs a) {
   const int n = __builtin_amdgcn_readfirstlane(loc.n);
   const int L = __builtin_amdgcn_readfirstlane(loc.L);
   const int total_keys = L + n;
-  const int ns = attn_splits(total_keys, a.split);
-  const int key_begin = __builtin_amdgcn_readfirstlane(s * a.split);
-  const int key_end = __builtin_amdgcn_readfirstlane(min(key_begin + a.split, total_keys));
+  const int split = attn_split_for(a.split, n, a.G, ROWS, a.weighted);
+  const int ns = attn_splits(total_keys, split);
+  const int key_begin = __builtin_amdgcn_readfirstlane(s * split);
+  const int key_end = __builtin_amdgcn_readfirstlane(s == ns - 1 ? total_keys : key_begin + split);
   const int M = n * a.G;
 
   if (a.max_ns > 1) {
@@ -896,7 +916,8 @@ AttnPlan plan_attention(int B, const int32_t* row_offsets_h, const int32_t* pref
   constexpr int64_t kCUs = 256;
   auto round_up = [](int64_t x) { return ((x + kTileKeys - 1) / kTileKeys) * kTileKeys; };
   int64_t split;
-  if (B > 0 && max_keys <= min_keys + min_keys / 8) {
+  const bool equal = B > 0 && max_keys <= min_keys + min_keys / 8;
+  if (equal) {
     const int64_t ns = std::max<int64_t>(1, (kCUs + units - 1) / std::max<int64_t>(units, 1));
     split = std::min<int64_t>(round_up((max_keys + ns - 1) / ns), kMaxSplit);
   } else {
@@ -910,17 +931,27 @@ AttnPlan plan_attention(int B, const int32_t* row_offsets_h, const int32_t* pref
   p.partial_items = 0;
   p.items_a = 0;
   p.lpt = 0;
+  p.weighted = 0;
   if (split > kMaxSplit) {          // a request longer than kMaxSplit * kMaxSplitsCombine keys
     p.split_keys = 0;
     p.items = -1;
     return p;
   }
   p.split_keys = (int)split;
+  // mixed lengths: heavy units split 2/3 as long, unless that would give a
+  // request more splits than the combine takes
+  p.weighted = equal ? 0 : 1;
+  for (int b = 0; b < B && p.weighted; ++b) {
+    const int n = row_offsets_h[b + 1] - row_offsets_h[b];
+    const int sp = attn_split_for(p.split_keys, n, G, p.rows_per_block, 1);
+    if (attn_splits(prefix_len_h[b] + n, sp) > kMaxSplitsCombine) p.weighted = 0;
+  }
   p.lpt = (B <= kLptMax) ? 1 : 0;
   p.max_ns = 1;
   for (int b = 0; b < B; ++b) {
     const int n = row_offsets_h[b + 1] - row_offsets_h[b];
-    const int ns = attn_splits(prefix_len_h[b] + n, p.split_keys);
+    const int ns = attn_splits(prefix_len_h[b] + n,
+                               attn_split_for(p.split_keys, n, G, p.rows_per_block, p.weighted));
     p.max_ns = std::max(p.max_ns, ns);
     const int64_t per = (int64_t)hkv * attn_row_blocks(n, G, p.rows_per_block);
     p.items += per * ns;
@@ -928,13 +959,17 @@ AttnPlan plan_attention(int B, const int32_t* row_offsets_h, const int32_t* pref
     if (ns > 1) p.partial_items += per * ns;
   }
   if (p.lpt) {
-    // second phase: requests by the length of their last split, longest
-    // first (ties by request index)
+    // second phase: requests by the estimated time of their last split,
+    // longest first (ties by request index): its keys, 1.5x for heavy units
+    // (see attn_split_for), plus ~200 keys' worth of start-up
     int64_t tail_len[kLptMax];
     for (int b = 0; b < B; ++b) {
-      const int keys = prefix_len_h[b] + row_offsets_h[b + 1] - row_offsets_h[b];
-      const int ns = attn_splits(keys, p.split_keys);
-      tail_len[b] = keys - (int64_t)(ns - 1) * p.split_keys;
+      const int n = row_offsets_h[b + 1] - row_offsets_h[b];
+      const int keys = prefix_len_h[b] + n;
+      const int sp = attn_split_for(p.split_keys, n, G, p.rows_per_block, p.weighted);
+      const int ns = attn_splits(keys, sp);
+      const int64_t len = keys - (int64_t)(ns - 1) * sp;
+      tail_len[b] = (sp < p.split_keys ? len * 3 / 2 : len) + 200;
       p.order[b] = (uint16_t)b;
     }
     std::stable_sort(p.order, p.order + B,
@@ -976,6 +1011,7 @@ hipError_t launch_attention_bf16(const LaunchCtx& cx, const AttnPlan& plan, cons
   a.unit_items = a.unit_desc + (size_t)plan.units * 8;
   a.max_ns = plan.max_ns;
   a.lpt = plan.lpt;
+  a.weighted = plan.weighted;
   a.items_a = plan.items_a;
   if (plan.lpt) std::copy(plan.order, plan.order + cx.B, a.order);
   if (plan.items <= 0 || plan.items > 0x7fffffff) return hipErrorInvalidValue;

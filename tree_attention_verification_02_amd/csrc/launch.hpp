@@ -36,6 +36,7 @@ struct AttnPlan {
   int64_t units;        // (request, KV head, row block) triples
   int max_ns;           // most splits of any request
   int lpt;              // two-phase order in use
+  int weighted;         // heavy units get 2/3-length splits (mixed-length batches)
   int64_t items_a;      // workgroups of the first phase
   uint16_t order[kLptMax];  // second phase: requests, longest last split first
 };
