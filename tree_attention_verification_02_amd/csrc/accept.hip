@@ -139,12 +139,12 @@ constexpr double kInvLn2x256 = 0x1.71547652b82fep+8;
 constexpr double kLn2by256Hi = 0x1.62e42ff000000p-9;
 constexpr double kLn2by256Lo = -0x1.718432a1b0e26p-43;
 
-SPEC_DEVICE double exp_f64(double x, const double* tab) {
-  // Results below e^-708 (about 3e-308) are flushed to zero.  k is rounded
-  // with a 1.5 * 2^52 shifter so that its value sits in the low word, and
-  // the power of two is assembled from the exponent bits: only full-rate
-  // fp64 operations (fma/add/mul) are used.
-  if (!(x >= -708.0)) return 0.0;
+// exp(x) for x <= 709 in fp64 with only full-rate fp64 operations: k =
+// round(x * 256 / ln 2) with a 1.5 * 2^52 shifter (its value lands in the low
+// word), r = x - k ln2 / 256 in two parts, e^r - 1 by a degree-4 Taylor
+// polynomial, times 2^(k mod 256 / 256) from the table, times 2^(k div 256)
+// by ldexp (exact: the results stay normal).
+SPEC_DEVICE double exp_f64_stream(double x, const double* tab) {
   constexpr double kShift = 0x1.8p52;
   const double t = fma(x, kInvLn2x256, kShift);
   const double k = t - kShift;
@@ -152,41 +152,17 @@ SPEC_DEVICE double exp_f64(double x, const double* tab) {
   const double r = fma(-k, kLn2by256Lo, fma(-k, kLn2by256Hi, x));
   const double p = r * fma(r, fma(r, fma(r, 1.0 / 24, 1.0 / 6), 0.5), 1.0);
   const double s = tab[ki & 255];
-  const double scale = __longlong_as_double((long long)((ki >> 8) + 1023) << 52);
-  return fma(s, p, s) * scale;
+  return ldexp(fma(s, p, s), ki >> 8);
 }
-// The same value for -708 <= x <= 709 only, without the range handling.
-SPEC_DEVICE double exp_f64_raw(double x, const double* tab) {
-  constexpr double kShift = 0x1.8p52;
-  const double t = fma(x, kInvLn2x256, kShift);
-  const double k = t - kShift;
-  const int ki = (int)(uint32_t)__double_as_longlong(t);
-  const double r = fma(-k, kLn2by256Lo, fma(-k, kLn2by256Hi, x));
-  const double p = r * fma(r, fma(r, fma(r, 1.0 / 24, 1.0 / 6), 0.5), 1.0);
-  const double s = tab[ki & 255];
-  const double scale = __longlong_as_double((long long)((ki >> 8) + 1023) << 52);
-  return fma(s, p, s) * scale;
+// Results below e^-708 (about 3e-308) are flushed to zero.
+SPEC_DEVICE double exp_f64(double x, const double* tab) {
+  return (x >= -708.0) ? exp_f64_stream(x, tab) : 0.0;
 }
 // Streaming sums: arguments below -708 give e^-708 (about 3e-308) instead of
 // a smaller value or 0 -- invisible in any sum of weights whose total is a
 // probability mass (the draws rescan their segment with exp_f64).
 SPEC_DEVICE double exp_f64_clamped(double x, const double* tab) {
-  return exp_f64_raw(fmax(x, -708.0), tab);
-}
-// The same value as exp_f64 without a branch (for unrolled streaming loops).
-SPEC_DEVICE double exp_f64_flat(double x, const double* tab) {
-  const bool under = !(x >= -708.0);
-  x = under ? -708.0 : x;
-  constexpr double kShift = 0x1.8p52;
-  const double t = fma(x, kInvLn2x256, kShift);
-  const double k = t - kShift;
-  const int ki = (int)(uint32_t)__double_as_longlong(t);
-  const double r = fma(-k, kLn2by256Lo, fma(-k, kLn2by256Hi, x));
-  const double p = r * fma(r, fma(r, fma(r, 1.0 / 24, 1.0 / 6), 0.5), 1.0);
-  const double s = tab[ki & 255];
-  const double scale = __longlong_as_double((long long)((ki >> 8) + 1023) << 52);
-  const double e = fma(s, p, s) * scale;
-  return under ? 0.0 : e;
+  return exp_f64_stream(fmax(x, -708.0), tab);
 }
 SPEC_DEVICE void load_exp_table(double* s_tab) {
   for (int i = threadIdx.x; i < 256; i += blockDim.x) s_tab[i] = kExp2Frac[i];
@@ -320,16 +296,19 @@ accept_stats_kernel(const int32_t* __restrict__ row_offsets, int B, int R,
   const int v4 = (vocab + 3) >> 2;
   const int f_begin = chunk * (kStatThreads * kStatF4);
   // the whole chunk in flight: clamped (in-bounds) loads, masked to -inf
+  // (only the row's last chunk can reach past it)
   float4 x[kStatF4];
 #pragma unroll
   for (int k = 0; k < kStatF4; ++k) x[k] = row4[min(f_begin + k * kStatThreads + tid, v4 - 1)];
+  if ((chunk + 1) * kStatChunkLen > vocab) {
 #pragma unroll
-  for (int k = 0; k < kStatF4; ++k) {
-    const int y0 = (f_begin + k * kStatThreads + tid) * 4;
-    if (y0 + 0 >= vocab) x[k].x = -INFINITY;
-    if (y0 + 1 >= vocab) x[k].y = -INFINITY;
-    if (y0 + 2 >= vocab) x[k].z = -INFINITY;
-    if (y0 + 3 >= vocab) x[k].w = -INFINITY;
+    for (int k = 0; k < kStatF4; ++k) {
+      const int y0 = (f_begin + k * kStatThreads + tid) * 4;
+      if (y0 + 0 >= vocab) x[k].x = -INFINITY;
+      if (y0 + 1 >= vocab) x[k].y = -INFINITY;
+      if (y0 + 2 >= vocab) x[k].z = -INFINITY;
+      if (y0 + 3 >= vocab) x[k].w = -INFINITY;
+    }
   }
   if (kGreedy) {
     float m = -INFINITY;
@@ -465,15 +444,6 @@ SPEC_DEVICE double walk_weight(float py, float qy, double invT, double lse_p, do
   const double P = exp_f64((double)py * invT - lse_p, tab);
   if (!need_q) return P;
   const double Q = exp_f64((double)qy * invT - lse_q, tab);
-  return fmax(0.0, fma(-t, Q, P));
-}
-
-// The same weight with the branch-free exponential (streaming passes).
-SPEC_DEVICE double walk_weight_flat(float py, float qy, double invT, double lse_p, double lse_q,
-                                    double t, bool need_q, const double* tab) {
-  const double P = exp_f64_flat((double)py * invT - lse_p, tab);
-  if (!need_q) return P;
-  const double Q = exp_f64_flat((double)qy * invT - lse_q, tab);
   return fmax(0.0, fma(-t, Q, P));
 }
 
