@@ -66,6 +66,8 @@ struct AttnArgs {
   int* unit_items;   // [units][max_ns]: item of each split of the unit
   int max_ns;
   int lpt;           // two-phase (longest-first) item order, see AttnPlan
+  unsigned* ticket;  // workgroups take items in start order (null: blockIdx)
+  int items;
   int weighted;      // heavy units get shorter splits (attn_split_for)
   int64_t items_a;   // items of the first phase
   uint16_t order[kLptMax];
@@ -492,7 +494,25 @@ __global__ void __launch_bounds__(kWaves * 64, 1) attn_bf16_kernel(AttnArgs a) {
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-  const int64_t item = blockIdx.x;
+  // Items in the order workgroups start, across all XCDs: the dispatcher
+  // deals workgroups to the XCDs round-robin, and the XCDs stream at
+  // different rates, so a fixed blockIdx -> item map leaves the slow XCDs
+  // finishing last.  atomicInc wraps at items - 1, so every item is taken
+  // exactly once whatever the counter held (the combine resets it to 0 for
+  // the next call, and only a first call on a fresh workspace starts the
+  // longest-first order elsewhere); an out-of-range start value is returned
+  // once and replaced by 0.
+  __shared__ int s_item;
+  int64_t item = blockIdx.x;
+  if (a.ticket) {
+    if (tid == 0) {
+      unsigned t = atomicInc(a.ticket, (unsigned)(a.items - 1));
+      if (t >= (unsigned)a.items) t = atomicInc(a.ticket, (unsigned)(a.items - 1));
+      s_item = (int)t;
+    }
+    __syncthreads();
+    item = s_item;
+  }
   const ItemLoc loc = locate_item(item, a);
   const int b = loc.b;
   if (b < 0) return;
@@ -739,6 +759,7 @@ __global__ void __launch_bounds__(256) attn_combine_kernel(AttnArgs a) {
   const int4 d0 = *reinterpret_cast<const int4*>(a.unit_desc + unit * 8);
   const int2 d1 = *reinterpret_cast<const int2*>(a.unit_desc + unit * 8 + 4);
   const int kvh = d0.y, rb = d0.z, ns = d0.w, o = d1.x, m_blk = d1.y;
+  if (blockIdx.x == 0 && threadIdx.x == 0 && a.ticket) *a.ticket = 0u;   // for the next call
   if (ns == 1) return;
   const int r0 = chunk * kCombineRows;             // first row (within the block)
   const int rows = min(kCombineRows, m_blk - r0);
@@ -1009,6 +1030,13 @@ hipError_t launch_attention_bf16(const LaunchCtx& cx, const AttnPlan& plan, cons
   a.part_ml = a.part + (size_t)plan.items * plan.rows_per_block * addr.d;
   a.unit_desc = (int*)(a.part_ml + (size_t)plan.items * plan.rows_per_block * 2);
   a.unit_items = a.unit_desc + (size_t)plan.units * 8;
+  // the ticket counter follows unit_items (inside the workspace's last 256
+  // bytes).  Only mixed-length batches use it (several items per CU); plans
+  // without partials have no combine to reset it: blockIdx.
+  a.ticket = (plan.partial_items && plan.weighted)
+                 ? (unsigned*)(a.unit_items + (size_t)plan.units * plan.max_ns)
+                 : nullptr;
+  a.items = (int)plan.items;
   a.max_ns = plan.max_ns;
   a.lpt = plan.lpt;
   a.weighted = plan.weighted;
