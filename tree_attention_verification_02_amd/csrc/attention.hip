@@ -930,10 +930,11 @@ AttnPlan plan_attention(int B, const int32_t* row_offsets_h, const int32_t* pref
   }
   // One workgroup per CU at a time (256 CUs).  Requests of (nearly) equal
   // length: the fewest splits that give every CU one workgroup (each split
-  // costs a partial-result round trip).  Otherwise ~3 workgroups per CU, so
-  // that longest-first dispatch evens out the mixed lengths (measured on
-  // the batched dynamic trees: 3 per CU beat 2.5, 3.5, 4, 5 and 8).  Splits are at
-  // least 256 keys and at most kMaxSplitsCombine per request.
+  // costs a partial-result round trip).  Otherwise ~2.5 workgroups per CU,
+  // so that longest-first dispatch evens out the mixed lengths (measured on
+  // the batched dynamic trees with start-order dispatch: 2.5 per CU beat
+  // 1.5, 2, 3, 3.5, 4 and 5).  Splits are at least 256 keys and at most
+  // kMaxSplitsCombine per request.
   constexpr int64_t kCUs = 256;
   auto round_up = [](int64_t x) { return ((x + kTileKeys - 1) / kTileKeys) * kTileKeys; };
   int64_t split;
@@ -942,7 +943,7 @@ AttnPlan plan_attention(int B, const int32_t* row_offsets_h, const int32_t* pref
     const int64_t ns = std::max<int64_t>(1, (kCUs + units - 1) / std::max<int64_t>(units, 1));
     split = std::min<int64_t>(round_up((max_keys + ns - 1) / ns), kMaxSplit);
   } else {
-    const int64_t target = 3 * kCUs;
+    const int64_t target = 5 * kCUs / 2;
     split = std::min<int64_t>(round_up((work + target - 1) / target), kMaxSplit);
   }
   split = std::max<int64_t>(split, round_up((max_keys + kMaxSplitsCombine - 1) / kMaxSplitsCombine));
