@@ -369,17 +369,34 @@ accept_stats_kernel(const int32_t* __restrict__ row_offsets, int B, int R,
 }
 
 // Per-row results from the chunk partials, merged in chunk order (so every
-// run gives the same bits): (reference, sum) of a row (its log-sum-exp is
-// ref + log(sum); the sampling walk merges its own rows), or the target
-// argmax.  accept_finalize (greedy): one thread per row writes the argmax
-// and, per child, 1 if its token is the parent's argmax.
-SPEC_DEVICE void merged_ref_sum(const AcceptWs& ws, int rr, const double* tab, double& ref,
-                                double& s) {
+// run gives the same bits): a row's log-sum-exp (the sampling walk merges its
+// own rows; the partials are loaded 8 at a time, all in flight together), or
+// the target argmax.  accept_finalize (greedy): one thread per row writes the
+// argmax and, per child, 1 if its token is the parent's argmax.
+SPEC_DEVICE void merged_ref_sum(const AcceptWs& ws, int rr, const double* tab, double& lse) {
   const int nch = ws.nch;
-  ref = ws.part_ref[rr * nch];
-  s = ws.part_s[rr * nch];
-  for (int c = 1; c < nch; ++c)
-    merge_ref(ref, s, ws.part_ref[rr * nch + c], ws.part_s[rr * nch + c], tab);
+  const double* pr = ws.part_ref + (int64_t)rr * nch;
+  const double* ps = ws.part_s + (int64_t)rr * nch;
+  double ref = 0.0, s = 0.0;
+  for (int c0 = 0; c0 < nch; c0 += 8) {
+    double r8[8], s8[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      r8[j] = (c0 + j < nch) ? pr[c0 + j] : 0.0;
+      s8[j] = (c0 + j < nch) ? ps[c0 + j] : 0.0;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (c0 + j >= nch) break;
+      if (c0 + j == 0) {
+        ref = r8[0];
+        s = s8[0];
+      } else {
+        merge_ref(ref, s, r8[j], s8[j], tab);
+      }
+    }
+  }
+  lse = ref + log(s);
 }
 SPEC_DEVICE int merged_argmax(const AcceptWs& ws, int r) {
   const int nch = ws.nch;
@@ -413,7 +430,7 @@ accept_finalize_kernel(const int32_t* __restrict__ row_offsets, int B, int R,
 // Walk.
 
 struct WalkShared {
-  int par[kMaxRows];
+  alignas(16) int par[kMaxRows];   // read as int4 by load_tree
   int tok[kMaxRows];
   int kid_start[kMaxRows + 1];
   int kid_list[kMaxRows];
@@ -708,35 +725,76 @@ SPEC_DEVICE int walk_draw(WalkShared& sh, const WalkCtx& c, int pass, double t, 
   return res;
 }
 
+// The request's tree into LDS (and, with `tab`, the exponential table in the
+// same memory round trip): parents, tokens, validity, children lists.
+// Needs blockDim.x >= max(n, 256).
 SPEC_DEVICE void load_tree(WalkShared& sh, const int32_t* parents, const int32_t* tokens, int o,
-                           int n) {
-  const int tid = threadIdx.x;
+                           int n, double* tab = nullptr) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  int p = -1, tk = 0;
+  if (tid < n) {
+    p = parents[o + tid];
+    tk = tokens[o + tid];
+  }
+  if (tab && tid < 256) tab[tid] = kExp2Frac[tid];
+  const bool ok = tid >= n || ((tid == 0) ? (p == -1) : (p >= 0 && p < tid));
+  if (tid < n) {
+    sh.par[tid] = p;
+    sh.tok[tid] = tk;
+  }
+  if (__syncthreads_or(!ok)) {
+    if (tid == 0) sh.bad = 1;
+    __syncthreads();
+    return;
+  }
   if (tid == 0) sh.bad = 0;
+  // children of row tid: rows j > tid with par[j] == tid, read 4 at a time
+  // (par is padded with -1 to a multiple of 4)
+  if (tid < ((n + 3) & ~3) && tid >= n) sh.par[tid] = -1;
   __syncthreads();
-  for (int i = tid; i < n; i += blockDim.x) {
-    const int p = parents[o + i];
-    sh.par[i] = p;
-    sh.tok[i] = tokens[o + i];
-    const bool ok = (i == 0) ? (p == -1) : (p >= 0 && p < i);
-    if (!ok) sh.bad = 1;
-  }
-  __syncthreads();
-  if (sh.bad) return;
-  for (int i = tid; i < n; i += blockDim.x) {
+  const int4* par4 = reinterpret_cast<const int4*>(sh.par);
+  if (tid < n) {
     int cnt = 0;
-    for (int j = i + 1; j < n; ++j) cnt += (sh.par[j] == i);
-    sh.kid_start[i + 1] = cnt;
+    for (int j4 = (tid + 1) >> 2; j4 < (n + 3) >> 2; ++j4) {
+      const int4 q = par4[j4];
+      cnt += (q.x == tid) + (q.y == tid) + (q.z == tid) + (q.w == tid);
+    }
+    sh.kid_start[tid + 1] = cnt;
   }
   __syncthreads();
-  if (tid == 0) {
-    sh.kid_start[0] = 0;
-    for (int i = 1; i <= n; ++i) sh.kid_start[i] += sh.kid_start[i - 1];
+  if (tid < 64) {                       // inclusive prefix of the counts, 4 per lane
+    int v[4], t = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int i = 1 + 4 * lane + j;
+      v[j] = (i <= n) ? sh.kid_start[i] : 0;
+      t += v[j];
+    }
+    int incl = t;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int x = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += x;
+    }
+    int run = incl - t;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int i = 1 + 4 * lane + j;
+      run += v[j];
+      if (i <= n) sh.kid_start[i] = run;
+    }
+    if (lane == 0) sh.kid_start[0] = 0;
   }
   __syncthreads();
-  for (int i = tid; i < n; i += blockDim.x) {
-    int pos = sh.kid_start[i];
-    for (int j = i + 1; j < n; ++j)
-      if (sh.par[j] == i) sh.kid_list[pos++] = j;
+  if (tid < n) {
+    int pos = sh.kid_start[tid];
+    for (int j4 = (tid + 1) >> 2; j4 < (n + 3) >> 2; ++j4) {
+      const int4 q = par4[j4];
+      if (q.x == tid) sh.kid_list[pos++] = 4 * j4;
+      if (q.y == tid) sh.kid_list[pos++] = 4 * j4 + 1;
+      if (q.z == tid) sh.kid_list[pos++] = 4 * j4 + 2;
+      if (q.w == tid) sh.kid_list[pos++] = 4 * j4 + 3;
+    }
   }
   __syncthreads();
 }
@@ -895,37 +953,49 @@ accept_walk_kernel(const int32_t* __restrict__ row_offsets, int R, int S,
   const int o = row_offsets[b];
   const int n = row_offsets[b + 1] - o;
   const int tid = threadIdx.x;
-  load_exp_table(sh.tab);
   if (tid == 0) sh.timeout = 0;
-  load_tree(sh, parents, tokens, o, n);
+  load_tree(sh, parents, tokens, o, n, sh.tab);
   // This request's row statistics: each row's log-sum-exp from its chunk
   // partials (in chunk order), then each child's P_u(x_c), Q_u(x_c) in fp64.
   // Every slice computes them; slice 0 writes the fp32 outputs (NaN at roots
   // and at rows whose parent is invalid; Q is NaN everywhere without draft
-  // rows).
+  // rows).  Thread k takes row k's partials and child k's logit; all of
+  // them are loaded at once (one memory round trip), the child logits are
+  // held in registers until the parents' log-sum-exps are in LDS.
   const bool topk = q_logits == nullptr;
   const double invT = 1.0 / (double)temperature;
-  for (int k = tid; k < (topk ? n : 2 * n); k += blockDim.x) {
+  constexpr int kRowsPerThread = 2 * kMaxRows / kWalkThreads;
+  float clog[kRowsPerThread];
+  bool cval[kRowsPerThread];
+#pragma unroll
+  for (int j = 0; j < kRowsPerThread; ++j) {
+    const int k = tid + j * kWalkThreads;
     const int which = k >= n ? 1 : 0;
     const int i = k - which * n;
-    double ref, s;
-    merged_ref_sum(ws, which * R + o + i, sh.tab, ref, s);
-    sh.lse[which][i] = ref + log(s);
+    cval[j] = false;
+    clog[j] = 0.0f;
+    if (k < 2 * n && !(which && topk)) {
+      const int pu = sh.par[i];
+      const int x = sh.tok[i];
+      if (i > 0 && pu >= 0 && pu < i && x >= 0 && x < vocab) {
+        cval[j] = true;
+        clog[j] = ((which ? q_logits : p_logits) + (int64_t)(o + pu) * ld)[x];
+      }
+      merged_ref_sum(ws, which * R + o + i, sh.tab, sh.lse[which][i]);
+    }
   }
   __syncthreads();
-  for (int k = tid; k < 2 * n; k += blockDim.x) {
+#pragma unroll
+  for (int j = 0; j < kRowsPerThread; ++j) {
+    const int k = tid + j * kWalkThreads;
+    if (k >= 2 * n) continue;
     const int which = k >= n ? 1 : 0;
     const int i = k - which * n;
     float* dst = which ? out.child_q : out.child_p;
     const int pu = sh.par[i];
     double val = __longlong_as_double(0x7ff8000000000000LL);
     if (i > 0 && pu >= 0 && pu < i && !(which && topk)) {
-      const int x = sh.tok[i];
-      val = 0.0;
-      if (x >= 0 && x < vocab) {
-        const float* prow = (which ? q_logits : p_logits) + (int64_t)(o + pu) * ld;
-        val = exp_f64((double)prow[x] * invT - sh.lse[which][pu], sh.tab);
-      }
+      val = cval[j] ? exp_f64((double)clog[j] * invT - sh.lse[which][pu], sh.tab) : 0.0;
       (which ? sh.cq : sh.cp)[i] = val;
     }
     if (dst && slice == 0) dst[o + i] = (float)val;
@@ -1100,6 +1170,7 @@ hipError_t launch_accept(const LaunchCtx& cx, int R, const int32_t* parents, con
                          uint8_t* accept_mask, float* child_p, float* child_q, int32_t* flags,
                          void* workspace, int slices_override) {
   static_assert(sizeof(WalkShared) < 20480, "walk LDS");
+  static_assert(kWalkThreads >= kMaxRows && kWalkThreads >= 256, "load_tree: a thread per row and table entry");
   const int nseg = segs_for(vocab);
   AcceptWs ws = accept_ws(workspace, R, cx.B, vocab);
   const int nch = ws.nch;
