@@ -88,33 +88,44 @@ kv_commit_kernel(const int32_t* __restrict__ row_offsets, const int32_t* __restr
                  const int32_t* __restrict__ path, int path_stride, char* __restrict__ k_cache,
                  char* __restrict__ v_cache, int32_t* __restrict__ new_len,
                  int32_t* __restrict__ freed) {
+  static_assert(kMaxRows <= 256, "one thread per path entry");
   const int b = blockIdx.x / addr.hkv;
   const int h = blockIdx.x % addr.hkv;
+  const int tid = threadIdx.x;
+  __shared__ int pth[kMaxRows];
+  // one memory round trip: the request's bounds, accept_len and its path row
   const int o = row_offsets[b];
   const int n = row_offsets[b + 1] - o;
   const int L = prefix_len[b];
-  __shared__ int ok;
-  __shared__ int pth[kMaxRows];
   const int a = accept_len[b];
-  // the path row is read together with accept_len (one memory round trip)
-  for (int k = threadIdx.x; k < path_stride && k < kMaxRows; k += blockDim.x)
-    pth[k] = path[(int64_t)b * path_stride + k];
-  if (threadIdx.x == 0) ok = (a >= 0 && a < n && a < path_stride) ? 1 : 0;
+  const int lim = min(path_stride, kMaxRows);
+  const int pk = (tid < lim) ? path[(int64_t)b * path_stride + tid] : -1;
+  if (tid < lim) pth[tid] = pk;
   __syncthreads();
-  if (!ok) {
-    if (h == 0 && threadIdx.x == 0) new_len[b] = -1;
+  // the path must start at the root and increase strictly within the tree
+  const bool a_ok = a >= 0 && a < n && a < path_stride;
+  bool bad = !a_ok;
+  if (a_ok && tid <= a) bad = (tid == 0) ? (pk != 0) : !(pk > pth[tid - 1] && pk < n);
+  if (__syncthreads_or(bad)) {
+    if (h == 0 && tid == 0) new_len[b] = -1;
     return;
   }
-  if (threadIdx.x == 0) {
-    int good = (pth[0] == 0);
-    for (int k = 1; k <= a; ++k) good &= (pth[k] > pth[k - 1] && pth[k] < n);
-    ok = good;
+  const int nl = L + a + 1;
+  if (h == 0) {
+    if (tid == 0) new_len[b] = nl;
+    if (freed && addr.paged) {
+      const int first = (nl + kBlock - 1) / kBlock;
+      const int end = (L + n + kBlock - 1) / kBlock;
+      for (int j = tid; j < addr.mbps; j += blockDim.x) {
+        const int src = first + j;
+        freed[(int64_t)b * addr.mbps + j] =
+            (src < end) ? addr.block_table[(int64_t)b * addr.mbps + src] : -1;
+      }
+    }
   }
-  __syncthreads();
-  if (!ok) {
-    if (h == 0 && threadIdx.x == 0) new_len[b] = -1;
-    return;
-  }
+  // rows already in place (path[k] == k, e.g. an accepted first child) are
+  // neither read nor written
+  if (!__syncthreads_or(tid >= 1 && tid <= a && pk != tid)) return;
   const int chunks = addr.d * esize / 16;
   for (int k0 = 1; k0 <= a; k0 += kCommitRows) {
     const int rows = min(kCommitRows, a + 1 - k0);
@@ -123,20 +134,22 @@ kv_commit_kernel(const int32_t* __restrict__ row_offsets, const int32_t* __restr
     uint4 buf[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const int it = threadIdx.x + q * 256;
+      const int it = tid + q * 256;
       if (it < items) {
         const int isv = it / (rows * chunks);
         const int rem = it % (rows * chunks);
         const int k = k0 + rem / chunks;
         const int c = rem % chunks;
-        const int64_t src = addr(b, h, L + pth[k]) * esize + (int64_t)c * 16;
-        buf[q] = *reinterpret_cast<const uint4*>((isv ? v_cache : k_cache) + src);
+        if (pth[k] != k) {
+          const int64_t src = addr(b, h, L + pth[k]) * esize + (int64_t)c * 16;
+          buf[q] = *reinterpret_cast<const uint4*>((isv ? v_cache : k_cache) + src);
+        }
       }
     }
     __syncthreads();
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const int it = threadIdx.x + q * 256;
+      const int it = tid + q * 256;
       if (it < items) {
         const int isv = it / (rows * chunks);
         const int rem = it % (rows * chunks);
@@ -149,19 +162,6 @@ kv_commit_kernel(const int32_t* __restrict__ row_offsets, const int32_t* __restr
       }
     }
     __syncthreads();
-  }
-  if (h == 0) {
-    const int nl = L + a + 1;
-    if (threadIdx.x == 0) new_len[b] = nl;
-    if (freed && addr.paged) {
-      const int first = (nl + kBlock - 1) / kBlock;
-      const int end = (L + n + kBlock - 1) / kBlock;
-      for (int j = threadIdx.x; j < addr.mbps; j += blockDim.x) {
-        const int src = first + j;
-        freed[(int64_t)b * addr.mbps + j] =
-            (src < end) ? addr.block_table[(int64_t)b * addr.mbps + src] : -1;
-      }
-    }
   }
 }
 
