@@ -17,11 +17,11 @@
 // Kernels:
 //  * accept_stats: one workgroup per (row, {target, draft}, 16K-logit chunk)
 //    streams its chunk once (16-byte loads) into fp64 partial sums (or the
-//    first argmax); accept_finalize merges them into each row's log-sum-exp
-//    of logits/T and the child probabilities P_u(x_c), Q_u(x_c).  Draft rows
-//    of leaves are never read.
+//    first argmax).  Draft rows of leaves are never read.  At temperature 0,
+//    accept_finalize merges the argmax partials per row.
 //  * accept_walk: S workgroups ("slices", taken by ticket in start order) per
-//    request.  Each pass is split over the S slices by 1024-element
+//    request; each merges its request's partials into the rows' log-sum-exps
+//    of logits/T and the child probabilities P_u(x_c), Q_u(x_c) itself.  Each pass is split over the S slices by 1024-element
 //    segments; segment sums go to global memory and the S slices meet at a
 //    per-request counter barrier (bounded spin).  Every slice then sums the
 //    segments in the same order and replays the same scalar decisions, so no
