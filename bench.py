@@ -200,6 +200,8 @@ def main():
                          "row offsets back to the host) before the verify calls")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-copy-probe", action="store_true",
+                    help="skip the device-copy bandwidth probe printed as context")
     ap.add_argument("--calib-copy-gib", type=float, default=0.0,
                     help="also run one device copy of this many GiB (counter calibration)")
     args = ap.parse_args()
@@ -255,6 +257,22 @@ def main():
     per = {n: v / args.steps for n, v in per.items()}      # ms per call
     gpu_ms = sum(per.values())
 
+    # context: a plain device copy (read + write) on the same GPU
+    copy_gbs = None
+    if not args.no_copy_probe:
+        n = (1 << 30) // 4
+        src = torch.empty(n, dtype=torch.float32, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(5):
+            dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        copy_gbs = 5 * 2 * n * 4 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+        del src, dst
+
     if args.calib_copy_gib > 0:
         n = int(args.calib_copy_gib * (1 << 30)) // 4
         src = torch.empty(n, dtype=torch.float32, device="cuda").fill_(1.0)
@@ -294,10 +312,12 @@ def main():
                      "mfma_tflops": f_attn / t_attn / 1e12,
                      "mfma_frac": f_attn / t_attn / 1e12 / BF16_PEAK_TFLOPS},
         "attn_plus_accept": {"bytes": a_attn + a_acc, "ms": per["attention"] + per["accept"],
+                             "tree_tokens_per_s": R / (t_attn + t_acc),
                              "gbs": (a_attn + a_acc) / (t_attn + t_acc) / 1e9,
                              "hbm_frac": (a_attn + a_acc) / (t_attn + t_acc) / 1e9 / HBM_PEAK_GBS,
                              "accept_gbs": a_acc / t_acc / 1e9},
         "per_call_ms": per,
+        "stream_copy_gbs": copy_gbs,
         "gpu_ms_per_step": gpu_ms,
         "mean_accepted_drafts": float(vs.acc.accept_len.float().mean()),
     }
