@@ -81,11 +81,66 @@ def test_walk_slices(lib, slices, monkeypatch):
 
 
 @pytest.mark.parametrize("case,T,seed,step", [("dynamic-small", 0.7, 5, 3),
-                                              ("medusa-small", 1.6, 1, 9)])
+                                              ("medusa-small", 1.6, 1, 9),
+                                              ("specinfer-small", 0.05, 3, 1),
+                                              ("chain8-small", 4.0, 2, 2)])
 def test_small_other_temperatures(lib, case, T, seed, step):
     w = make(BASE[case], **SMALL[case])
     vs = run_step(w, temperature=T, seed=seed, step=step)
     check_accept(w, vs, T, seed, step)
+
+
+@pytest.mark.parametrize("mode", ["sample", "topk", "greedy"])
+def test_ragged_vocab_with_padded_rows(lib, mode):
+    """vocab = 4001 inside rows of 4004 floats whose padding holds NaN: the
+    last float4 of every row is partly outside the vocabulary and must be
+    masked, never read as a logit.  Checked against the oracle on the
+    unpadded rows."""
+    import tree_attention_verification_02_amd._lib as L
+    from oracle import accept as OA
+    V, LD = 4001, 4004
+    w = make("dynamic", B=5, L=64, V=V, Hq=4, Hkv=1,
+             **({"draft": "topk"} if mode == "topk" else {}))
+    dev = "cuda"
+    R = w.R
+    pl = torch.full((R, LD), float("nan"), dtype=torch.float32, device=dev)
+    ql = torch.full((R, LD), float("nan"), dtype=torch.float32, device=dev)
+    pl[:, :V] = w.p_logits
+    ql[:, :V] = torch.nan_to_num(w.q_logits, nan=0.0)
+    batch = L.Batch(w.row_offsets, w.prefix_len, dev)
+    S = batch.c.max_rows
+    out = L.AcceptOut(torch.empty(w.B, dtype=torch.int32, device=dev),
+                      torch.empty((w.B, S), dtype=torch.int32, device=dev),
+                      torch.empty((w.B, S), dtype=torch.int32, device=dev),
+                      child_p=torch.empty(R, dtype=torch.float32, device=dev),
+                      flags=torch.empty(w.B, dtype=torch.int32, device=dev))
+    ws = torch.empty(L.spec_accept_workspace_bytes(batch, V), dtype=torch.uint8, device=dev)
+    par = torch.from_numpy(w.parents.astype(np.int32)).to(dev)
+    tok = torch.from_numpy(w.tokens.astype(np.int32)).to(dev)
+    T = 0.0 if mode == "greedy" else 1.0
+    if mode == "topk":
+        L.spec_accept_topk(batch, par, tok, pl, V, T, 4, 0, out, ws, logits_ld=LD)
+    else:
+        L.spec_accept_sample(batch, par, tok, pl, ql if T > 0 else None, V, T, 4, 0, out, ws,
+                             logits_ld=LD)
+    torch.cuda.synchronize()
+    alen = out.accept_len.cpu().numpy()
+    toks = out.tokens.cpu().numpy()
+    cp = out.child_p.cpu().numpy()
+    assert np.isfinite(cp[np.asarray(w.parents) >= 0]).all()
+    for b in range(w.B):
+        o, e = request_slice(w, b)
+        p64 = w.p_logits[o:e].double().cpu().numpy()
+        q64 = torch.nan_to_num(w.q_logits[o:e], nan=0.0).double().cpu().numpy()
+        if mode == "topk":
+            r = OA.accept_request_topk(w.parents[o:e], w.tokens[o:e], p64, T, 4, 0, b)
+        else:
+            r = OA.accept_request(w.parents[o:e], w.tokens[o:e], p64, q64 if T > 0 else None, T,
+                                  4, 0, b)
+        if r["result"].first_flag() is not None:
+            continue
+        assert alen[b] == r["accept_len"], b
+        assert list(toks[b, :len(r["tokens"])]) == r["tokens"], b
 
 
 def test_fp32_output_of_bf16_path(lib):
