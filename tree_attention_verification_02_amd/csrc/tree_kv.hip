@@ -51,12 +51,25 @@ build_mask_kernel(const int32_t* __restrict__ row_offsets, const int32_t* __rest
   if (i == 0) err_row[b] = (bad == 0x7fffffff) ? -1 : bad;
 }
 
+// Batches up to this many requests keep their row offsets in LDS.
+constexpr int kAppendLdsRows = 4096;
+
 // One thread per 16-byte chunk of a new K or V row.
 __global__ void __launch_bounds__(256)
 kv_append_kernel(const int32_t* __restrict__ row_offsets, const int32_t* __restrict__ prefix_len,
                  int B, int R, KvAddr addr, int esize, const uint4* __restrict__ k_new,
                  const uint4* __restrict__ v_new, char* __restrict__ k_cache,
                  char* __restrict__ v_cache) {
+  // the row offsets go to LDS first (one load round trip), so that finding
+  // each row's request is a search in LDS rather than a chain of dependent
+  // global loads; larger batches search in global memory
+  __shared__ int s_ro[kAppendLdsRows + 1];
+  const bool in_lds = B <= kAppendLdsRows;
+  if (in_lds) {
+    for (int i = threadIdx.x; i <= B; i += blockDim.x) s_ro[i] = row_offsets[i];
+    __syncthreads();
+  }
+  const int32_t* ro = in_lds ? s_ro : row_offsets;
   const int chunks = addr.d * esize / 16;           // per (row, head)
   const int64_t total = (int64_t)R * addr.hkv * chunks;
   int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -67,8 +80,8 @@ kv_append_kernel(const int32_t* __restrict__ row_offsets, const int32_t* __restr
     const int c = (int)(e % chunks);
     const int h = (int)((e / chunks) % addr.hkv);
     const int r = (int)(e / ((int64_t)chunks * addr.hkv));
-    const int b = request_of_row(row_offsets, B, r);
-    const int t = prefix_len[b] + (r - row_offsets[b]);
+    const int b = request_of_row(ro, B, r);
+    const int t = prefix_len[b] + (r - ro[b]);
     const int64_t dst = addr(b, h, t) * esize + (int64_t)c * 16;
     const uint4 val = is_v ? v_new[e] : k_new[e];
     *reinterpret_cast<uint4*>((is_v ? v_cache : k_cache) + dst) = val;
