@@ -293,3 +293,36 @@ def test_draft_expand_and_select_validation():
     big = _tree(batch=4096, capacity=256)
     assert sel(ctypes.byref(big), 5000, 8, FAKE, FAKE, FAKE, None, 5000, FAKE, 1 << 30, None) == 7
     assert "batch * (max_rows - 1)" in _err()
+
+
+def test_header_is_plain_c_and_links(tmp_path):
+    """A C99 program includes the header, links against the library and gets
+    the documented status for an empty batch (no device pointer is used)."""
+    import shutil
+    import subprocess
+
+    gcc = shutil.which("gcc")
+    rocm_inc = "/opt/rocm/include"
+    if gcc is None or not os.path.isdir(rocm_inc):
+        pytest.skip("gcc or the ROCm headers are not available")
+    src = tmp_path / "use_header.c"
+    src.write_text(
+        "#include <stdio.h>\n#include <string.h>\n#include \"spec_verify.h\"\n"
+        "int main(void) {\n"
+        "  spec_batch b; memset(&b, 0, sizeof b);\n"
+        "  if (spec_tree_build_mask(&b, 0, 0, 0, 0, 0, 0) != SPEC_ERR_SHAPE) return 2;\n"
+        "  printf(\"%s|%s\\n\", spec_status_string(SPEC_ERR_SHAPE), spec_last_error());\n"
+        "  return spec_abi_version() == SPEC_ABI_VERSION ? 0 : 1;\n"
+        "}\n")
+    exe = tmp_path / "use_header"
+    libdir = os.path.dirname(L.LIB_PATH)
+    cc = subprocess.run(
+        [gcc, "-std=c99", "-Wall", "-Wextra", "-Werror", "-D__HIP_PLATFORM_AMD__",
+         "-I", os.path.join(ROOT, "include"), "-I", rocm_inc, str(src),
+         "-L", libdir, "-lspecverify", "-Wl,-rpath," + libdir, "-o", str(exe)],
+        capture_output=True, text=True)
+    assert cc.returncode == 0, cc.stderr
+    run = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
+    assert run.returncode == 0, (run.returncode, run.stdout, run.stderr)
+    status, msg = run.stdout.strip().split("|")
+    assert status == "SPEC_ERR_SHAPE" and "batch" in msg
