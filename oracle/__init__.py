@@ -25,10 +25,13 @@ Pages followed (title, section):
 * "投机推理算法的常见优化手段" (cnblogs) -- draft-tree generation (EAGLE-2
   expansion of the most probable leaves) and dynamic draft length (ECHO's
   global budget and checkpoints).  -> ``draft``.
+* "投机推理算法的常见优化手段" (cnblogs) tree-mask section, and the survey
+  page's Medusa / EAGLE sections (the original LM head after the last layer)
+  -- the target LM head that produces every tree row's logits.  -> ``lm_head``.
 
 Readings of the pages where they are silent or garbled are listed in the
 module that takes them.  Every function here is pinned by the CPU tests
 against printed values, closed forms, library routines or brute force,
 except where a module header says "parity unpinned".
 """
-from . import philox, tree, attention, accept, kv, draft  # noqa: F401
+from . import philox, tree, attention, accept, kv, draft, lm_head  # noqa: F401

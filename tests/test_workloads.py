@@ -36,3 +36,15 @@ def test_drafter_candidates():
     assert (np.diff(p, axis=-1) <= 0).all() and (p > 0).all() and (p.sum(-1) <= 1 + 1e-6).all()
     t2, p2 = W.drafts.candidates(3, 4, 5, 1000, seed=9)
     assert np.array_equal(t, t2.numpy()) and np.array_equal(p, p2.numpy())
+
+
+def test_head_operands_shapes_scale_and_seeding():
+    w = W.make("chain8", L=64, V=3000, Hq=4, Hkv=4)
+    h, wt = W.heads.head_inputs(w, H=256)
+    assert h.shape == (w.R, 256) and wt.shape == (3000, 256)
+    assert h.dtype == wt.dtype and str(h.dtype) == "torch.bfloat16"
+    s = float(wt.float().std()) * 256 ** 0.5
+    assert 2.8 < s < 3.2
+    h2, wt2 = W.heads.head_inputs(w, H=256)
+    assert bool((h == h2).all()) and bool((wt == wt2).all())
+    assert W.heads.head_inputs(w)[0].shape == (w.R, w.Hq * w.D)
