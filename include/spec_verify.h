@@ -10,6 +10,8 @@
  *   spec_tree_attn_verify  tree attention: prefix + ancestors only
  *   spec_accept_sample     lossless acceptance walk + final token
  *   spec_accept_topk       the same for deterministic (top-k) children
+ *   spec_lm_head_accept    target LM head fused with the acceptance statistics,
+ *                          then the same walk
  *   spec_draft_begin / spec_draft_expand / spec_draft_select
  *                          build dynamic draft trees under a batch budget
  *   spec_kv_commit         compact the accepted path's K/V, roll back the rest
@@ -267,6 +269,57 @@ spec_status spec_accept_topk(const spec_batch *batch, const int32_t *parents_d,
                              int32_t vocab, float temperature, uint64_t seed, uint64_t step,
                              int32_t path_stride, const spec_accept_out *out, void *workspace_d,
                              size_t workspace_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * spec_lm_head_accept -- the target LM head feeding the acceptance directly.
+ * [TREE] tree-mask section (one target forward over the tree gives every
+ * node's next-token logits, and verification starts from them) and [SURV]
+ * Medusa / EAGLE sections (the model's original LM head maps a position's
+ * final feature to vocabulary logits).
+ *
+ * Target logits of tree row r: z[r][v] = sum_k hidden[r][k] * weight[v][k]
+ * (bias-free), bf16 operands, fp32 accumulation.  The statistics the
+ * acceptance needs from the target rows (log-sum-exp of z/T, or the argmax
+ * at T = 0) are formed from the fp32 results inside the product, so the
+ * logits are not read back for them.  Then the walk runs exactly as
+ * spec_accept_sample (children = SPEC_CHILDREN_SAMPLED, q_logits_d the
+ * drafter's rows) or spec_accept_topk (SPEC_CHILDREN_TOPK, q_logits_d
+ * ignored) would on the stored logits; temperature 0 is the greedy walk.
+ *
+ *   head->hidden_d   bf16 [R][hidden_size] (row stride hidden_size): the
+ *                    final feature of every tree row, in row order
+ *   head->weight_d   bf16 [vocab][hidden_size]: one row per vocabulary entry
+ *   head->hidden_size  a multiple of 64 in 64 .. 65536, with
+ *                    vocab * hidden_size and R * hidden_size below 2^31
+ *   head->logits_d   fp32 [R][logits_ld] output, written in full; required
+ *                    at temperature > 0 (the residual and bonus draws read
+ *                    back the rows they need), optional at temperature 0
+ *                    (NULL: the logits are never written)
+ *   q_logits_d       as spec_accept_sample (same logits_ld)
+ *   workspace >= spec_lm_head_accept_workspace_bytes(batch, vocab) bytes
+ *                    (no init needed; 16-byte aligned)
+ *
+ * Everything else (outputs, coins, flags) is as spec_accept_sample.  Inputs
+ * must be finite.  All pointers are device pointers except batch's host
+ * arrays; the caller owns every buffer.
+ */
+#define SPEC_CHILDREN_SAMPLED 0   /* children drafted from q (spec_accept_sample rule) */
+#define SPEC_CHILDREN_TOPK 1      /* deterministic children (spec_accept_topk rule) */
+
+typedef struct {
+  const void *hidden_d;
+  const void *weight_d;
+  int32_t hidden_size;
+  float *logits_d;
+} spec_lm_head;
+
+size_t spec_lm_head_accept_workspace_bytes(const spec_batch *batch, int32_t vocab);
+spec_status spec_lm_head_accept(const spec_batch *batch, const int32_t *parents_d,
+                                const int32_t *tokens_d, const spec_lm_head *head,
+                                const float *q_logits_d, int64_t logits_ld, int32_t vocab,
+                                float temperature, int32_t children, uint64_t seed, uint64_t step,
+                                int32_t path_stride, const spec_accept_out *out, void *workspace_d,
+                                size_t workspace_bytes, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
  * spec_kv_commit -- [SD] KV-cache management: keep accepted tokens' K/V,

@@ -29,7 +29,7 @@ def _declared():
 
 def test_header_declarations_are_all_exported():
     names = _declared()
-    assert "spec_tree_attn_verify" in names and len(names) == 15
+    assert "spec_tree_attn_verify" in names and len(names) == 17
     assert sorted(L.EXPORTS) == names
     lib = ctypes.CDLL(L.LIB_PATH)
     for n in names:
@@ -293,6 +293,38 @@ def test_draft_expand_and_select_validation():
     big = _tree(batch=4096, capacity=256)
     assert sel(ctypes.byref(big), 5000, 8, FAKE, FAKE, FAKE, None, 5000, FAKE, 1 << 30, None) == 7
     assert "batch * (max_rows - 1)" in _err()
+
+
+def test_lm_head_accept_validation():
+    b = _B([0, 3, 5], [4, 7])
+    out = L.CAcceptOut(FAKE, FAKE, FAKE, None, None, None, None)
+    need = L.LIB.spec_lm_head_accept_workspace_bytes(ctypes.byref(b.c), 1000)
+    assert need >= L.LIB.spec_accept_workspace_bytes(ctypes.byref(b.c), 1000)
+
+    def call(head=None, q=FAKE, ld=1000, vocab=1000, T=1.0, children=0, ws=need, parents=FAKE):
+        h = L.CLmHead(FAKE, FAKE, 256, FAKE) if head is None else head
+        return L.LIB.spec_lm_head_accept(ctypes.byref(b.c), parents, FAKE, ctypes.byref(h), q, ld,
+                                         vocab, T, children, 0, 0, 4, ctypes.byref(out), FAKE,
+                                         ws, None)
+    assert call(parents=None) == 1
+    assert call(head=L.CLmHead(None, FAKE, 256, FAKE)) == 1 and "hidden_d" in _err()
+    assert call(head=L.CLmHead(FAKE + 2, FAKE, 256, FAKE)) == 2 and "aligned" in _err()
+    assert call(head=L.CLmHead(FAKE, FAKE, 96, FAKE)) == 7 and "hidden_size" in _err()
+    assert call(head=L.CLmHead(FAKE, FAKE, 0, FAKE)) == 7
+    assert call(head=L.CLmHead(FAKE, FAKE, 256, None)) == 1 and "logits_d" in _err()
+    assert call(q=None) == 1 and "q_logits_d" in _err()
+    assert call(children=2) == 2 and "children" in _err()
+    assert call(T=-1.0) == 2 and "temperature" in _err()
+    assert call(ld=998) == 2 and "logits_ld" in _err()
+    assert call(vocab=0) == 7
+    assert call(head=L.CLmHead(FAKE, FAKE, 65536, FAKE), vocab=40000, ld=40000) == 7
+    assert "2^31" in _err()
+    assert call(ws=need - 1) == 8
+    # greedy: no draft rows and no logits buffer are needed (validation only;
+    # a missing workspace then stops the call before any launch)
+    assert call(head=L.CLmHead(FAKE, FAKE, 256, None), q=None, T=0.0, ws=0) == 8
+    # deterministic children: no draft rows
+    assert call(q=None, children=1, ws=0) == 8
 
 
 def test_header_is_plain_c_and_links(tmp_path):

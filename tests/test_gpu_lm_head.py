@@ -1,0 +1,252 @@
+"""GPU parity of the fused target LM head (spec_lm_head_accept).
+
+The oracle evaluates logits = hidden . weight^T in float64 from the same bf16
+operands; the library accumulates in fp32, so:
+
+* logits: every entry within the worst-case fp32 accumulation bound
+  gamma_H * sum_k |h_k w_k| of its oracle value, and an rms error below 1e-5
+  of the logits' own (``parity.check_head_logits``);
+* child probabilities: |d log P| <= 2 max_v |d z_v| / T (the logit and the
+  row's log-sum-exp each move by at most the row's largest logit error),
+  with that largest error measured against the oracle on the same rows;
+* acceptance: paths and tokens equal to the oracle's on the oracle logits;
+  decisions whose margin is within the logit error (1e-4 for a child test,
+  1e-7 of the mass for a draw) are reported, not failed;
+* greedy: paths equal unless an argmax on the way is a near tie (top-two
+  gap within twice the row's logit error), which is reported.
+
+A consistency check beside the oracle: the fused statistics against the
+plain acceptance (spec_accept_sample / spec_accept_topk) run on the logits
+the head stored -- same walk on the same logits; only the log-sum-exp is
+formed differently (fp32 exponentials summed in fp32 per lane, 64 terms:
+at most (64 + 2) * 2^-24 = 4e-6 relative).
+"""
+import numpy as np
+import pytest
+import torch
+
+pytestmark = pytest.mark.gpu
+
+import workloads as W  # noqa: E402
+from parity import (check_accept, check_head_logits, log, make, oracle_head_accept,  # noqa: E402
+                    oracle_head_logits, request_slice, run_step)
+
+FLAG_EPS = (1e-4, 1e-7)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import tree_attention_verification_02_amd._lib as L
+    return L
+
+
+def _rows_of(w, requests):
+    rows = []
+    for b in requests:
+        o, e = request_slice(w, b)
+        rows.extend(range(o, e))
+    return rows
+
+
+def _head_case(name, H, requests=None, temperature=1.0, seed=0, topk=False, store=True,
+               **kw):
+    w = make(name, **({"draft": "topk"} if topk else {}), **kw)
+    hidden, weight = W.heads.head_inputs(w, H=H)
+    log(f"[parity] head R={w.R} V={w.V} H={H} T={temperature} topk={topk}")
+    vs = run_step(w, temperature=temperature, seed=seed, step=0, commit=False,
+                  acceptance="topk" if topk else "sample", head=(hidden, weight),
+                  store_head_logits=store)
+    requests = list(range(w.B)) if requests is None else requests
+    rows = _rows_of(w, requests)
+    z, bound = oracle_head_logits(hidden, weight, rows)
+    return w, vs, hidden, weight, requests, rows, z, bound
+
+
+def _z_by_request(w, requests, rows, z):
+    pos = {r: i for i, r in enumerate(rows)}
+    out = {}
+    for b in requests:
+        o, e = request_slice(w, b)
+        out[b] = z[[pos[r] for r in range(o, e)]]
+    return out
+
+
+def _check_sampled(w, vs, requests, rows, z, bound, temperature, seed, topk):
+    got = vs.head_logits[torch.as_tensor(rows, device="cuda"), :w.V].double().cpu().numpy()
+    err = check_head_logits(got, z, bound, f"{w.name} rows {len(rows)}")
+    zb = _z_by_request(w, requests, rows, z)
+    ref = oracle_head_accept(w, zb, temperature, seed, 0, requests, topk=topk)
+    pos = {r: i for i, r in enumerate(rows)}
+    T = float(np.float32(temperature))
+    tol = {}
+    for b in requests:
+        o, e = request_slice(w, b)
+        tol[b] = 2.0 * max(err[pos[r]] for r in range(o, e)) / T + 1e-6
+    check_accept(w, vs, temperature, seed, 0, requests=requests, topk=topk, ref=ref,
+                 flag_eps=FLAG_EPS, prob_rtol=tol, max_flagged=2)
+
+
+def _check_greedy(w, vs, requests, rows, z, bound):
+    from oracle import accept as OA
+    zb = _z_by_request(w, requests, rows, z)
+    errb = {}
+    pos = {r: i for i, r in enumerate(rows)}
+    alen = vs.acc.accept_len.cpu().numpy()
+    path = vs.acc.path.cpu().numpy()
+    toks = vs.acc.tokens.cpu().numpy()
+    near = 0
+    for b in requests:
+        o, e = request_slice(w, b)
+        r = OA.accept_request(w.parents[o:e], w.tokens[o:e], zb[b], None, 0.0, 0, 0, b)
+        S = path.shape[1]
+        exp_path = r["path"] + [-1] * (S - len(r["path"]))
+        exp_tok = r["tokens"] + [-1] * (S - len(r["tokens"]))
+        if alen[b] == r["accept_len"] and list(path[b]) == exp_path and list(toks[b]) == exp_tok:
+            continue
+        # allowed only through a near tie on the oracle's path
+        tie = False
+        for u in r["path"]:
+            row = np.sort(zb[b][u])
+            gap = row[-1] - row[-2]
+            errb = 2.0 * float(bound[pos[o + u]].max())
+            tie |= gap <= errb
+        assert tie, f"request {b}: greedy path differs with no near tie"
+        near += 1
+    log(f"[parity] head greedy: {len(requests)} requests, {near} differ through a near tie")
+    assert near <= 1
+
+
+def _check_consistent(lib, w, vs, temperature, seed, topk):
+    """The plain acceptance on the stored head logits gives the same walk."""
+    dev = "cuda"
+    batch = vs.batch
+    S = vs.acc.path.shape[1]
+    out = lib.AcceptOut(torch.empty(w.B, dtype=torch.int32, device=dev),
+                        torch.empty((w.B, S), dtype=torch.int32, device=dev),
+                        torch.empty((w.B, S), dtype=torch.int32, device=dev),
+                        accept_mask=torch.empty(w.R, dtype=torch.uint8, device=dev),
+                        child_p=torch.empty(w.R, dtype=torch.float32, device=dev),
+                        flags=torch.empty(w.B, dtype=torch.int32, device=dev))
+    ws = torch.empty(lib.spec_accept_workspace_bytes(batch, w.V), dtype=torch.uint8, device=dev)
+    if topk:
+        lib.spec_accept_topk(batch, vs.parents, vs.tokens, vs.head_logits, w.V, temperature, seed,
+                             0, out, ws, logits_ld=vs.head_ld)
+    else:
+        q = w.q_logits if temperature > 0 else None
+        lib.spec_accept_sample(batch, vs.parents, vs.tokens, vs.head_logits, q, w.V, temperature,
+                               seed, 0, out, ws, logits_ld=vs.head_ld)
+    torch.cuda.synchronize()
+    for name in ("accept_len", "path", "tokens", "accept_mask", "flags"):
+        a, b = getattr(out, name), getattr(vs.acc, name)
+        assert torch.equal(a, b), f"{name} differs from the plain acceptance"
+    cp0 = out.child_p.double().cpu().numpy()
+    cp1 = vs.acc.child_p.double().cpu().numpy()
+    fin = np.isfinite(cp0)
+    assert np.array_equal(fin, np.isfinite(cp1))
+    rel = np.abs(cp0[fin] - cp1[fin]) / np.maximum(np.abs(cp0[fin]), 1e-30)
+    assert rel.max(initial=0) <= 4e-6, rel.max(initial=0)
+    log(f"[parity] head vs plain acceptance on the stored logits: child_p rel "
+        f"{rel.max(initial=0):.3g}")
+
+
+SMALL = {
+    # one row tile (R = 92 < 256), a ragged last vocabulary tile (6000 = 23 x 256 + 112)
+    "specinfer-1tile": dict(name="specinfer", H=256, B=2, L=64, Hq=4, Hkv=1, V=6000),
+    # two row tiles (ragged), 129 vocabulary tiles, 3 statistics chunks
+    "dynamic-2tiles": dict(name="dynamic", H=512, B=24, L=("uniform", 8, 64), Hq=4, Hkv=1,
+                           V=33000),
+}
+
+
+@pytest.mark.parametrize("case", sorted(SMALL))
+@pytest.mark.parametrize("mode", ["sample", "topk", "greedy"])
+def test_head_parity_small(lib, case, mode):
+    kw = dict(SMALL[case])
+    name, H = kw.pop("name"), kw.pop("H")
+    T = 0.0 if mode == "greedy" else (0.7 if mode == "topk" else 1.0)
+    w, vs, hidden, weight, req, rows, z, bound = _head_case(
+        name, H, temperature=T, seed=3, topk=mode == "topk", store=True, **kw)
+    if mode == "greedy":
+        got = vs.head_logits[torch.as_tensor(rows, device="cuda"), :w.V].double().cpu().numpy()
+        check_head_logits(got, z, bound, f"{name} greedy")
+        _check_greedy(w, vs, req, rows, z, bound)
+    else:
+        _check_sampled(w, vs, req, rows, z, bound, T, 3, mode == "topk")
+    _check_consistent(lib, w, vs, T, 3, mode == "topk")
+
+
+@pytest.mark.parametrize("mode", ["sample", "greedy"])
+def test_head_ragged_vocab_padded_rows(lib, mode):
+    """vocab 4001 in rows of 4004 floats: the head writes only the first 4001
+    of each stored row (the padding keeps its NaN), and the last vocabulary
+    tile's entries past 4001 never reach the statistics."""
+    from oracle import accept as OA
+    V, LD = 4001, 4004
+    w = make("specinfer", B=2, L=64, Hq=4, Hkv=1, V=V)
+    hidden, weight = W.heads.head_inputs(w, H=256)
+    dev = "cuda"
+    R = w.R
+    ql = torch.full((R, LD), float("nan"), dtype=torch.float32, device=dev)
+    ql[:, :V] = torch.nan_to_num(w.q_logits, nan=0.0)
+    logits = torch.full((R, LD), float("nan"), dtype=torch.float32, device=dev)
+    batch = lib.Batch(w.row_offsets, w.prefix_len, dev)
+    S = batch.c.max_rows
+    out = lib.AcceptOut(torch.empty(w.B, dtype=torch.int32, device=dev),
+                        torch.empty((w.B, S), dtype=torch.int32, device=dev),
+                        torch.empty((w.B, S), dtype=torch.int32, device=dev),
+                        child_p=torch.empty(R, dtype=torch.float32, device=dev),
+                        flags=torch.empty(w.B, dtype=torch.int32, device=dev))
+    ws = torch.empty(lib.spec_lm_head_accept_workspace_bytes(batch, V), dtype=torch.uint8,
+                     device=dev)
+    par = torch.from_numpy(w.parents.astype(np.int32)).to(dev)
+    tok = torch.from_numpy(w.tokens.astype(np.int32)).to(dev)
+    T = 0.0 if mode == "greedy" else 1.0
+    lib.spec_lm_head_accept(batch, par, tok, hidden, weight, ql if T > 0 else None, V, T, 4, 0,
+                            out, ws, logits=logits, logits_ld=LD)
+    torch.cuda.synchronize()
+    assert torch.isnan(logits[:, V:]).all(), "padding was written"
+    z, bound = oracle_head_logits(hidden, weight, list(range(R)))
+    check_head_logits(logits[:, :V].double().cpu().numpy(), z, bound, "ragged vocab")
+    alen = out.accept_len.cpu().numpy()
+    toks = out.tokens.cpu().numpy()
+    for b in range(w.B):
+        o, e = request_slice(w, b)
+        q64 = torch.nan_to_num(w.q_logits[o:e], nan=0.0).double().cpu().numpy()
+        r = OA.accept_request(w.parents[o:e], w.tokens[o:e], z[o:e], q64 if T > 0 else None, T,
+                              4, 0, b)
+        if T > 0 and r["result"].first_flag(*FLAG_EPS) is not None:
+            continue
+        assert alen[b] == r["accept_len"], (b, alen[b], r["accept_len"])
+        assert list(toks[b][:alen[b] + 1]) == r["tokens"], b
+
+
+def test_head_greedy_without_logits(lib):
+    """temperature 0 with no logits buffer: nothing is written, and the walk
+    equals the one that stores them."""
+    w = make("specinfer", B=2, L=64, Hq=4, Hkv=1, V=6000)
+    hidden, weight = W.heads.head_inputs(w, H=256)
+    a = run_step(w, temperature=0.0, commit=False, head=(hidden, weight), store_head_logits=False)
+    sentinel = a.head_logits.clone()
+    b = run_step(w, temperature=0.0, commit=False, head=(hidden, weight), store_head_logits=True)
+    assert torch.equal(a.head_logits.view(torch.int32), sentinel.view(torch.int32))
+    for name in ("accept_len", "path", "tokens", "accept_mask", "child_p", "flags"):
+        x, y = getattr(a.acc, name), getattr(b.acc, name)
+        assert torch.equal(x.view(torch.uint8), y.view(torch.uint8)), name
+
+
+def test_head_full_size_sampled(lib):
+    """The batched dynamic workload at full size (64 requests, 1024 rows,
+    vocabulary 128256, H = 4096), the launch the benchmark times: logits and
+    acceptance of three requests (first, middle, last -- the last row tile)
+    against the oracle, and every request against the plain acceptance on
+    the stored logits."""
+    w = make("dynamic")
+    hidden, weight = W.heads.head_inputs(w)
+    vs = run_step(w, temperature=1.0, seed=0, step=0, commit=False, head=(hidden, weight))
+    req = [0, w.B // 2, w.B - 1]
+    rows = _rows_of(w, req)
+    z, bound = oracle_head_logits(hidden, weight, rows)
+    _check_sampled(w, vs, req, rows, z, bound, 1.0, 0, False)
+    _check_consistent(lib, w, vs, 1.0, 0, False)
+    del vs, hidden, weight
+    torch.cuda.empty_cache()

@@ -32,7 +32,9 @@ STATUS_NAMES = {0: "SPEC_OK", 1: "SPEC_ERR_NULL", 2: "SPEC_ERR_SHAPE", 3: "SPEC_
 EXPORTS = ["spec_tree_build_mask", "spec_kv_append", "spec_tree_attn_workspace_bytes",
            "spec_tree_attn_verify", "spec_accept_workspace_bytes", "spec_accept_sample",
            "spec_accept_topk", "spec_kv_commit", "spec_draft_begin", "spec_draft_expand",
-           "spec_draft_select_workspace_bytes", "spec_draft_select", "spec_status_string", "spec_last_error", "spec_abi_version"]
+           "spec_draft_select_workspace_bytes", "spec_draft_select", "spec_lm_head_accept_workspace_bytes",
+           "spec_lm_head_accept", "spec_status_string", "spec_last_error", "spec_abi_version"]
+SPEC_CHILDREN_SAMPLED, SPEC_CHILDREN_TOPK = 0, 1
 
 
 class SpecError(RuntimeError):
@@ -60,6 +62,11 @@ class CAcceptOut(ctypes.Structure):
                 ("tokens_d", ctypes.c_void_p), ("accept_mask_d", ctypes.c_void_p),
                 ("child_p_d", ctypes.c_void_p), ("child_q_d", ctypes.c_void_p),
                 ("flags_d", ctypes.c_void_p)]
+
+
+class CLmHead(ctypes.Structure):
+    _fields_ = [("hidden_d", ctypes.c_void_p), ("weight_d", ctypes.c_void_p),
+                ("hidden_size", ctypes.c_int32), ("logits_d", ctypes.c_void_p)]
 
 
 class CDraftTree(ctypes.Structure):
@@ -95,6 +102,9 @@ def _load():
         "spec_draft_select_workspace_bytes": ([i32, i32], sz),
         "spec_draft_select": ([P(CDraftTree), i32, i32, vp, vp, vp, vp, i32, vp, sz, vp],
                               ctypes.c_int),
+        "spec_lm_head_accept_workspace_bytes": ([P(CBatch), i32], sz),
+        "spec_lm_head_accept": ([P(CBatch), vp, vp, P(CLmHead), vp, i64, i32, f32, i32, u64, u64,
+                                 i32, P(CAcceptOut), vp, sz, vp], ctypes.c_int),
         "spec_status_string": ([ctypes.c_int], ctypes.c_char_p),
         "spec_last_error": ([], ctypes.c_char_p),
         "spec_abi_version": ([], ctypes.c_int),
@@ -250,6 +260,30 @@ def spec_accept_topk(batch, parents, tokens, p_logits, vocab, temperature, seed,
                                 _ptr(p_logits), int(logits_ld), int(vocab), float(temperature),
                                 int(seed), int(step), out.path_stride, ctypes.byref(out.c),
                                 _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def spec_lm_head_accept_workspace_bytes(batch, vocab):
+    n = LIB.spec_lm_head_accept_workspace_bytes(ctypes.byref(batch.c), int(vocab))
+    if n == 0:
+        raise SpecError(2, LIB.spec_last_error().decode())
+    return int(n)
+
+
+def spec_lm_head_accept(batch, parents, tokens, hidden, weight, q_logits, vocab, temperature,
+                        seed, step, out, workspace, logits=None, children=SPEC_CHILDREN_SAMPLED,
+                        logits_ld=None, stream=None):
+    """hidden [R][H] and weight [V][H] bf16; logits [R][ld] fp32 output (None
+    allowed at temperature 0); q_logits as spec_accept_sample."""
+    if logits_ld is None:
+        ref = logits if logits is not None else q_logits
+        logits_ld = ref.stride(0) if ref is not None else ((int(vocab) + 3) // 4) * 4
+    head = CLmHead(_ptr(hidden), _ptr(weight), int(hidden.shape[1]), _ptr(logits))
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(LIB.spec_lm_head_accept(ctypes.byref(batch.c), _ptr(parents), _ptr(tokens),
+                                   ctypes.byref(head), _ptr(q_logits), int(logits_ld), int(vocab),
+                                   float(temperature), int(children), int(seed), int(step),
+                                   out.path_stride, ctypes.byref(out.c), _ptr(workspace), ws_bytes,
+                                   _stream(stream)))
 
 
 def spec_kv_commit(batch, kv, accept_len, path, new_len, freed_blocks=None, stream=None):

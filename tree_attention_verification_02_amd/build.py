@@ -22,7 +22,7 @@ CSRC = os.path.join(PKG, "csrc")
 LIBDIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIBDIR, "libspecverify.so")
 BUILD = os.path.join(ROOT, "_build")
-SOURCES = ["api.cpp", "tree_kv.hip", "attention.hip", "accept.hip", "draft.hip"]
+SOURCES = ["api.cpp", "tree_kv.hip", "attention.hip", "accept.hip", "draft.hip", "lm_head.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

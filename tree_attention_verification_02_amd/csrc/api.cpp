@@ -293,6 +293,64 @@ spec_status spec_accept_topk(const spec_batch* batch, const int32_t* parents_d, 
                      "spec_accept_topk");
 }
 
+size_t spec_lm_head_accept_workspace_bytes(const spec_batch* batch, int32_t vocab) {
+  int R = 0;
+  if (check_batch(batch, &R) != SPEC_OK || vocab < 1 || vocab > kMaxVocab) return 0;
+  return ((spec::accept_workspace_bytes(R, batch->batch, vocab) + 255) & ~(size_t)255) +
+         spec::head_tiles_bytes(R, vocab);
+}
+
+spec_status spec_lm_head_accept(const spec_batch* batch, const int32_t* parents_d,
+                                const int32_t* tokens_d, const spec_lm_head* head,
+                                const float* q_logits_d, int64_t logits_ld, int32_t vocab,
+                                float temperature, int32_t children, uint64_t seed, uint64_t step,
+                                int32_t path_stride, const spec_accept_out* out, void* workspace_d,
+                                size_t workspace_bytes, hipStream_t stream) {
+  int R = 0;
+  spec_status st = check_batch(batch, &R);
+  if (st != SPEC_OK) return st;
+  if (!parents_d || !tokens_d) return fail(SPEC_ERR_NULL, "parents_d and tokens_d are required");
+  if (!head || !head->hidden_d || !head->weight_d)
+    return fail(SPEC_ERR_NULL, "head, head->hidden_d and head->weight_d are required");
+  if (!aligned16(head->hidden_d) || !aligned16(head->weight_d))
+    return fail(SPEC_ERR_SHAPE, "head->hidden_d / head->weight_d must be 16-byte aligned");
+  const int H = head->hidden_size;
+  if (H < 64 || H > 65536 || H % 64)
+    return fail(SPEC_ERR_UNSUPPORTED, "hidden_size = %d, supported: multiples of 64 in 64..65536", H);
+  if (!(temperature >= 0.0f) || temperature > 1e30f) return fail(SPEC_ERR_SHAPE, "temperature must be finite and >= 0");
+  if (children != SPEC_CHILDREN_SAMPLED && children != SPEC_CHILDREN_TOPK)
+    return fail(SPEC_ERR_SHAPE, "children = %d, need SPEC_CHILDREN_SAMPLED or SPEC_CHILDREN_TOPK", children);
+  const bool topk = children == SPEC_CHILDREN_TOPK;
+  if (!topk && temperature > 0.0f && !q_logits_d) return fail(SPEC_ERR_NULL, "q_logits_d is required when temperature > 0");
+  if (temperature > 0.0f && !head->logits_d) return fail(SPEC_ERR_NULL, "head->logits_d is required when temperature > 0");
+  if (vocab < 1 || vocab > kMaxVocab) return fail(SPEC_ERR_UNSUPPORTED, "vocab = %d, supported 1..%d", vocab, kMaxVocab);
+  if ((int64_t)vocab * H >= (1ll << 31) || (int64_t)R * H >= (1ll << 31))
+    return fail(SPEC_ERR_UNSUPPORTED, "vocab * hidden_size and rows * hidden_size must stay below 2^31");
+  if (logits_ld < vocab || logits_ld % 4) return fail(SPEC_ERR_SHAPE, "logits_ld = %lld must be >= vocab and a multiple of 4", (long long)logits_ld);
+  if ((head->logits_d && !aligned16(head->logits_d)) || (q_logits_d && !aligned16(q_logits_d)))
+    return fail(SPEC_ERR_SHAPE, "logits pointers must be 16-byte aligned");
+  if (path_stride < 1) return fail(SPEC_ERR_SHAPE, "path_stride = %d, need >= 1", path_stride);
+  if (!out || !out->accept_len_d || !out->path_d || !out->tokens_d)
+    return fail(SPEC_ERR_NULL, "out, accept_len_d, path_d and tokens_d are required");
+  const size_t acc_bytes = (spec::accept_workspace_bytes(R, batch->batch, vocab) + 255) & ~(size_t)255;
+  const size_t need = acc_bytes + spec::head_tiles_bytes(R, vocab);
+  if (!workspace_d || workspace_bytes < need)
+    return fail(SPEC_ERR_WORKSPACE, "LM head workspace %zu bytes < required %zu", workspace_bytes, need);
+  if (!aligned16(workspace_d)) return fail(SPEC_ERR_SHAPE, "workspace must be 16-byte aligned");
+  const spec::HeadTiles tiles = spec::head_tiles((char*)workspace_d + acc_bytes, R, vocab);
+  hipError_t e = spec::launch_lm_head(R, (const uint16_t*)head->hidden_d, H,
+                                      (const uint16_t*)head->weight_d, vocab, temperature,
+                                      head->logits_d, logits_ld, tiles, stream);
+  if (e != hipSuccess) return launched(e, "spec_lm_head_accept (head)");
+  return launched(spec::launch_accept(ctx(batch, stream), R, parents_d, tokens_d, head->logits_d,
+                                      (temperature > 0.0f && !topk) ? q_logits_d : nullptr,
+                                      logits_ld, vocab, temperature, seed, step, path_stride,
+                                      out->accept_len_d, out->path_d, out->tokens_d,
+                                      out->accept_mask_d, out->child_p_d, out->child_q_d,
+                                      out->flags_d, workspace_d, walk_slices_override(), &tiles),
+                  "spec_lm_head_accept");
+}
+
 spec_status spec_kv_commit(const spec_batch* batch, const spec_kv* kv, const int32_t* accept_len_d,
                            const int32_t* path_d, int32_t path_stride, int32_t* new_len_d,
                            int32_t* freed_blocks_d, hipStream_t stream) {

@@ -61,15 +61,37 @@ hipError_t launch_attention_f32(const LaunchCtx& cx, int R, const KvAddr& addr, 
                                 const float* q, const uint64_t* mask, int words, float scale,
                                 const float* k_cache, const float* v_cache, void* out, int out_f32);
 
+// Target LM head: logits = hidden . weight^T (bf16 in, fp32 out) with, per
+// (tree row, kHeadTileV-entry vocabulary tile), the partial statistics of the
+// acceptance: (reference, sum) at temperature > 0, (max, first argmax) at 0.
+constexpr int kHeadTileV = 256;   // vocabulary entries per tile
+constexpr int kHeadTileR = 256;   // tree rows per workgroup
+struct HeadTiles {
+  int ntile;      // vocabulary tiles per row
+  double* ref;    // [R][ntile]  temperature > 0
+  double* s;
+  float* m;       // [R][ntile]  temperature 0 (aliases ref / s)
+  int32_t* am;
+};
+int head_vocab_tiles(int vocab);
+size_t head_tiles_bytes(int R, int vocab);
+HeadTiles head_tiles(void* base, int R, int vocab);
+hipError_t launch_lm_head(int R, const uint16_t* hidden, int H, const uint16_t* weight, int vocab,
+                          float temperature, float* logits, int64_t ld, const HeadTiles& tiles,
+                          hipStream_t stream);
+
 // Acceptance.  At temperature > 0, q_logits == nullptr selects deterministic
-// children (each child a point-mass draft; no draft rows are read).
+// children (each child a point-mass draft; no draft rows are read).  With
+// `head`, the target rows' statistics come from the LM head's tile partials
+// (merged here) instead of a pass over p_logits; p_logits may then be null at
+// temperature 0.
 size_t accept_workspace_bytes(int R, int B, int vocab);
 hipError_t launch_accept(const LaunchCtx& cx, int R, const int32_t* parents, const int32_t* tokens,
                          const float* p_logits, const float* q_logits, int64_t ld, int vocab,
                          float temperature, uint64_t seed, uint64_t step, int path_stride,
                          int32_t* accept_len, int32_t* path, int32_t* tokens_out,
                          uint8_t* accept_mask, float* child_p, float* child_q, int32_t* flags,
-                         void* workspace, int slices_override);
+                         void* workspace, int slices_override, const HeadTiles* head = nullptr);
 
 // Dynamic draft trees (EAGLE-2 rounds, global row budget).
 constexpr int kDraftMaxK = 16;          // children per expanded node, nodes expanded per round

@@ -30,10 +30,14 @@ def pack_visibility(visibility, row_offsets, words):
 
 class VerifyStep:
     def __init__(self, w, path_stride=None, out_dtype=None, temperature=None, seed=None, step=None,
-                 acceptance="sample"):
+                 acceptance="sample", head=None, store_head_logits=False):
         """``w`` is any object with the workload fields (see workloads.gen.Workload).
         ``acceptance``: "sample" (children drawn from the draft rows) or "topk"
-        (deterministic children: spec_accept_topk, draft rows unused)."""
+        (deterministic children: spec_accept_topk, draft rows unused).
+        ``head``: optional (hidden [R][H], weight [V][H]) bf16 tensors; the
+        target logits then come from the LM head (spec_lm_head_accept) instead
+        of ``w.p_logits``, and are kept in ``head_logits`` (always at
+        temperature > 0; at 0 only with ``store_head_logits``)."""
         if acceptance not in ("sample", "topk"):
             raise ValueError(f"acceptance must be 'sample' or 'topk', not {acceptance!r}")
         self.acceptance = acceptance
@@ -72,6 +76,13 @@ class VerifyStep:
             flags=torch.empty(B, dtype=torch.int32, device=dev))
         self.acc_ws = torch.empty(L.spec_accept_workspace_bytes(self.batch, w.V),
                                   dtype=torch.uint8, device=dev)
+        self.head = head
+        self.store_head_logits = store_head_logits
+        if head is not None:
+            self.head_ld = int(w.q_logits.stride(0))
+            self.head_logits = torch.empty((R, self.head_ld), dtype=torch.float32, device=dev)
+            self.head_ws = torch.empty(L.spec_lm_head_accept_workspace_bytes(self.batch, w.V),
+                                       dtype=torch.uint8, device=dev)
         self.new_len = torch.empty(B, dtype=torch.int32, device=dev)
         mbps = int(w.block_table.shape[1]) if w.block_table is not None else 1
         self.freed = torch.empty((B, mbps), dtype=torch.int32, device=dev)
@@ -96,6 +107,17 @@ class VerifyStep:
                                 self.attn_out, self.attn_ws, stream)
 
     def accept(self, stream=None):
+        if self.head is not None:
+            hidden, weight = self.head
+            topk = self.acceptance == "topk"
+            store = self.temperature > 0 or self.store_head_logits
+            q = self.w.q_logits if (self.temperature > 0 and not topk) else None
+            L.spec_lm_head_accept(self.batch, self.parents, self.tokens, hidden, weight, q,
+                                  self.w.V, self.temperature, self.seed, self.step, self.acc,
+                                  self.head_ws, logits=self.head_logits if store else None,
+                                  children=L.SPEC_CHILDREN_TOPK if topk else L.SPEC_CHILDREN_SAMPLED,
+                                  logits_ld=self.head_ld, stream=stream)
+            return
         if self.acceptance == "topk":
             L.spec_accept_topk(self.batch, self.parents, self.tokens, self.w.p_logits, self.w.V,
                                self.temperature, self.seed, self.step, self.acc, self.acc_ws,
