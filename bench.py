@@ -9,7 +9,10 @@ spec_accept_topk with --acceptance topk) -> spec_kv_commit, on synthetic inputs 
 line: verified tree tokens/s (all verify rows, roots included, per second of
 wall-clock over K steps), the roofline of the dominant kernel (tree
 attention) from live HIP-event timing, and the CPU oracle timed on a bounded
-sample of the same workload on this host's cores.
+sample of the same workload on this host's cores.  Beside the step (not in
+its time): the fused target LM head (spec_lm_head_accept) on the same rows,
+with a library GEMM plus the plain acceptance as context (--no-lm-head skips
+it).
 """
 import argparse
 import json
@@ -185,6 +188,57 @@ class TreeBuilder:
         return ro, self.par[:ro[-1]].cpu().numpy(), self.tok[:ro[-1]].cpu().numpy()
 
 
+def measure_lm_head(w, acceptance, accept_ms, reps=15):
+    """The fused target LM head (spec_lm_head_accept) on the same workload:
+    hidden states [R][Hq*D] and a [V][Hq*D] head, bf16.  Reported beside the
+    step, with a library GEMM (torch.mm, hipBLASLt, fp32 output) followed by
+    the plain acceptance as context."""
+    import torch
+    import workloads as W
+    from tree_attention_verification_02_amd.pipeline import VerifyStep
+    hidden, weight = W.heads.head_inputs(w)
+    H = int(hidden.shape[1])
+    flops = 2.0 * w.R * H * w.V
+
+    def med(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        ts.sort()
+        return ts[len(ts) // 2]
+
+    hs = VerifyStep(w, acceptance=acceptance, head=(hidden, weight))
+    t_head = med(hs.accept)
+    hg = VerifyStep(w, acceptance=acceptance, temperature=0.0, head=(hidden, weight))
+    t_greedy = med(hg.accept)
+    try:
+        t_lib = med(lambda: torch.mm(hidden, weight.t(), out_dtype=torch.float32))
+        lib_kind = "torch.mm bf16 -> fp32 (hipBLASLt)"
+    except (RuntimeError, TypeError):
+        t_lib = med(lambda: torch.mm(hidden, weight.t()).float())
+        lib_kind = "torch.mm bf16 -> bf16, then to fp32"
+    mean_acc = float(hs.acc.accept_len.float().mean())
+    del hs, hg, hidden, weight
+    torch.cuda.empty_cache()
+    return {"call": "spec_lm_head_accept (head GEMM with the acceptance statistics in its "
+                    "epilogue, then the walk)",
+            "hidden": H, "flops": flops, "temperature": float(w.temperature),
+            "ms": t_head, "ms_greedy": t_greedy,
+            "tflops_greedy": flops / (t_greedy * 1e-3) / 1e12,
+            "mfma_frac_greedy": flops / (t_greedy * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+            "library_gemm": lib_kind, "library_gemm_ms": t_lib,
+            "library_gemm_plus_accept_ms": t_lib + accept_ms,
+            "mean_accepted_drafts": mean_acc}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -202,6 +256,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-copy-probe", action="store_true",
                     help="skip the device-copy bandwidth probe printed as context")
+    ap.add_argument("--no-lm-head", action="store_true",
+                    help="skip the fused target LM head measurement (spec_lm_head_accept)")
     ap.add_argument("--calib-copy-gib", type=float, default=0.0,
                     help="also run one device copy of this many GiB (counter calibration)")
     args = ap.parse_args()
@@ -321,6 +377,8 @@ def main():
         "gpu_ms_per_step": gpu_ms,
         "mean_accepted_drafts": float(vs.acc.accept_len.float().mean()),
     }
+    if not args.no_lm_head and builder is None:
+        out["lm_head"] = measure_lm_head(w, args.acceptance, per["accept"])
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, topk)
     print(json.dumps(out), flush=True)
