@@ -250,3 +250,41 @@ def test_head_full_size_sampled(lib):
     _check_consistent(lib, w, vs, 1.0, 0, False)
     del vs, hidden, weight
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("T", [1.0, 0.0])
+def test_head_single_row_single_tile(lib, T):
+    """One request with only its root (R = 1): one row tile holding a single
+    row, a vocabulary of 200 (one partial tile) and H = 64 (one K slice)."""
+    w = make("dynamic", B=1, L=[5], V=200, Hq=2, Hkv=1, tree=("given", [np.array([-1])]),
+             given_tokens=np.array([7]))
+    hidden, weight = W.heads.head_inputs(w, H=64)
+    vs = run_step(w, temperature=T, seed=1, step=0, commit=False, head=(hidden, weight),
+                  store_head_logits=True)
+    z, bound = oracle_head_logits(hidden, weight, [0])
+    check_head_logits(vs.head_logits[:1, :200].double().cpu().numpy(), z, bound, "single row")
+    from oracle import accept as OA
+    r = OA.accept_request(w.parents, w.tokens, z, None, T, 1, 0, 0)
+    assert int(vs.acc.accept_len[0]) == 0 == r["accept_len"]
+    flag = r["result"].first_flag(*FLAG_EPS)
+    if T == 0 or flag is None:
+        assert int(vs.acc.tokens[0, 0]) == r["tokens"][0]
+    else:
+        log("[parity] single-row bonus draw near a boundary: not compared")
+
+
+def test_head_full_size_specinfer_wide(lib):
+    """The SpecInfer batch at full size with the 70B-class width H = Hq * D =
+    8192: 368 rows (the second row tile holds 112), vocabulary 128256; the last
+    request against the oracle, every request against the plain acceptance."""
+    w = make("specinfer")
+    hidden, weight = W.heads.head_inputs(w)
+    assert hidden.shape[1] == 8192
+    vs = run_step(w, temperature=1.0, seed=2, step=0, commit=False, head=(hidden, weight))
+    req = [w.B - 1]
+    rows = _rows_of(w, req)
+    z, bound = oracle_head_logits(hidden, weight, rows)
+    _check_sampled(w, vs, req, rows, z, bound, 1.0, 2, False)
+    _check_consistent(lib, w, vs, 1.0, 2, False)
+    del vs, hidden, weight
+    torch.cuda.empty_cache()
