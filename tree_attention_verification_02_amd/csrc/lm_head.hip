@@ -163,6 +163,15 @@ __global__ void __launch_bounds__(WAVES * 64, 1) lm_head_kernel(HeadArgs a) {
 #pragma unroll
         for (int j = 0; j < JT; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+      // Scheduling hint: alternate the 4 + JT fragment reads with as many
+      // MFMAs (mask 0x100 = LDS read, 0x008 = MFMA), so a wave's reads for the
+      // next K step overlap its multiplies instead of bunching before them.
+#pragma unroll
+      for (int q = 0; q < 4 + JT; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 4 * JT - (4 + JT), 0);
     }
   };
 
