@@ -41,7 +41,8 @@
  *  - All pointers named *_d are device memory, *_h host memory.  The caller
  *    owns every buffer; the library never allocates or frees, and keeps no
  *    pointer after a call returns.  Scratch comes from caller workspaces
- *    sized by the *_workspace_bytes queries.
+ *    sized by the *_workspace_bytes queries (which return 0 for invalid
+ *    arguments).
  *  - Every call validates its arguments on the host first.  Invalid
  *    arguments return a status != SPEC_OK and launch nothing; the detail is
  *    in spec_last_error() (thread-local).  Valid calls enqueue kernels on
