@@ -33,8 +33,9 @@
 //    one chunk per LDS cycle -- touches all 64 banks once.
 //  * The dispatcher deals workgroup ids round-robin to the 8 XCDs; the ids
 //    that land on one XCD walk vocabulary tiles with the row tiles inner, so
-//    the row tiles sharing a weight tile run together behind one L2 and the
-//    weight (the bulk of the bytes) comes from HBM about once.
+//    the row tiles sharing a weight tile run together behind one L2, and the
+//    weight (the bulk of the bytes) is fetched from beyond L2 about 1.5 times
+//    rather than once per row tile.
 #include <math.h>
 
 #include "common.hpp"
