@@ -288,3 +288,15 @@ def test_head_full_size_specinfer_wide(lib):
     _check_consistent(lib, w, vs, 1.0, 2, False)
     del vs, hidden, weight
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("T", [0.05, 4.0])
+def test_head_extreme_temperatures(lib, T):
+    """Very sharp and very flat target distributions through the head: the
+    tile sums' reference (tile max / T) keeps every exponent <= 0 at T = 0.05,
+    and T = 4 spreads the mass over the whole 33000-entry vocabulary."""
+    kw = dict(SMALL["dynamic-2tiles"])
+    name, H = kw.pop("name"), kw.pop("H")
+    w, vs, hidden, weight, req, rows, z, bound = _head_case(name, H, temperature=T, seed=5, **kw)
+    _check_sampled(w, vs, req, rows, z, bound, T, 5, False)
+    _check_consistent(lib, w, vs, T, 5, False)
