@@ -257,7 +257,9 @@ __global__ void __launch_bounds__(WAVES * 64, 1) lm_head_kernel(HeadArgs a) {
         if (r >= a.R) continue;
         float* dst = a.logits + (int64_t)r * a.ld + vcol;
         if (vcol + 3 < a.V) {
-          *reinterpret_cast<f32x4*>(dst) = x;
+          // streaming hint: the walk reads back only a few rows, so the
+          // logits should not displace the weight and hidden tiles in L2
+          __builtin_nontemporal_store(x, reinterpret_cast<f32x4*>(dst));
         } else {
 #pragma unroll
           for (int e = 0; e < 4; ++e)
