@@ -1097,7 +1097,6 @@ hipError_t launch_accept(const LaunchCtx& cx, int R, const int32_t* parents, con
                          void* workspace, int slices_override, const HeadTiles* head) {
   static_assert(sizeof(WalkShared) < 20480, "walk LDS");
   static_assert(kWalkThreads >= kMaxRows && kWalkThreads >= 256, "load_tree: a thread per row and table entry");
-  const int nseg = segs_for(vocab);
   AcceptWs ws = accept_ws(workspace, R, cx.B, vocab);
   const int nch = ws.nch;
   const bool greedy = temperature == 0.0f;
