@@ -176,6 +176,10 @@ __global__ void __launch_bounds__(WAVES * 64, 1) lm_head_kernel(HeadArgs a) {
     }
   };
 
+  // A wave whose rows all lie past the last tree row (the ragged last row
+  // tile) loads its share and meets every barrier but skips the multiplies;
+  // its SIMD then runs only the other wave's MFMAs.
+  const bool active = r0 + wr * JT * 32 < a.R;
   const int nk = a.H / BK;
   issue(st0, 0);
   if (STAGES > 2 && nk > 1) issue(st1, BK);
@@ -196,7 +200,7 @@ __global__ void __launch_bounds__(WAVES * 64, 1) lm_head_kernel(HeadArgs a) {
       __builtin_amdgcn_s_waitcnt(HEAD_VMCNT(0));                                                  \
     __builtin_amdgcn_s_barrier();                                                                 \
     if ((KT) + STAGES - 1 < nk) issue(NXT, ((KT) + STAGES - 1) * BK);                             \
-    compute(CUR);                                                                                 \
+    if (active) compute(CUR);                                                                     \
     __builtin_amdgcn_s_waitcnt(HEAD_LGKMCNT0);                                                    \
   }
   static_assert(STAGES >= 2 && STAGES <= 4, "ring depth");
