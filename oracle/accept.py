@@ -55,12 +55,28 @@ Readings taken where the pages are silent or garbled:
    R(x) = 0 and is never accepted.
 
 Decisions whose outcome is within rounding of its threshold are reported as
-flagged: |r - R(x)/Q_u(x)| < FLAG_EPS (1e-6) for a child test, and a sampling
-target within FLAG_EPS_DRAW * Z (1e-9) of a cumulative boundary.  The draw
-window is narrower because a vocabulary of 128256 entries puts that many
-cumulative boundaries in [0, Z]: a 1e-6 window would flag about a quarter of
-all draws, while a float64 evaluation (as the GPU library does) places the
-boundaries within about 1e-11 * Z.
+flagged (windows of reading 11 below):
+
+* a child test: |r - R(x)/Q_u(x)| < FLAG_EPS (1e-6), and every child test
+  on a probability in (0, TINY), TINY = 1e-300: a float64 exponential may
+  flush values below e^-708 (3.3e-308) to zero.  A test on R(x) = Q_u(x) = 0
+  (both below e^-745 here, so zero anywhere) rejects for every coin and is
+  not flagged, nor is Q_u(x) = 0 with R(x) >= TINY (accepts for every coin);
+* a draw: the target r * Z within FLAG_EPS_DRAW * Z (1e-9) of a cumulative
+  boundary.  This window is narrower because a vocabulary of 128256 entries
+  puts that many boundaries in [0, Z]: a 1e-6 window would flag about a
+  quarter of all draws, while a float64 evaluation places the boundaries
+  within about 1e-11 * Z;
+* a residual after a rejection: a mass Z with 0 < Z < FLAG_EPS_RES (1e-8).
+  Renormalising by such a Z multiplies the ~1e-15 absolute rounding of the
+  mass into a relative error above 1e-7 in every later test.  A mass of
+  exactly 0 is not flagged: it arises only where R <= Q_u entry by entry,
+  i.e. where both are the same distribution computed from the same logits,
+  which any evaluation reproduces exactly (reading 2 keeps R and raises the
+  zero-residual flag).
+
+11. Parity compares a walk only up to its first flagged decision: the
+    decisions before it fix the accepted prefix of the path and its tokens.
 """
 from __future__ import annotations
 
@@ -71,6 +87,8 @@ from .tree import validate
 
 FLAG_EPS = 1e-6
 FLAG_EPS_DRAW = 1e-9
+FLAG_EPS_RES = 1e-8
+TINY = 1e-300
 
 
 def softmax(x: np.ndarray) -> np.ndarray:
@@ -111,6 +129,17 @@ def sample_inverse_cdf(w: np.ndarray, r: float):
     return t, margin
 
 
+def accept_margin(r: float, Rx: float, Qx: float) -> float:
+    """Distance of child test r * Q(x) < R(x) from its threshold, in coin
+    units (|r - R(x)/Q(x)|); 0 for a test on a probability in (0, TINY),
+    infinity for a test whose outcome no coin can change."""
+    if 0.0 < Rx < TINY or 0.0 < Qx < TINY:
+        return 0.0
+    if Qx == 0.0:
+        return np.inf            # accept iff R(x) > 0, whatever r
+    return abs(r - Rx / Qx)
+
+
 class WalkResult:
     """Outcome of one request's acceptance walk."""
 
@@ -124,12 +153,79 @@ class WalkResult:
     def accept_len(self) -> int:
         return len(self.path) - 1
 
-    def first_flag(self, eps: float = FLAG_EPS, eps_draw: float = FLAG_EPS_DRAW):
-        """Index into ``decisions`` of the first near-threshold decision, or None."""
+    def first_flag(self, eps: float = FLAG_EPS, eps_draw: float = FLAG_EPS_DRAW,
+                   eps_res: float = FLAG_EPS_RES):
+        """Index into ``decisions`` of the first near-threshold decision, or None.
+
+        Kinds and their margins: "accept" (child row, |r - R(x)/Q(x)|),
+        "sample" (node, distance of the target to the nearest cumulative
+        boundary over Z), "residual" (rejected child row, the residual mass Z
+        itself; flagged only when positive and below ``eps_res``)."""
         for i, (kind, _, m) in enumerate(self.decisions):
-            if m < (eps_draw if kind == "sample" else eps):
+            if kind == "residual":
+                if 0.0 < m < eps_res:
+                    return i
+            elif m < (eps_draw if kind == "sample" else eps):
                 return i
         return None
+
+    def prefix_before(self, i):
+        """What the decisions before index ``i`` fix: (path prefix, tokens of
+        that prefix's accepted children, rows rejected by those decisions).
+        ``i = None`` means every decision."""
+        decs = self.decisions if i is None else self.decisions[:i]
+        accepted = [row for kind, row, _ in decs if kind == "accept" and row in self.path]
+        rejected = {row for kind, row, _ in decs if kind == "accept" and row not in self.path}
+        k = len(accepted)
+        assert accepted == self.path[1:1 + k]
+        return self.path[:1 + k], self.tokens[:k], rejected
+
+    def check_outputs(self, accept_len, path_row, tokens_row, flags=None, accept_mask=None,
+                      flag_eps=None, what=""):
+        """Compare another implementation's outputs for this walk (accept_len,
+        the path and tokens rows padded with -1, optionally its flags word and
+        accept mask) with this result, up to the first flagged decision.
+
+        Raises AssertionError on any difference the unflagged decisions fix:
+        the accepted path prefix and its tokens, no continuation through a
+        child those decisions rejected, the zero-residual flag if a zero mass
+        came before the flag.  Without a flagged decision everything must be
+        equal.  Returns (flagged, same): whether a flagged decision exists and
+        whether the whole outputs are equal anyway."""
+        got_path = [int(x) for x in path_row]
+        got_tok = [int(x) for x in tokens_row]
+        S = len(got_path)
+        exp_path = self.path + [-1] * (S - len(self.path))
+        exp_tok = self.tokens + [-1] * (S - len(self.tokens))
+        same = int(accept_len) == self.accept_len and got_path == exp_path and got_tok == exp_tok
+        flag = self.first_flag(*flag_eps) if flag_eps else self.first_flag()
+        if flag is None:
+            assert int(accept_len) == self.accept_len, \
+                f"{what}: accept_len {int(accept_len)} != {self.accept_len}"
+            assert got_path == exp_path, f"{what}: path {got_path} != {exp_path}"
+            assert got_tok == exp_tok, f"{what}: tokens {got_tok} != {exp_tok}"
+            if flags is not None:
+                assert int(flags) == (1 if self.zero_residual else 0), f"{what}: flags {int(flags)}"
+            if accept_mask is not None:
+                m = np.zeros(len(accept_mask), dtype=np.uint8)
+                m[self.path] = 1
+                assert np.array_equal(np.asarray(accept_mask, dtype=np.uint8), m), \
+                    f"{what}: accept mask"
+            return False, True
+        pre_path, pre_tok, rejected = self.prefix_before(flag)
+        k = len(pre_path)
+        assert got_path[:k] == pre_path, \
+            f"{what}: path {got_path} does not start with {pre_path} (fixed before the flag)"
+        assert got_tok[:k - 1] == pre_tok, \
+            f"{what}: tokens {got_tok} do not start with {pre_tok} (fixed before the flag)"
+        assert int(accept_len) >= k - 1, f"{what}: accept_len {int(accept_len)} < {k - 1}"
+        if int(accept_len) >= k:
+            assert got_path[k] not in rejected, \
+                f"{what}: continues through row {got_path[k]}, rejected before the flag"
+        if flags is not None and any(kd == "residual" and m == 0.0
+                                     for kd, _, m in self.decisions[:flag]):
+            assert int(flags) & 1, f"{what}: zero residual before the flag, flags {int(flags)}"
+        return True, same
 
 
 def walk_sampling(parents, tokens, P, Q, coin_accept, coin_sample) -> WalkResult:
@@ -157,11 +253,7 @@ def walk_sampling(parents, tokens, P, Q, coin_accept, coin_sample) -> WalkResult
         for c in kids[u]:
             x = int(tokens[c])
             r = float(coin_accept[c])
-            if Qu[x] > 0:
-                margin = abs(r - R[x] / Qu[x])
-            else:
-                margin = np.inf if R[x] != 0 else 0.0
-            res.decisions.append(("accept", c, margin))
+            res.decisions.append(("accept", c, accept_margin(r, R[x], Qu[x])))
             if r * Qu[x] < R[x]:
                 res.path.append(c)
                 res.tokens.append(x)
@@ -170,11 +262,11 @@ def walk_sampling(parents, tokens, P, Q, coin_accept, coin_sample) -> WalkResult
                 break
             w = np.maximum(0.0, R - Qu)
             Z = float(np.sum(w))
+            res.decisions.append(("residual", c, Z))
             if Z > 0:
                 R = w / Z
-            else:
+            else:                   # R <= Q_u everywhere: keep R, raise the flag
                 res.zero_residual = True
-                res.decisions.append(("residual", c, 0.0))
         if not moved:
             t, m = sample_inverse_cdf(R, coin_sample[u])
             res.decisions.append(("sample", u, m))
@@ -199,7 +291,7 @@ def walk_topk(parents, tokens, P, coin_accept, coin_sample) -> WalkResult:
         for c in kids[u]:
             x = int(tokens[c])
             r = float(coin_accept[c])
-            res.decisions.append(("accept", c, abs(r - R[x])))
+            res.decisions.append(("accept", c, accept_margin(r, R[x], 1.0)))
             if r < R[x]:
                 res.path.append(c)
                 res.tokens.append(x)
@@ -209,11 +301,13 @@ def walk_topk(parents, tokens, P, coin_accept, coin_sample) -> WalkResult:
             w = R.copy()
             w[x] = max(0.0, R[x] - 1.0)
             Z = float(np.sum(w))
-            if Z > 0:
-                R = w / Z
-            else:
-                res.zero_residual = True
-                res.decisions.append(("residual", c, 0.0))
+            res.decisions.append(("residual", c, Z))
+            # Z > 0 always: a rejection needs r >= R(x) with r < 1, so R(x) < 1;
+            # R is normalised, and R(x) = w_x / Z_prev < 1 means another entry
+            # of w was positive, so it still is.  (The zero-residual case of
+            # reading 2 cannot arise for point-mass drafts.)
+            assert Z > 0, "unreachable: a rejected point-mass draft leaves mass elsewhere"
+            R = w / Z
         if not moved:
             t, m = sample_inverse_cdf(R, coin_sample[u])
             res.decisions.append(("sample", u, m))

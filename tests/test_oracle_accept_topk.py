@@ -139,8 +139,7 @@ def _mutant(old, new):
 @pytest.mark.parametrize("old,new", [
     ("            w[x] = max(0.0, R[x] - 1.0)", "            pass"),      # rejected token kept
     ("            if r < R[x]:", "            if r < P[u][x]:"),           # stale target
-    ("            if Z > 0:\n                R = w / Z\n            else:\n                res.zero_residual = True\n"
-     "                res.decisions.append((\"residual\", c, 0.0))\n        if not moved:",
+    ("            R = w / Z\n        if not moved:",
      "            R = w\n        if not moved:"),                          # no renormalisation
 ])
 def test_planted_mistakes_fail_the_chi_square(old, new):
