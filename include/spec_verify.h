@@ -220,6 +220,14 @@ spec_status spec_tree_attn_verify(const spec_batch *batch, const spec_kv *kv,
  *   child_q_d     [R]  Q_parent(c)(token c); NaN at roots; untouched at T = 0 (optional)
  *   flags_d       [B]  SPEC_FLAG_* bits (optional)
  * workspace >= spec_accept_workspace_bytes(batch, vocab) bytes (no init needed).
+ *
+ * At T > 0 a request's walk may be shared by several workgroups that meet
+ * once per vocabulary pass; the library launches only as many as fit on the
+ * device together.  If other work holds the compute units so long that a
+ * meeting does not complete within a bounded wait (about 2^21 polls), that
+ * request comes back with accept_len = -1, path and tokens all -1, an empty
+ * accept mask and SPEC_FLAG_SYNC_TIMEOUT; every kernel still ends.  Any
+ * other request's outputs are complete and exact.
  */
 #define SPEC_FLAG_ZERO_RESIDUAL 1   /* a residual had zero mass; R kept unchanged */
 #define SPEC_FLAG_PATH_TRUNCATED 2  /* path longer than path_stride; walk cut short */
@@ -243,6 +251,24 @@ spec_status spec_accept_sample(const spec_batch *batch, const int32_t *parents_d
                                float temperature, uint64_t seed, uint64_t step,
                                int32_t path_stride, const spec_accept_out *out,
                                void *workspace_d, size_t workspace_bytes, hipStream_t stream);
+
+/* spec_accept_sample with the sampling walk's two launch knobs exposed, for
+ * tests of its cross-workgroup meetings (the outputs do not depend on them
+ * except through SPEC_FLAG_SYNC_TIMEOUT):
+ *   max_slices  > 0: at most this many workgroups share one request's walk
+ *               (0: as many as fit, up to 32)
+ *   max_spins   polls of a meeting's counter before the wait gives up
+ *               (-1: the default of spec_accept_sample; 0 gives up at once
+ *               unless every workgroup of the request has already arrived)
+ * Other arguments, outputs and errors as spec_accept_sample. */
+spec_status spec_accept_sample_walk_knobs(const spec_batch *batch, const int32_t *parents_d,
+                                          const int32_t *tokens_d, const float *p_logits_d,
+                                          const float *q_logits_d, int64_t logits_ld,
+                                          int32_t vocab, float temperature, uint64_t seed,
+                                          uint64_t step, int32_t path_stride,
+                                          const spec_accept_out *out, void *workspace_d,
+                                          size_t workspace_bytes, int32_t max_slices,
+                                          int32_t max_spins, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
  * spec_accept_topk -- acceptance when the children are the drafter's top-k

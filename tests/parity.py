@@ -164,27 +164,18 @@ def check_accept(w, vs, temperature, seed, step, requests=None, max_flagged=1, t
         elif prob_rtol is None:
             assert np.array_equal(got_p, ref_p), f"request {b}: greedy child_p"
         res = r["result"]
-        a = r["accept_len"]
-        S = path.shape[1]
-        exp_path = r["path"] + [-1] * (S - len(r["path"]))
-        exp_tok = r["tokens"] + [-1] * (S - len(r["tokens"]))
-        same = (alen[b] == a and list(path[b]) == exp_path and list(toks[b]) == exp_tok)
-        flag = res.first_flag(*flag_eps) if flag_eps else res.first_flag()
-        if temperature > 0 and flag is not None:
+        is_flagged, same = res.check_outputs(
+            alen[b], path[b], toks[b], flags=flags[b] if temperature > 0 else None,
+            accept_mask=amask[o:e], flag_eps=flag_eps if temperature > 0 else None,
+            what=f"request {b}")
+        if temperature == 0:
+            assert flags[b] == 0, f"request {b}: greedy flags {flags[b]}"
+        if is_flagged:
             flagged += 1
             if not same:
                 flagged_mismatch += 1
                 log(f"[parity] request {b}: differs after a near-threshold decision "
-                    f"(margin {min(m for _, _, m in res.decisions):.2e})")
-            continue
-        assert alen[b] == a, f"request {b}: accept_len {alen[b]} != {a}"
-        assert list(path[b]) == exp_path, f"request {b}: path {list(path[b])} != {exp_path}"
-        assert list(toks[b]) == exp_tok, f"request {b}: tokens {list(toks[b])} != {exp_tok}"
-        m = np.zeros(e - o, dtype=np.uint8)
-        m[r["path"]] = 1
-        assert np.array_equal(amask[o:e], m)
-        expf = 1 if res.zero_residual else 0
-        assert flags[b] == expf, f"request {b}: flags {flags[b]}"
+                    f"(first flagged: {res.decisions[res.first_flag(*(flag_eps or ()))]})")
     log(f"[parity] acceptance: {len(ref)} requests, {flagged} with a near-threshold decision, "
         f"{flagged_mismatch} of those differ")
     assert flagged_mismatch <= max_flagged, f"{flagged_mismatch} flagged requests differ"

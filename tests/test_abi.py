@@ -16,7 +16,8 @@ import pytest
 
 from conftest import ROOT
 
-L = pytest.importorskip("tree_attention_verification_02_amd._lib")
+# No skip: an unbuilt library fails every test here (the binding raises on import).
+import tree_attention_verification_02_amd._lib as L  # noqa: E402
 
 FAKE = 0x1000   # placeholder device address: validation fails before any use
 
@@ -29,7 +30,7 @@ def _declared():
 
 def test_header_declarations_are_all_exported():
     names = _declared()
-    assert "spec_tree_attn_verify" in names and len(names) == 17
+    assert "spec_tree_attn_verify" in names and len(names) == 18
     assert sorted(L.EXPORTS) == names
     lib = ctypes.CDLL(L.LIB_PATH)
     for n in names:
@@ -325,6 +326,57 @@ def test_lm_head_accept_validation():
     assert call(head=L.CLmHead(FAKE, FAKE, 256, None), q=None, T=0.0, ws=0) == 8
     # deterministic children: no draft rows
     assert call(q=None, children=1, ws=0) == 8
+
+
+def test_accept_walk_knobs_validation():
+    """The test entry point with the walk's knobs validates like
+    spec_accept_sample, plus its two knobs."""
+    b = _B([0, 3, 5], [4, 7])
+    out = L.CAcceptOut(FAKE, FAKE, FAKE, None, None, None, None)
+    need = L.LIB.spec_accept_workspace_bytes(ctypes.byref(b.c), 1000)
+
+    def call(slices=0, spins=-1, ws=need, q=FAKE):
+        return L.LIB.spec_accept_sample_walk_knobs(ctypes.byref(b.c), FAKE, FAKE, FAKE, q, 1000,
+                                                   1000, 1.0, 0, 0, 4, ctypes.byref(out), FAKE,
+                                                   ws, slices, spins, None)
+    assert call(slices=-1) == 2 and "max_slices" in _err()
+    assert call(spins=-2) == 2 and "max_spins" in _err()
+    assert call(q=None) == 1 and "q_logits_d" in _err()
+    assert call(ws=need - 1) == 8 and "spec_accept_sample_walk_knobs" not in _err()
+
+
+def test_lm_head_binding_checks_shapes_before_the_call():
+    """The binding rejects operands the library could only see as raw
+    pointers -- wrong dtypes, a transposed weight, too few rows, a row stride
+    that differs from logits_ld, host memory -- before calling it."""
+    import torch
+    b = L.Batch(np.array([0, 3, 5]), np.array([4, 7]), "cpu")
+    V, H = 1000, 256
+    hid = torch.zeros((5, H), dtype=torch.bfloat16)
+    wgt = torch.zeros((V, H), dtype=torch.bfloat16)
+    lg = torch.zeros((5, 1004), dtype=torch.float32)
+    ql = torch.zeros((5, 1004), dtype=torch.float32)
+    out = L.AcceptOut(torch.zeros(2, dtype=torch.int32), torch.zeros((2, 4), dtype=torch.int32),
+                      torch.zeros((2, 4), dtype=torch.int32))
+    ws = torch.zeros(16, dtype=torch.uint8)
+
+    def call(**kw):
+        a = dict(hidden=hid, weight=wgt, q_logits=ql, logits=lg, vocab=V)
+        a.update(kw)
+        with pytest.raises(L.SpecError) as e:
+            L.spec_lm_head_accept(b, None, None, a["hidden"], a["weight"], a["q_logits"],
+                                  a["vocab"], 1.0, 0, 0, out, ws, logits=a["logits"])
+        return e.value.status, str(e.value)
+    assert call(hidden=hid.float())[0] == 5
+    assert call(weight=wgt.float())[0] == 5
+    assert call(weight=torch.zeros((H, V), dtype=torch.bfloat16).t())[0] == 2     # transposed
+    assert call(weight=wgt[:V - 1])[0] == 2                                         # < vocab rows
+    assert call(weight=torch.zeros((V, H + 64), dtype=torch.bfloat16))[0] == 2     # other width
+    assert call(hidden=hid[:4])[0] == 2                                             # < R rows
+    assert call(q_logits=torch.zeros((5, 1008), dtype=torch.float32))[0] == 2      # other stride
+    assert call(logits=torch.zeros((5, 999), dtype=torch.float32))[0] == 2         # < vocab cols
+    status, msg = call()
+    assert status == 1 and "device memory" in msg
 
 
 def test_header_is_plain_c_and_links(tmp_path):

@@ -31,6 +31,7 @@ STATUS_NAMES = {0: "SPEC_OK", 1: "SPEC_ERR_NULL", 2: "SPEC_ERR_SHAPE", 3: "SPEC_
 
 EXPORTS = ["spec_tree_build_mask", "spec_kv_append", "spec_tree_attn_workspace_bytes",
            "spec_tree_attn_verify", "spec_accept_workspace_bytes", "spec_accept_sample",
+           "spec_accept_sample_walk_knobs",
            "spec_accept_topk", "spec_kv_commit", "spec_draft_begin", "spec_draft_expand",
            "spec_draft_select_workspace_bytes", "spec_draft_select", "spec_lm_head_accept_workspace_bytes",
            "spec_lm_head_accept", "spec_status_string", "spec_last_error", "spec_abi_version"]
@@ -94,6 +95,9 @@ def _load():
         "spec_accept_workspace_bytes": ([P(CBatch), i32], sz),
         "spec_accept_sample": ([P(CBatch), vp, vp, vp, vp, i64, i32, f32, u64, u64, i32,
                                 P(CAcceptOut), vp, sz, vp], ctypes.c_int),
+        "spec_accept_sample_walk_knobs": ([P(CBatch), vp, vp, vp, vp, i64, i32, f32, u64, u64,
+                                           i32, P(CAcceptOut), vp, sz, i32, i32, vp],
+                                          ctypes.c_int),
         "spec_accept_topk": ([P(CBatch), vp, vp, vp, i64, i32, f32, u64, u64, i32,
                               P(CAcceptOut), vp, sz, vp], ctypes.c_int),
         "spec_kv_commit": ([P(CBatch), P(CKv), vp, vp, i32, vp, vp, vp], ctypes.c_int),
@@ -138,6 +142,25 @@ def _stream(stream):
 def _check(status):
     if status != SPEC_OK:
         raise SpecError(status, LIB.spec_last_error().decode())
+
+
+def _need(cond, status, msg):
+    if not cond:
+        raise SpecError(status, msg)
+
+
+def _shaped(t, name, dtype, rows=None, cols=None, row_contiguous=True):
+    """Checks the binding can make without the library: a 2-D tensor of the
+    given dtype, at least `rows` x `cols`, unit stride along its last axis
+    (rows may be padded)."""
+    _need(isinstance(t, torch.Tensor), 1, f"{name} must be a tensor")
+    _need(t.dtype == dtype, 5, f"{name} must be {dtype}, not {t.dtype}")
+    _need(t.dim() == 2, 2, f"{name} must be 2-D, not {tuple(t.shape)}")
+    _need(not row_contiguous or t.stride(1) == 1, 2, f"{name} rows must be contiguous")
+    if rows is not None:
+        _need(t.shape[0] >= rows, 2, f"{name} has {t.shape[0]} rows < {rows}")
+    if cols is not None:
+        _need(t.shape[1] >= cols, 2, f"{name} has {t.shape[1]} columns < {cols}")
 
 
 def _dtype_code(dt):
@@ -251,6 +274,21 @@ def spec_accept_sample(batch, parents, tokens, p_logits, q_logits, vocab, temper
                                   ctypes.byref(out.c), _ptr(workspace), ws_bytes, _stream(stream)))
 
 
+def spec_accept_sample_walk_knobs(batch, parents, tokens, p_logits, q_logits, vocab, temperature,
+                                  seed, step, out, workspace, max_slices=0, max_spins=-1,
+                                  logits_ld=None, stream=None):
+    """spec_accept_sample with the walk's workgroups per request and barrier
+    polls set by the caller (tests of the walk's meetings)."""
+    if logits_ld is None:
+        logits_ld = p_logits.stride(0)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(LIB.spec_accept_sample_walk_knobs(
+        ctypes.byref(batch.c), _ptr(parents), _ptr(tokens), _ptr(p_logits), _ptr(q_logits),
+        int(logits_ld), int(vocab), float(temperature), int(seed), int(step), out.path_stride,
+        ctypes.byref(out.c), _ptr(workspace), ws_bytes, int(max_slices), int(max_spins),
+        _stream(stream)))
+
+
 def spec_accept_topk(batch, parents, tokens, p_logits, vocab, temperature, seed, step, out,
                      workspace, logits_ld=None, stream=None):
     if logits_ld is None:
@@ -273,10 +311,27 @@ def spec_lm_head_accept(batch, parents, tokens, hidden, weight, q_logits, vocab,
                         seed, step, out, workspace, logits=None, children=SPEC_CHILDREN_SAMPLED,
                         logits_ld=None, stream=None):
     """hidden [R][H] and weight [V][H] bf16; logits [R][ld] fp32 output (None
-    allowed at temperature 0); q_logits as spec_accept_sample."""
+    allowed at temperature 0); q_logits as spec_accept_sample.  The shapes the
+    library cannot see through raw pointers are checked here first."""
+    R = batch.R
+    _shaped(hidden, "hidden", torch.bfloat16, rows=R)
+    H = int(hidden.shape[1])
+    _need(hidden.is_contiguous(), 2, "hidden must be contiguous [R][H]")
+    _shaped(weight, "weight", torch.bfloat16, rows=int(vocab), cols=H)
+    _need(weight.is_contiguous() and int(weight.shape[1]) == H, 2,
+          f"weight must be contiguous [V][{H}], not {tuple(weight.shape)}")
     if logits_ld is None:
         ref = logits if logits is not None else q_logits
         logits_ld = ref.stride(0) if ref is not None else ((int(vocab) + 3) // 4) * 4
+    named = [("hidden", hidden), ("weight", weight)]
+    for name, t in (("logits", logits), ("q_logits", q_logits)):
+        if t is not None:
+            _shaped(t, name, torch.float32, rows=R, cols=int(vocab))
+            _need(t.stride(0) == int(logits_ld), 2,
+                  f"{name} row stride {t.stride(0)} differs from logits_ld {int(logits_ld)}")
+            named.append((name, t))
+    for name, t in named:
+        _need(t.is_cuda, 1, f"{name} must be in device memory")
     head = CLmHead(_ptr(hidden), _ptr(weight), int(hidden.shape[1]), _ptr(logits))
     ws_bytes = workspace.numel() * workspace.element_size()
     _check(LIB.spec_lm_head_accept(ctypes.byref(batch.c), _ptr(parents), _ptr(tokens),

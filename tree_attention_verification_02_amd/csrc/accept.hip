@@ -62,7 +62,7 @@ constexpr int kPassChunk = 64;                // segments per partial-sum flush
 constexpr int kMaxSlices = 32;                // more pollers per counter cost more than they save
 constexpr int kMaxDevices = 64;
 constexpr int kSyncStride = 64;               // ints between barrier counters (own 256 B each)
-constexpr int kMaxSpins = 1 << 21;
+constexpr int kWalkMaxSpins = 1 << 21;       // barrier polls before a walk gives up
 
 // ---------------------------------------------------------------------------
 // Workspace.
@@ -400,12 +400,16 @@ SPEC_DEVICE double wave_incl_scan(double v, int lane) {
 }
 
 // Per-request barrier of the S workgroups.  The data exchanged across
-// workgroups (segment sums) is written with agent-scope
-// atomic stores and read with agent-scope atomic loads, both coherent at the
-// device level, so no L2 writeback/invalidate is needed: each thread waits
-// for its own stores to complete, then thread 0 arrives on the counter and
-// waits (bounded) for S * pass arrivals.
-SPEC_DEVICE void slice_barrier(WalkShared& sh, int* ctr, int target, int S) {
+// workgroups (segment sums) is written with agent-scope atomic stores and
+// read with agent-scope atomic loads.  Each thread's stores complete before
+// the workgroup meets; thread 0 then arrives on the counter with a release
+// add, waits (bounded: `max_spins` polls) for S * pass arrivals, and an
+// acquire fence after the last poll orders every sum published before those
+// arrivals before this workgroup's reads of them.  A wait that gives up sets
+// sh.timeout: the walk then ends for this workgroup, and the request reports
+// the timeout unless slice 0 passed every barrier (slice 0 alone writes the
+// outputs, so they are then complete).
+SPEC_DEVICE void slice_barrier(WalkShared& sh, int* ctr, int target, int S, int max_spins) {
   if (S == 1) {                 // nothing crosses workgroups
     __syncthreads();
     return;
@@ -413,15 +417,16 @@ SPEC_DEVICE void slice_barrier(WalkShared& sh, int* ctr, int target, int S) {
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (threadIdx.x == 0) {
-    __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
     int spins = 0;
     while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
-      __builtin_amdgcn_s_sleep(2);
-      if (++spins > kMaxSpins) {
+      if (++spins > max_spins) {
         sh.timeout = 1;
         break;
       }
+      __builtin_amdgcn_s_sleep(2);
     }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   }
   __syncthreads();
 }
@@ -443,7 +448,7 @@ struct WalkCtx {
   const float* p;     // target row of the current node
   const float* q;     // draft row of the current node
   double invT, lse_p, lse_q;
-  int vocab, nseg, seg_lo, seg_hi, slice, S;
+  int vocab, nseg, seg_lo, seg_hi, slice, S, max_spins;
   double* seg;        // this request's [2][nseg]
   const int* rej;     // tokens whose weight is 0 (LDS), nrej of them
   int nrej;
@@ -537,7 +542,7 @@ SPEC_DEVICE double walk_pass(WalkShared& sh, const WalkCtx& c, int* ctr, int pas
     pass_segments<true>(sh, c, seg, t);
   else
     pass_segments<false>(sh, c, seg, t);
-  slice_barrier(sh, ctr, pass * c.S, c.S);
+  slice_barrier(sh, ctr, pass * c.S, c.S, c.max_spins);
   if (wave == 0) {
     const int per = (c.nseg + 63) / 64;
     double part = 0.0;
@@ -553,8 +558,9 @@ SPEC_DEVICE double walk_pass(WalkShared& sh, const WalkCtx& c, int* ctr, int pas
   return sh.total;
 }
 
-// Inverse-CDF draw from the weights of pass `pass` with coin r.  Returns the
-// token if this workgroup determined it, else -1 (another slice owns it).
+// Inverse-CDF draw from the weights of pass `pass` with coin r: every slice
+// finds the segment from the published sums; slice 0 rescans it and returns
+// the token (other slices return -1).
 SPEC_DEVICE int walk_draw(WalkShared& sh, const WalkCtx& c, int pass, double t, bool need_q,
                           double r) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -606,7 +612,7 @@ SPEC_DEVICE int walk_draw(WalkShared& sh, const WalkCtx& c, int pass, double t, 
   __syncthreads();
   const int fs = sh.found_seg;
   if (fs < 0) return -1;                             // no positive weight (not reached)
-  if (fs < c.seg_lo || fs >= c.seg_hi) return -1;
+  if (c.slice != 0) return -1;
   // rescan the segment with the same arithmetic as the pass
   const int y0 = fs * kSeg + 4 * tid;
   const int ex = need_q ? 0 : excluded4(c, y0);
@@ -757,7 +763,9 @@ SPEC_DEVICE void write_outputs(WalkShared& sh, const WalkOut& w, int b, int o, i
   }
 }
 
-SPEC_DEVICE void write_bad_tree(const WalkOut& w, int b, int o, int n) {
+// A request without a result (invalid tree, or a walk barrier that gave
+// up): accept_len -1, path and tokens -1, empty accept mask, the flags given.
+SPEC_DEVICE void write_abandoned(const WalkOut& w, int b, int o, int n, int flags) {
   const int tid = threadIdx.x;
   for (int k = tid; k < w.path_stride; k += blockDim.x) {
     w.path[(int64_t)b * w.path_stride + k] = -1;
@@ -767,7 +775,7 @@ SPEC_DEVICE void write_bad_tree(const WalkOut& w, int b, int o, int n) {
     for (int i = tid; i < n; i += blockDim.x) w.accept_mask[o + i] = 0;
   if (tid == 0) {
     w.accept_len[b] = -1;
-    if (w.flags) w.flags[b] = kFlagBadTree;
+    if (w.flags) w.flags[b] = flags;
   }
 }
 
@@ -861,7 +869,7 @@ accept_walk_kernel(const int32_t* __restrict__ row_offsets, int R, int S,
                    const int32_t* __restrict__ parents, const int32_t* __restrict__ tokens,
                    const float* __restrict__ p_logits, const float* __restrict__ q_logits,
                    int64_t ld, int vocab, float temperature, uint64_t seed, uint64_t step,
-                   AcceptWs ws, WalkOut out) {
+                   AcceptWs ws, WalkOut out, int max_spins) {
   __shared__ WalkShared sh;
   __shared__ WalkState st;
   // (request, slice) by ticket, in the order the workgroups start running:
@@ -928,7 +936,7 @@ accept_walk_kernel(const int32_t* __restrict__ row_offsets, int R, int S,
   }
   __syncthreads();
   if (sh.bad) {
-    if (slice == 0) write_bad_tree(out, b, o, n);
+    if (slice == 0) write_abandoned(out, b, o, n, kFlagBadTree);
     return;
   }
   WalkCtx c;
@@ -940,6 +948,7 @@ accept_walk_kernel(const int32_t* __restrict__ row_offsets, int R, int S,
   c.seg_hi = min(c.nseg, c.seg_lo + per);
   c.slice = slice;
   c.S = S;
+  c.max_spins = max_spins;
   c.seg = ws.seg + (size_t)b * 2 * c.nseg;
   int* ctr = ws.sync + (int64_t)(b + 1) * kSyncStride;
   if (tid == 0) {
@@ -956,7 +965,6 @@ accept_walk_kernel(const int32_t* __restrict__ row_offsets, int R, int S,
   }
   int pass = 0;
   int final_token = -1;
-  bool final_here = false;
   while (true) {
     if (tid == 0)
       walk_decide(sh, st, seed, step, b, out.path_stride, topk);
@@ -995,24 +1003,20 @@ accept_walk_kernel(const int32_t* __restrict__ row_offsets, int R, int S,
     const double dt = (action == 2) ? st.pass_t : act_t;
     const bool dq = (action == 2) ? true : act_q;
     final_token = walk_draw(sh, c, pass, dt, dq, r);
-    final_here = final_token >= 0;
     break;
   }
+  // Only slice 0 writes: it passed every barrier of the walk (then every sum
+  // it read was complete, whatever the other slices did afterwards) or it
+  // gave up at one (then the request reports the timeout).
+  if (slice != 0) return;
   __syncthreads();
   if (sh.timeout) {
-    if (slice == 0 && tid == 0) {
-      sh.flags |= kFlagSyncTimeout;
-      out.accept_len[b] = -1;
-      if (out.flags) out.flags[b] = sh.flags;
-    }
+    write_abandoned(out, b, o, n, sh.flags | kFlagSyncTimeout);
     return;
   }
-  const bool has_final = !(sh.flags & kFlagPathTruncated);
-  if (tid == 0 && has_final) sh.ntok += 1;       // the final token's slot
+  if (tid == 0 && !(sh.flags & kFlagPathTruncated)) sh.toks[sh.ntok++] = final_token;
   __syncthreads();
-  if (slice == 0) write_outputs(sh, out, b, o, n, has_final ? sh.ntok - 1 : -1);
-  if (has_final && final_here && tid == 0)
-    out.tokens_out[(int64_t)b * out.path_stride + sh.ntok - 1] = final_token;
+  write_outputs(sh, out, b, o, n, -1);
 }
 
 // Greedy (temperature 0): one workgroup per request, decisions by thread 0.
@@ -1025,7 +1029,7 @@ accept_greedy_kernel(const int32_t* __restrict__ row_offsets, const int32_t* __r
   const int n = row_offsets[b + 1] - o;
   load_tree(sh, parents, tokens, o, n);
   if (sh.bad) {
-    write_bad_tree(out, b, o, n);
+    write_abandoned(out, b, o, n, kFlagBadTree);
     return;
   }
   if (threadIdx.x == 0) {
@@ -1094,7 +1098,7 @@ hipError_t launch_accept(const LaunchCtx& cx, int R, const int32_t* parents, con
                          float temperature, uint64_t seed, uint64_t step, int path_stride,
                          int32_t* accept_len, int32_t* path, int32_t* tokens_out,
                          uint8_t* accept_mask, float* child_p, float* child_q, int32_t* flags,
-                         void* workspace, int slices_override, const HeadTiles* head) {
+                         void* workspace, WalkKnobs walk, const HeadTiles* head) {
   static_assert(sizeof(WalkShared) < 20480, "walk LDS");
   static_assert(kWalkThreads >= kMaxRows && kWalkThreads >= 256, "load_tree: a thread per row and table entry");
   AcceptWs ws = accept_ws(workspace, R, cx.B, vocab);
@@ -1132,11 +1136,12 @@ hipError_t launch_accept(const LaunchCtx& cx, int R, const int32_t* parents, con
   int capacity = 0;
   if ((e = walk_capacity(dev, &capacity)) != hipSuccess) return e;
   int S = walk_slices(cx.B, vocab, capacity);
-  if (slices_override > 0) S = slices_override < S ? slices_override : S;
+  if (walk.max_slices > 0) S = walk.max_slices < S ? walk.max_slices : S;
+  const int max_spins = walk.max_spins >= 0 ? walk.max_spins : kWalkMaxSpins;
   // S > 1: B * S <= capacity workgroups, which take tickets (see the kernel).
   hipLaunchKernelGGL(accept_walk_kernel, dim3(cx.B * S), dim3(kWalkThreads), 0, cx.stream,
                      cx.row_offsets_d, R, S, parents, tokens, p_logits, q_logits, ld, vocab,
-                     temperature, seed, step, ws, out);
+                     temperature, seed, step, ws, out, max_spins);
   return hipGetLastError();
 }
 

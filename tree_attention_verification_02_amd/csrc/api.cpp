@@ -122,13 +122,6 @@ spec_status launched(hipError_t e, const char* what) {
 
 int esize(spec_dtype d) { return d == SPEC_BF16 ? 2 : 4; }
 
-// Test hook: SPEC_WALK_SLICES=<n> caps the workgroups per request of the
-// sampling walk (default: as many as fit, up to 32).
-int walk_slices_override() {
-  const char* v = getenv("SPEC_WALK_SLICES");
-  return v ? atoi(v) : 0;
-}
-
 }  // namespace
 
 extern "C" {
@@ -246,7 +239,8 @@ static spec_status accept_call(const spec_batch* batch, const int32_t* parents_d
                                const float* q_logits_d, bool topk, int64_t logits_ld,
                                int32_t vocab, float temperature, uint64_t seed, uint64_t step,
                                int32_t path_stride, const spec_accept_out* out, void* workspace_d,
-                               size_t workspace_bytes, hipStream_t stream, const char* name) {
+                               size_t workspace_bytes, hipStream_t stream, const char* name,
+                               spec::WalkKnobs knobs = spec::WalkKnobs()) {
   int R = 0;
   spec_status st = check_batch(batch, &R);
   if (st != SPEC_OK) return st;
@@ -269,7 +263,7 @@ static spec_status accept_call(const spec_batch* batch, const int32_t* parents_d
                                       logits_ld, vocab, temperature, seed, step, path_stride,
                                       out->accept_len_d, out->path_d, out->tokens_d,
                                       out->accept_mask_d, out->child_p_d, out->child_q_d,
-                                      out->flags_d, workspace_d, walk_slices_override()),
+                                      out->flags_d, workspace_d, knobs),
                   name);
 }
 
@@ -281,6 +275,24 @@ spec_status spec_accept_sample(const spec_batch* batch, const int32_t* parents_d
   return accept_call(batch, parents_d, tokens_d, p_logits_d, q_logits_d, false, logits_ld, vocab,
                      temperature, seed, step, path_stride, out, workspace_d, workspace_bytes, stream,
                      "spec_accept_sample");
+}
+
+spec_status spec_accept_sample_walk_knobs(const spec_batch* batch, const int32_t* parents_d,
+                                          const int32_t* tokens_d, const float* p_logits_d,
+                                          const float* q_logits_d, int64_t logits_ld,
+                                          int32_t vocab, float temperature, uint64_t seed,
+                                          uint64_t step, int32_t path_stride,
+                                          const spec_accept_out* out, void* workspace_d,
+                                          size_t workspace_bytes, int32_t max_slices,
+                                          int32_t max_spins, hipStream_t stream) {
+  if (max_slices < 0) return fail(SPEC_ERR_SHAPE, "max_slices = %d, need >= 0", max_slices);
+  if (max_spins < -1) return fail(SPEC_ERR_SHAPE, "max_spins = %d, need >= -1", max_spins);
+  spec::WalkKnobs k;
+  k.max_slices = max_slices;
+  k.max_spins = max_spins;
+  return accept_call(batch, parents_d, tokens_d, p_logits_d, q_logits_d, false, logits_ld, vocab,
+                     temperature, seed, step, path_stride, out, workspace_d, workspace_bytes, stream,
+                     "spec_accept_sample_walk_knobs", k);
 }
 
 spec_status spec_accept_topk(const spec_batch* batch, const int32_t* parents_d, const int32_t* tokens_d,
@@ -347,7 +359,7 @@ spec_status spec_lm_head_accept(const spec_batch* batch, const int32_t* parents_
                                       logits_ld, vocab, temperature, seed, step, path_stride,
                                       out->accept_len_d, out->path_d, out->tokens_d,
                                       out->accept_mask_d, out->child_p_d, out->child_q_d,
-                                      out->flags_d, workspace_d, walk_slices_override(), &tiles),
+                                      out->flags_d, workspace_d, spec::WalkKnobs(), &tiles),
                   "spec_lm_head_accept");
 }
 

@@ -84,14 +84,21 @@ hipError_t launch_lm_head(int R, const uint16_t* hidden, int H, const uint16_t* 
 // children (each child a point-mass draft; no draft rows are read).  With
 // `head`, the target rows' statistics come from the LM head's tile partials
 // (merged here) instead of a pass over p_logits; p_logits may then be null at
-// temperature 0.
+// temperature 0.  `walk` caps the sampling walk's workgroups per request
+// (max_slices > 0) and the polls of its barrier wait (max_spins >= 0); the
+// defaults are as many slices as fit and kWalkMaxSpins.
+struct WalkKnobs {
+  int max_slices = 0;
+  int max_spins = -1;
+};
 size_t accept_workspace_bytes(int R, int B, int vocab);
 hipError_t launch_accept(const LaunchCtx& cx, int R, const int32_t* parents, const int32_t* tokens,
                          const float* p_logits, const float* q_logits, int64_t ld, int vocab,
                          float temperature, uint64_t seed, uint64_t step, int path_stride,
                          int32_t* accept_len, int32_t* path, int32_t* tokens_out,
                          uint8_t* accept_mask, float* child_p, float* child_q, int32_t* flags,
-                         void* workspace, int slices_override, const HeadTiles* head = nullptr);
+                         void* workspace, WalkKnobs walk = WalkKnobs(),
+                         const HeadTiles* head = nullptr);
 
 // Dynamic draft trees (EAGLE-2 rounds, global row budget).
 constexpr int kDraftMaxK = 16;          // children per expanded node, nodes expanded per round
