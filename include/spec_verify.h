@@ -252,6 +252,26 @@ spec_status spec_accept_sample(const spec_batch *batch, const int32_t *parents_d
                                int32_t path_stride, const spec_accept_out *out,
                                void *workspace_d, size_t workspace_bytes, hipStream_t stream);
 
+/* spec_accept_sample_noalloc -- for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): spec_accept_sample without a workspace argument.  Its
+ * scratch is a device array inside the library, SPEC_ACCEPT_SCRATCH_BYTES
+ * (8 MiB) per GPU, held by each GPU the library runs on until the process
+ * ends; the call allocates nothing.  A batch whose
+ * spec_accept_workspace_bytes exceeds that size is refused with
+ * SPEC_ERR_WORKSPACE (e.g. 1024 rows over a 128256-entry vocabulary need
+ * about 0.5 MiB).  Every call on one GPU shares that GPU's array: calls that
+ * overlap on one GPU (two streams, two host threads) race and must be
+ * serialised by the caller.  Other arguments, outputs and errors as
+ * spec_accept_sample; the outputs are the same bits. */
+#define SPEC_ACCEPT_SCRATCH_BYTES (8u << 20)
+spec_status spec_accept_sample_noalloc(const spec_batch *batch, const int32_t *parents_d,
+                                       const int32_t *tokens_d, const float *p_logits_d,
+                                       const float *q_logits_d, int64_t logits_ld,
+                                       int32_t vocab, float temperature, uint64_t seed,
+                                       uint64_t step, int32_t path_stride,
+                                       const spec_accept_out *out, hipStream_t stream);
+
 /* spec_accept_sample with the sampling walk's two launch knobs exposed, for
  * tests of its cross-workgroup meetings (the outputs do not depend on them
  * except through SPEC_FLAG_SYNC_TIMEOUT):

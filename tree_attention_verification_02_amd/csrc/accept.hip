@@ -43,6 +43,7 @@
 #include <math.h>
 
 #include <atomic>
+#include <mutex>
 
 #include "common.hpp"
 #include "exp64.hpp"
@@ -1058,6 +1059,38 @@ accept_greedy_kernel(const int32_t* __restrict__ row_offsets, const int32_t* __r
   }
   __syncthreads();
   write_outputs(sh, out, b, o, n, -1);
+}
+
+// Workspace of the no-allocation acceptance entry point: a file-scope device
+// array (each GPU the library runs on holds its own copy until the process
+// ends).  Host code never uses the array's name as an address: its device
+// address is looked up once per device with hipGetSymbolAddress, with that
+// device current, and kept.  Every call on a device shares its copy; the
+// statistics kernel clears the counters that must start at zero, and every
+// other byte is written before it is read, so stale contents do not matter,
+// but calls that overlap on one device race.
+static __device__ __align__(256) unsigned char scratch[kAcceptScratchBytes];
+
+hipError_t accept_scratch(void** ptr) {
+  static std::atomic<void*> addr[kMaxDevices];
+  static std::mutex lock;
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void* p = addr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> g(lock);
+    p = addr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return e;
+      if (!p) return hipErrorInvalidSymbol;
+      addr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *ptr = p;
+  return hipSuccess;
 }
 
 // Walk workgroups that fit on device `dev` at once (CUs x occupancy),

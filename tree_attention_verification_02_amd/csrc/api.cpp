@@ -18,6 +18,7 @@ static_assert(SPEC_FLAG_ZERO_RESIDUAL == spec::kFlagZeroResidual, "flag");
 static_assert(SPEC_FLAG_PATH_TRUNCATED == spec::kFlagPathTruncated, "flag");
 static_assert(SPEC_FLAG_BAD_TREE == spec::kFlagBadTree, "flag");
 static_assert(SPEC_FLAG_SYNC_TIMEOUT == spec::kFlagSyncTimeout, "flag");
+static_assert(SPEC_ACCEPT_SCRATCH_BYTES == spec::kAcceptScratchBytes, "scratch size");
 static_assert(SPEC_DRAFT_FLAG_CAPACITY == spec::kDraftFlagCapacity, "flag");
 static_assert(SPEC_DRAFT_FLAG_BAD_STATE == spec::kDraftFlagBadState, "flag");
 
@@ -240,7 +241,8 @@ static spec_status accept_call(const spec_batch* batch, const int32_t* parents_d
                                int32_t vocab, float temperature, uint64_t seed, uint64_t step,
                                int32_t path_stride, const spec_accept_out* out, void* workspace_d,
                                size_t workspace_bytes, hipStream_t stream, const char* name,
-                               spec::WalkKnobs knobs = spec::WalkKnobs()) {
+                               spec::WalkKnobs knobs = spec::WalkKnobs(),
+                               bool use_scratch = false) {
   int R = 0;
   spec_status st = check_batch(batch, &R);
   if (st != SPEC_OK) return st;
@@ -255,6 +257,18 @@ static spec_status accept_call(const spec_batch* batch, const int32_t* parents_d
   if (!out || !out->accept_len_d || !out->path_d || !out->tokens_d)
     return fail(SPEC_ERR_NULL, "out, accept_len_d, path_d and tokens_d are required");
   const size_t need = spec::accept_workspace_bytes(R, batch->batch, vocab);
+  if (use_scratch) {
+    // the library's own device array instead of a caller workspace
+    if (need > spec::kAcceptScratchBytes)
+      return fail(SPEC_ERR_WORKSPACE,
+                  "%s: this batch needs %zu bytes of scratch, more than the %zu it holds "
+                  "(spec_accept_sample takes a caller workspace of any size)",
+                  name, need, spec::kAcceptScratchBytes);
+    const hipError_t e = spec::accept_scratch(&workspace_d);
+    if (e != hipSuccess)
+      return fail(SPEC_ERR_HIP, "%s: scratch lookup failed: %s", name, hipGetErrorString(e));
+    workspace_bytes = spec::kAcceptScratchBytes;
+  }
   if (!workspace_d || workspace_bytes < need)
     return fail(SPEC_ERR_WORKSPACE, "accept workspace %zu bytes < required %zu", workspace_bytes, need);
   if (!aligned16(workspace_d)) return fail(SPEC_ERR_SHAPE, "workspace must be 16-byte aligned");
@@ -275,6 +289,17 @@ spec_status spec_accept_sample(const spec_batch* batch, const int32_t* parents_d
   return accept_call(batch, parents_d, tokens_d, p_logits_d, q_logits_d, false, logits_ld, vocab,
                      temperature, seed, step, path_stride, out, workspace_d, workspace_bytes, stream,
                      "spec_accept_sample");
+}
+
+spec_status spec_accept_sample_noalloc(const spec_batch* batch, const int32_t* parents_d,
+                                       const int32_t* tokens_d, const float* p_logits_d,
+                                       const float* q_logits_d, int64_t logits_ld, int32_t vocab,
+                                       float temperature, uint64_t seed, uint64_t step,
+                                       int32_t path_stride, const spec_accept_out* out,
+                                       hipStream_t stream) {
+  return accept_call(batch, parents_d, tokens_d, p_logits_d, q_logits_d, false, logits_ld, vocab,
+                     temperature, seed, step, path_stride, out, nullptr, 0, stream,
+                     "spec_accept_sample_noalloc", spec::WalkKnobs(), /*use_scratch=*/true);
 }
 
 spec_status spec_accept_sample_walk_knobs(const spec_batch* batch, const int32_t* parents_d,

@@ -92,6 +92,10 @@ struct WalkKnobs {
   int max_spins = -1;
 };
 size_t accept_workspace_bytes(int R, int B, int vocab);
+// The no-allocation entry point's workspace: a device array of this many
+// bytes in accept.hip, its address on the current device.
+constexpr size_t kAcceptScratchBytes = (size_t)8 << 20;
+hipError_t accept_scratch(void** ptr);
 hipError_t launch_accept(const LaunchCtx& cx, int R, const int32_t* parents, const int32_t* tokens,
                          const float* p_logits, const float* q_logits, int64_t ld, int vocab,
                          float temperature, uint64_t seed, uint64_t step, int path_stride,
