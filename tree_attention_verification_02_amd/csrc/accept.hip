@@ -62,7 +62,6 @@ constexpr int kPassF = 8;                     // segments per pass round (float4
 constexpr int kPassChunk = 64;                // segments per partial-sum flush
 constexpr int kMaxSlices = 32;                // more pollers per counter cost more than they save
 constexpr int kMaxDevices = 64;
-constexpr int kSyncStride = 64;               // ints between barrier counters (own 256 B each)
 constexpr int kWalkMaxSpins = 1 << 21;       // barrier polls before a walk gives up
 
 // ---------------------------------------------------------------------------
@@ -74,9 +73,9 @@ struct AcceptWs {
   double* part_s;   //                     and sum of exp(z - reference)
   float* part_m;    // [R][nch]    chunk max (greedy)
   int32_t* part_am; //                     and its first index
-  int32_t* sync;    // [B+1][kSyncStride]: [0][0] walk ticket counter, [b+1][0] barrier counter
-                    // of request b (zeroed by accept_stats)
-  double* seg;      // [B][2][nseg] per-pass segment sums (double-buffered)
+  int32_t* sync;    // [64]: [0] the walk's ticket counter (zeroed with seg), own 256 B
+  double* seg;      // [B][2][nseg] per-pass segment sums carrying their pass tag
+                    // (double-buffered by pass parity; zeroed before every walk)
 };
 
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -101,7 +100,7 @@ __host__ __device__ inline AcceptWs accept_ws(void* base, int R, int B, int voca
   w.part_am = (int32_t*)p;
   p += align256((size_t)R * nch * sizeof(int32_t));
   w.sync = (int32_t*)p;
-  p += align256((size_t)(B + 1) * kSyncStride * sizeof(int32_t));
+  p += 256;
   w.seg = (double*)p;
   return w;
 }
@@ -116,8 +115,18 @@ size_t accept_workspace_bytes(int R, int B, int vocab) {
          2 * align256(2 * (size_t)R * nch * sizeof(double)) +
          align256((size_t)R * nch * sizeof(float)) +
          align256((size_t)R * nch * sizeof(int32_t)) +
-         align256((size_t)(B + 1) * kSyncStride * sizeof(int32_t)) +
+         256 +
          align256((size_t)B * 2 * nseg * sizeof(double));
+}
+
+// The walk's exchange area starts every call cleared: its ticket counter at
+// 0 and every segment sum with tag 0, which no pass uses.  Spread over the
+// first blocks of the kernel that runs before the walk.
+SPEC_DEVICE void clear_walk_state(const AcceptWs& ws, int B, int vocab) {
+  const int64_t nseg_all = (int64_t)B * 2 * ((vocab + kSeg - 1) / kSeg);
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < nseg_all) ws.seg[i] = 0.0;
+  if (i == 0) ws.sync[0] = 0;
 }
 
 // ---------------------------------------------------------------------------
@@ -150,8 +159,7 @@ accept_stats_kernel(const int32_t* __restrict__ row_offsets, int B, int R,
   const int r = rr - which * R;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int slot = rr * nch + chunk;
-  if (blockIdx.x == 0)
-    for (int i = tid; i <= B; i += kStatThreads) ws.sync[(int64_t)i * kSyncStride] = 0;
+  clear_walk_state(ws, B, vocab);
   if (!kGreedy) load_exp_table(s_tab);
   if (which == 1) {
     const int b = request_of_row(row_offsets, B, r);
@@ -257,11 +265,10 @@ static_assert(kStatChunkLen % kHeadTileV == 0 && kTilesPerChunk == kWave,
               "a statistics chunk is one wave of head tiles");
 
 __global__ void __launch_bounds__(256)
-accept_head_merge_kernel(int B, int R, HeadTiles t, int greedy, AcceptWs ws) {
+accept_head_merge_kernel(int B, int R, HeadTiles t, int greedy, AcceptWs ws, int vocab) {
   __shared__ double s_tab[256];
   const int tid = threadIdx.x, lane = tid & 63;
-  if (blockIdx.x == 0)
-    for (int i = tid; i <= B; i += 256) ws.sync[(int64_t)i * kSyncStride] = 0;
+  clear_walk_state(ws, B, vocab);
   if (!greedy) load_exp_table(s_tab);
   __syncthreads();
   const int nch = ws.nch;
@@ -400,49 +407,50 @@ SPEC_DEVICE double wave_incl_scan(double v, int lane) {
   return v;
 }
 
-// Per-request barrier of the S workgroups.  The data exchanged across
-// workgroups (segment sums) is written with agent-scope atomic stores and
-// read with agent-scope atomic loads.  Each thread's stores complete before
-// the workgroup meets; thread 0 then arrives on the counter with a release
-// add, waits (bounded: `max_spins` polls) for S * pass arrivals, and an
-// acquire fence after the last poll orders every sum published before those
-// arrivals before this workgroup's reads of them.  A wait that gives up sets
-// sh.timeout: the walk then ends for this workgroup, and the request reports
-// the timeout unless slice 0 passed every barrier (slice 0 alone writes the
-// outputs, so they are then complete).
-SPEC_DEVICE void slice_barrier(WalkShared& sh, int* ctr, int target, int S, int max_spins) {
-  if (S == 1) {                 // nothing crosses workgroups
-    __syncthreads();
-    return;
-  }
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-    int spins = 0;
-    while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
-      if (++spins > max_spins) {
-        sh.timeout = 1;
-        break;
-      }
-      __builtin_amdgcn_s_sleep(2);
-    }
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  }
-  __syncthreads();
-}
+// Exchange of segment sums between the S workgroups of a request.  Each
+// sum is published with a relaxed agent-scope atomic store that carries its
+// pass in the low 8 bits of the mantissa (the value rounded to 44 bits,
+// 2^-45 relative, far inside every near-threshold window), and read with
+// relaxed agent-scope atomic loads polled until the tag is the wanted pass.
+// A read that sees the wanted tag holds that pass's value: the protocol
+// needs no ordering between different locations, hence no fences, no cache
+// writeback or invalidate and no counter.  Tag 0 means cleared (the
+// exchange area is zeroed before every walk); passes cycle through 1..255,
+// and sums live in two buffers by pass parity, so a slot holds the tag of
+// its current pass, of the pass two before, or 0 -- never a stale copy of
+// the wanted tag.  A poll loop that exceeds `max_spins` gives up: the walk
+// ends for that workgroup, and the request reports a timeout unless slice 0
+// read every sum (slice 0 alone writes the outputs, so they are then
+// complete).
+SPEC_DEVICE int pass_tag(int pass) { return (pass - 1) % 255 + 1; }
 
-SPEC_DEVICE void store_shared_d(double* p, double v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+SPEC_DEVICE void publish_sum(double* p, double v, int tag) {
+  const unsigned long long bits =
+      (((unsigned long long)__double_as_longlong(v) + 0x80ull) & ~0xffull) | (unsigned)tag;
+  __hip_atomic_store(reinterpret_cast<unsigned long long*>(p), bits, __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
 }
-SPEC_DEVICE double load_shared_d(const double* p) {
-  return __hip_atomic_load(const_cast<double*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+SPEC_DEVICE double tagged_value(unsigned long long bits) {
+  return __longlong_as_double((long long)(bits & ~0xffull));
 }
-SPEC_DEVICE void store_shared_i(int* p, int v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+SPEC_DEVICE unsigned long long load_tagged(const double* p) {
+  return __hip_atomic_load(reinterpret_cast<unsigned long long*>(const_cast<double*>(p)),
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-SPEC_DEVICE int load_shared_i(const int* p) {
-  return __hip_atomic_load(const_cast<int*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// The value of slot p once it carries `tag`; false if polling gave up.
+SPEC_DEVICE bool read_sum(const double* p, int tag, int max_spins, double& v) {
+  unsigned long long bits = load_tagged(p);
+  int spins = 0;
+  while ((int)(bits & 0xffull) != tag) {
+    if (++spins > max_spins) {
+      v = 0.0;
+      return false;
+    }
+    __builtin_amdgcn_s_sleep(1);
+    bits = load_tagged(p);
+  }
+  v = tagged_value(bits);
+  return true;
 }
 
 struct WalkCtx {
@@ -513,7 +521,7 @@ SPEC_DEVICE void pass_round(WalkShared& sh, const WalkCtx& c, int s0, int base, 
 }
 
 template <bool kQ>
-SPEC_DEVICE void pass_segments(WalkShared& sh, const WalkCtx& c, double* seg, double t) {
+SPEC_DEVICE void pass_segments(WalkShared& sh, const WalkCtx& c, double* seg, double t, int tag) {
   const int tid = threadIdx.x;
   for (int base = c.seg_lo; base < c.seg_hi; base += kPassChunk) {
     const int end = min(c.seg_hi, base + kPassChunk);
@@ -527,30 +535,36 @@ SPEC_DEVICE void pass_segments(WalkShared& sh, const WalkCtx& c, double* seg, do
       double tot = 0.0;
 #pragma unroll
       for (int w = 0; w < kWalkWaves; ++w) tot += sh.part[tid][w];
-      store_shared_d(&seg[base + tid], tot);
+      publish_sum(&seg[base + tid], tot, tag);
     }
     __syncthreads();
   }
 }
 
 // One vocabulary pass: this workgroup's segments of max(0, P - tQ) (or P),
-// then the request barrier, then the ordered total over all segments.
-SPEC_DEVICE double walk_pass(WalkShared& sh, const WalkCtx& c, int* ctr, int pass, double t,
-                             bool need_q) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+// published; then every segment's sum of this pass (waiting for the other
+// slices' as they arrive) and their ordered total.
+SPEC_DEVICE double walk_pass(WalkShared& sh, const WalkCtx& c, int pass, double t, bool need_q) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   double* seg = c.seg + (pass & 1) * c.nseg;
+  const int tag = pass_tag(pass);
   if (need_q)
-    pass_segments<true>(sh, c, seg, t);
+    pass_segments<true>(sh, c, seg, t, tag);
   else
-    pass_segments<false>(sh, c, seg, t);
-  slice_barrier(sh, ctr, pass * c.S, c.S, c.max_spins);
+    pass_segments<false>(sh, c, seg, t, tag);
   if (wave == 0) {
     const int per = (c.nseg + 63) / 64;
     double part = 0.0;
+    bool late = false;
     for (int k = 0; k < per; ++k) {
       const int sidx = lane * per + k;
-      if (sidx < c.nseg) part += load_shared_d(&seg[sidx]);
+      if (sidx < c.nseg) {
+        double v;
+        late |= !read_sum(&seg[sidx], tag, c.max_spins, v);
+        part += v;
+      }
     }
+    if (__any(late) && lane == 0) sh.timeout = 1;
     const double incl = wave_incl_scan(part, lane);
     sh.lane_excl[lane] = incl - part;
     if (lane == 63) sh.total = incl;
@@ -575,7 +589,7 @@ SPEC_DEVICE int walk_draw(WalkShared& sh, const WalkCtx& c, int pass, double t, 
     for (int k = 0; k < per; ++k) {
       const int sidx = lane * per + k;
       if (sidx < c.nseg) {
-        const double v = load_shared_d(&seg[sidx]);
+        const double v = tagged_value(load_tagged(&seg[sidx]));
         const double nxt = cum + v;
         if (hit < 0 && nxt > target) {
           hit = sidx;
@@ -951,7 +965,6 @@ accept_walk_kernel(const int32_t* __restrict__ row_offsets, int R, int S,
   c.S = S;
   c.max_spins = max_spins;
   c.seg = ws.seg + (size_t)b * 2 * c.nseg;
-  int* ctr = ws.sync + (int64_t)(b + 1) * kSyncStride;
   if (tid == 0) {
     sh.len = 1;
     sh.ntok = 0;
@@ -982,7 +995,7 @@ accept_walk_kernel(const int32_t* __restrict__ row_offsets, int R, int S,
     const double act_t = st.act_t;
     const bool act_q = st.act_q != 0;
     if (action != 2) {
-      const double G = walk_pass(sh, c, ctr, ++pass, act_t, act_q);
+      const double G = walk_pass(sh, c, ++pass, act_t, act_q);
       if (sh.timeout) break;
       if (action == 0) {
         if (tid == 0) {
@@ -1143,7 +1156,7 @@ hipError_t launch_accept(const LaunchCtx& cx, int R, const int32_t* parents, con
   const int rows = ((greedy || !q_logits) ? R : 2 * R) - row_base;
   if (head)
     hipLaunchKernelGGL(accept_head_merge_kernel, dim3((R * nch + 3) / 4), dim3(256), 0,
-                       cx.stream, cx.B, R, *head, greedy ? 1 : 0, ws);
+                       cx.stream, cx.B, R, *head, greedy ? 1 : 0, ws, vocab);
   if (rows > 0) {
     if (greedy)
       hipLaunchKernelGGL(accept_stats_kernel<true>, dim3(rows * nch), dim3(kStatThreads), 0,
