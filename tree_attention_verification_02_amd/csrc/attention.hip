@@ -34,8 +34,9 @@ namespace spec {
 
 constexpr int kTileKeys = 64;
 constexpr int kRowsPerWave = 32;
-constexpr int kMaxRowsPerBlock = 8 * kRowsPerWave;
-constexpr int kWaves = 8;                  // waves per bf16 workgroup
+constexpr int kWaves = 8;                  // waves per bf16 workgroup (wide variant: 12)
+constexpr int kWideWaves = 12;
+constexpr int kDmaWaves = 8;               // waves that issue the K/V tile loads
 constexpr int kStages = 4;                 // LDS ring depth (tiles)
 constexpr int kCombineRows = 32;           // query rows per combine workgroup
 constexpr float kLazyMax = 8.0f;           // log2 headroom of the softmax reference
@@ -94,7 +95,7 @@ __host__ __device__ inline int attn_splits(int keys, int split) {
 // split takes about the same time.
 __host__ __device__ inline int attn_split_for(int split, int n, int G, int rpb, int weighted) {
   const int rows = n * G < rpb ? n * G : rpb;
-  if (!weighted || (rows + kRowsPerWave - 1) / kRowsPerWave <= kWaves / 2) return split;
+  if (!weighted || (rows + kRowsPerWave - 1) / kRowsPerWave <= rpb / kRowsPerWave / 2) return split;
   const int s2 = (split * 2 / 3) / kTileKeys * kTileKeys;
   return s2 > kTileKeys ? s2 : kTileKeys;
 }
@@ -207,22 +208,42 @@ SPEC_DEVICE int tile_slot_bytes(int row, int c) {
   return ((c >> 2) * 4 + (row >> 4)) * 1024 + (4 * r16 + ((c & 3) ^ (r16 >> 2))) * 16;
 }
 
-// Issue the direct-to-LDS loads of one 64-key K and V tile; each wave issues
-// PER_WAVE of the tile's 1 KB blocks.  A block is 16 consecutive keys (one
-// paged KV block: the tile start is 64-aligned), so its base address is
-// uniform; lane l writes LDS slot l and loads the global chunk that the
-// layout above puts there.
+// Direct-to-LDS load of 16 bytes per lane from a uniform base plus a 32-bit
+// per-lane byte offset: a raw buffer resource built in scalar registers for
+// the base, so a lane keeps only its offset in a vector register (the same
+// offset for every 16-key block of the whole tile).
+constexpr int kBufferWord3 = 0x00020000;   // raw (untyped) buffer resource, gfx9 family
+SPEC_DEVICE void dma16(gptr_u16 base, int lane_bytes, int scalar_bytes, uint16_t* dst) {
+  // the base is the same in every lane; saying so keeps it in scalar
+  // registers.  readfirstlane returns int: both halves go back through
+  // uint32_t, or a low word with bit 31 set would sign-extend into the high
+  // word.
+  const uint64_t a = (uint64_t)base;
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  const uint64_t u = ((uint64_t)hi << 32) | lo;
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc((void*)u, 0, 0x7fffffff, kBufferWord3);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lptr_void)dst, 16, lane_bytes, scalar_bytes, 0, 0);
+}
+
+// Issue the direct-to-LDS loads of one 64-key K and V tile; each loading
+// wave issues PER_WAVE of the tile's 1 KB blocks.  A block is 16 consecutive
+// keys (one paged KV block: the tile start is 64-aligned), so its base
+// address is uniform; lane l writes LDS slot l and loads the global chunk
+// that the layout above puts there.
 //  * Whole tiles (the common case): the tile's four block ids come from one
 //    16-byte LDS read; per load only a scalar base changes.
 //  * A tile that reaches the split end: keys at or past it read the split's
 //    last key instead (finite data; they are masked out of the softmax), which
 //    keeps every access inside the cache rows the caller owns.
-template <int D>
+template <int D, bool kBufferDma>
 SPEC_DEVICE void issue_tile(uint16_t* ks, uint16_t* vs, gptr_u16 gk, gptr_u16 gv, int t0,
                             int key_end, bool paged, const int* s_blk, int blk0,
                             int64_t blk_stride, int wave, int lane) {
   constexpr int NB = D / 8;                  // 1 KB blocks per K (or V) tile
-  constexpr int PER_WAVE = 2 * NB / kWaves;
+  constexpr int PER_WAVE = 2 * NB / kDmaWaves;
+  if (wave >= kDmaWaves) return;             // wide workgroups: the other waves load nothing
   const int rr = lane >> 2;                  // key row inside the 16-key group
   const int cl = (lane & 3) ^ (lane >> 4);   // chunk inside the 4-chunk group
   const int last = key_end - 1;
@@ -243,7 +264,7 @@ SPEC_DEVICE void issue_tile(uint16_t* ks, uint16_t* vs, gptr_u16 gk, gptr_u16 gv
       b3 = b0 + 3;
       stride = (int64_t)kBlock * D;
     }
-    const int lane_off = rr * D + cl * 8;    // elements inside a block
+    const int lane_bytes = (rr * D + cl * 8) * 2;    // inside a block
 #pragma unroll
     for (int j = 0; j < PER_WAVE; ++j) {
       const int gi = wave * PER_WAVE + j;    // uniform
@@ -251,9 +272,15 @@ SPEC_DEVICE void issue_tile(uint16_t* ks, uint16_t* vs, gptr_u16 gk, gptr_u16 gv
       const int bi = isv ? gi - NB : gi;
       const int grp = bi & 3;
       const int bid = (grp == 0) ? b0 : (grp == 1) ? b1 : (grp == 2) ? b2 : b3;
-      const gptr_u16 base = (isv ? gv : gk) + ((int64_t)bid * stride + (bi >> 2) * 32);
+      // block base by the block id (changes every tile); the chunk group
+      // (bi / 4: 32 elements) as the scalar offset
+      const gptr_u16 bb = (isv ? gv : gk) + (int64_t)bid * stride;
       uint16_t* dst = (isv ? vs : ks) + bi * 512;
-      __builtin_amdgcn_global_load_lds((gptr_void)(base + lane_off), (lptr_void)dst, 16, 0, 0);
+      if (kBufferDma)
+        dma16(bb, lane_bytes, (bi >> 2) * 64, dst);
+      else
+        __builtin_amdgcn_global_load_lds((gptr_void)(bb + (bi >> 2) * 32 + lane_bytes / 2),
+                                         (lptr_void)dst, 16, 0, 0);
     }
     return;
   }
@@ -270,9 +297,12 @@ SPEC_DEVICE void issue_tile(uint16_t* ks, uint16_t* vs, gptr_u16 gk, gptr_u16 gv
               : (int64_t)blk * (kBlock * D);
     const int key = min(t0 + 16 * grp + rr, last);     // same 16-key block as gs
     const int c = (bi >> 2) * 4 + cl;
-    const gptr_u16 src = (isv ? gv : gk) + base + ((key & 15) * D + c * 8);
-    uint16_t* dst = (isv ? vs : ks) + bi * 512;
-    __builtin_amdgcn_global_load_lds((gptr_void)src, (lptr_void)dst, 16, 0, 0);
+    const int lb = ((key & 15) * D + c * 8) * 2;
+    if (kBufferDma)
+      dma16((isv ? gv : gk) + base, lb, 0, (isv ? vs : ks) + bi * 512);
+    else
+      __builtin_amdgcn_global_load_lds((gptr_void)((isv ? gv : gk) + base + lb / 2),
+                                       (lptr_void)((isv ? vs : ks) + bi * 512), 16, 0, 0);
   }
 }
 
@@ -313,7 +343,14 @@ SPEC_DEVICE uint32_t visible_bits(int kb0, int L, int key_end, uint64_t mw0, uin
 // staged tile and one wave's 32 query rows.
 // S^T = K Q^T (a 32x32 block); sc[e] is the score of key
 // kb0 + half*4 + 8*(e/4) + e%4 (C layout of S^T).
-template <int D>
+// Scheduling-group masks (instruction classes) for the lean variants below.
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedDsRead = 0x100;
+
+// kLean (12-wave workgroups, three waves per SIMD): the fragment reads are
+// kept two MFMAs ahead instead of all hoisted, which holds the registers to
+// what three waves per SIMD allow.
+template <int D, bool kLean = false>
 SPEC_DEVICE f32x16 half_scores(const uint16_t* ks, int hk, int lane,
                                const bf16x8 (&qf)[D / 16]) {
   constexpr int NKS = D / 16;
@@ -327,6 +364,15 @@ SPEC_DEVICE f32x16 half_scores(const uint16_t* ks, int hk, int lane,
     const bf16x8 kf = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const char*>(ks) +
                                                        tile_slot_bytes(krow, kk * 2 + half));
     sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], sc, 0, 0, 0);
+  }
+  if (kLean) {
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+#pragma unroll
+    for (int i = 0; i < NKS - 2; ++i) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2, 0);
   }
   return sc;
 }
@@ -379,7 +425,7 @@ SPEC_DEVICE void scale_acc(f32x16 (&acc)[D / 32], float alpha) {
 // dim dbase+4q+c of 4 consecutive keys.  The k-slots of P^T (key
 // half*4 + 8*(e/4) + e%4 of each 16-key step) and of V^T follow the same
 // order.
-template <int D>
+template <int D, bool kLean = false>
 SPEC_DEVICE void half_pv(const uint16_t* vs, int hk, int lane, const bf16x8 (&pb)[2],
                          f32x16 (&acc)[D / 32]) {
   constexpr int NDB = D / 32;
@@ -407,18 +453,27 @@ SPEC_DEVICE void half_pv(const uint16_t* vs, int hk, int lane, const bf16x8 (&pb
       acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[mm], acc[db], 0, 0, 0);
     }
   }
+  if (kLean) {
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 0);
+#pragma unroll
+    for (int i = 0; i < 2 * NDB - 2; ++i) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2, 0);
+  }
 }
 
 // One 32-key half (hk) of a staged tile for one wave's 32 query rows:
 // scores, mask (tiles at the tree or split end), online softmax, P V^T.
 // kb0 is the absolute index of the half's first key.
-template <int D>
+template <int D, bool kLean = false>
 SPEC_DEVICE void compute_half(const uint16_t* ks, const uint16_t* vs, int hk, int kb0, int lane,
                               int L, int key_end, float scale_log2, const uint64_t* mw,
                               const bf16x8 (&qf)[D / 16],
                               f32x16 (&acc)[D / 32], float& m_run, float& l_run) {
   const int half = lane >> 5;
-  f32x16 sc = half_scores<D>(ks, hk, lane, qf);
+  f32x16 sc = half_scores<D, kLean>(ks, hk, lane, qf);
   if (kb0 + 32 > min(L, key_end)) {          // uniform: only tiles at the tree or split end
     const uint32_t vis = visible_bits(kb0, L, key_end, mw[0], mw[1], mw[2], mw[3]);
 #pragma unroll
@@ -430,7 +485,7 @@ SPEC_DEVICE void compute_half(const uint16_t* ks, const uint16_t* vs, int hk, in
   bf16x8 pb[2];
   float alpha;
   if (__any(half_softmax(sc, scale_log2, m_run, l_run, pb, alpha))) scale_acc<D>(acc, alpha);
-  half_pv<D>(vs, hk, lane, pb, acc);
+  half_pv<D, kLean>(vs, hk, lane, pb, acc);
 }
 
 // A whole tile of prefix keys (no mask) for one wave's 32 rows, pipelined
@@ -477,14 +532,15 @@ SPEC_DEVICE int64_t unit_base(const AttnArgs& a, int b) {
 // the end), so small trees still keep every SIMD busy.  K/V tiles of 64 keys
 // stream through a 4-stage LDS ring filled by direct-to-LDS loads, three
 // tiles ahead of the compute.
-template <int D>
-__global__ void __launch_bounds__(kWaves * 64, 1) attn_bf16_kernel(AttnArgs a) {
+template <int D, int W>
+__global__ void __launch_bounds__(W * 64, 1) attn_bf16_kernel(AttnArgs a) {
   constexpr int NKS = D / 16;
   constexpr int NDB = D / 32;
-  constexpr int ROWS = kWaves * kRowsPerWave;
+  constexpr int ROWS = W * kRowsPerWave;
   constexpr int TILE = kTileKeys * D;                 // bf16 per K (or V) tile
-  constexpr int PER_WAVE = 2 * (D / 8) / kWaves;      // DMA blocks per wave per tile
+  constexpr int PER_WAVE = 2 * (D / 8) / kDmaWaves;   // DMA blocks per loading wave per tile
   static_assert(PER_WAVE * 3 < 64, "vmcnt range");
+  static_assert(W == kWaves || W == kWideWaves, "workgroup shapes");
   __shared__ __attribute__((aligned(16))) uint16_t k0[TILE], k1[TILE], k2[TILE], k3[TILE];
   __shared__ __attribute__((aligned(16))) uint16_t v0[TILE], v1[TILE], v2[TILE], v3[TILE];
   __shared__ __attribute__((aligned(16))) int s_blk[kMaxSplit / kBlock + 4];
@@ -514,9 +570,14 @@ __global__ void __launch_bounds__(kWaves * 64, 1) attn_bf16_kernel(AttnArgs a) {
     item = s_item;
   }
   const ItemLoc loc = locate_item(item, a);
-  const int b = loc.b;
+  // Uniform results of the wave-parallel search.  The wide variant says so
+  // (its K/V bases then stay in scalar registers for the buffer-resource
+  // loads); the 8-wave one keeps the allocation measured fastest for it.
+  const int b = (W > kWaves) ? __builtin_amdgcn_readfirstlane(loc.b) : loc.b;
   if (b < 0) return;
-  const int kvh = loc.kvh, rb = loc.rb, s = loc.s;
+  const int kvh = (W > kWaves) ? __builtin_amdgcn_readfirstlane(loc.kvh) : loc.kvh;
+  const int rb = (W > kWaves) ? __builtin_amdgcn_readfirstlane(loc.rb) : loc.rb;
+  const int s = (W > kWaves) ? __builtin_amdgcn_readfirstlane(loc.s) : loc.s;
   const int o = __builtin_amdgcn_readfirstlane(loc.o);
   const int n = __builtin_amdgcn_readfirstlane(loc.n);
   const int L = __builtin_amdgcn_readfirstlane(loc.L);
@@ -545,7 +606,7 @@ __global__ void __launch_bounds__(kWaves * 64, 1) attn_bf16_kernel(AttnArgs a) {
     }
   }
   const int groups = (min(ROWS, M - rb * ROWS) + kRowsPerWave - 1) / kRowsPerWave;
-  const bool pair = groups <= kWaves / 2;
+  const bool pair = groups <= W / 2;
   const int g = pair ? (wave >> 1) : wave;
   const int h_lo = pair ? (wave & 1) : 0;
   const int h_hi = pair ? h_lo + 1 : 2;
@@ -571,7 +632,7 @@ __global__ void __launch_bounds__(kWaves * 64, 1) attn_bf16_kernel(AttnArgs a) {
   const uint16_t* vbase;
   if (paged) {
     const int nblk = ((key_end + kBlock - 1) >> 4) - blk0;
-    for (int i = tid; i < nblk; i += kWaves * 64)
+    for (int i = tid; i < nblk; i += W * 64)
       s_blk[i] = a.addr.block_table[(int64_t)b * a.addr.mbps + blk0 + i];
     kbase = a.k + (int64_t)kvh * kBlock * D;
     vbase = a.v + (int64_t)kvh * kBlock * D;
@@ -592,12 +653,12 @@ __global__ void __launch_bounds__(kWaves * 64, 1) attn_bf16_kernel(AttnArgs a) {
   // computes tile t.  No tile past the split is issued, and the last steps
   // wait for correspondingly fewer loads in flight.
   const int ntiles = (key_end - key_begin + kTileKeys - 1) / kTileKeys;
-  issue_tile<D>(k0, v0, gk, gv, key_begin, key_end, paged, s_blk, blk0, blk_stride, wave, lane);
+  issue_tile<D, (W > kWaves)>(k0, v0, gk, gv, key_begin, key_end, paged, s_blk, blk0, blk_stride, wave, lane);
   if (ntiles > 1)
-    issue_tile<D>(k1, v1, gk, gv, key_begin + kTileKeys, key_end, paged, s_blk, blk0, blk_stride,
+    issue_tile<D, (W > kWaves)>(k1, v1, gk, gv, key_begin + kTileKeys, key_end, paged, s_blk, blk0, blk_stride,
                   wave, lane);
   if (ntiles > 2)
-    issue_tile<D>(k2, v2, gk, gv, key_begin + 2 * kTileKeys, key_end, paged, s_blk, blk0,
+    issue_tile<D, (W > kWaves)>(k2, v2, gk, gv, key_begin + 2 * kTileKeys, key_end, paged, s_blk, blk0,
                   blk_stride, wave, lane);
   // The query rows and mask words load while the first tiles stream in.
   bf16x8 qf[NKS];
@@ -631,7 +692,9 @@ __global__ void __launch_bounds__(kWaves * 64, 1) attn_bf16_kernel(AttnArgs a) {
 #define SPEC_ATTN_STEP(KC, VC, KN, VN, T)                                                       \
   {                                                                                              \
     const int t0_ = key_begin + (T) * kTileKeys;                                                 \
-    if ((T) + 2 < ntiles)                                                                        \
+    if (W > kDmaWaves && wave >= kDmaWaves)                                                      \
+      __builtin_amdgcn_s_waitcnt(SPEC_VMCNT(0));                                                 \
+    else if ((T) + 2 < ntiles)                                                                   \
       __builtin_amdgcn_s_waitcnt(SPEC_VMCNT(2 * PER_WAVE));                                      \
     else if ((T) + 1 < ntiles)                                                                   \
       __builtin_amdgcn_s_waitcnt(SPEC_VMCNT(PER_WAVE));                                          \
@@ -639,14 +702,15 @@ __global__ void __launch_bounds__(kWaves * 64, 1) attn_bf16_kernel(AttnArgs a) {
       __builtin_amdgcn_s_waitcnt(SPEC_VMCNT(0));                                                 \
     __builtin_amdgcn_s_barrier();                                                                \
     if ((T) + 3 < ntiles)                                                                        \
-      issue_tile<D>(KN, VN, gk, gv, t0_ + 3 * kTileKeys, key_end, paged, s_blk, blk0,            \
+      issue_tile<D, (W > kWaves)>(KN, VN, gk, gv, t0_ + 3 * kTileKeys, key_end, paged, s_blk, blk0,            \
                     blk_stride, wave, lane);                                                     \
     if (wave_active) {                                                                           \
-      if (!pair && t0_ + kTileKeys <= min(L, key_end)) {                                         \
+      if (W == kWaves && !pair && t0_ + kTileKeys <= min(L, key_end)) {                          \
         compute_tile_full<D>(KC, VC, lane, a.scale_log2, qf, acc, m_run, l_run);                 \
       } else {                                                                                   \
         for (int hk = h_lo; hk < h_hi; ++hk)                                                     \
-          compute_half<D>(KC, VC, hk, t0_ + 32 * hk, lane, L, key_end, a.scale_log2, mw, qf,     \
+          compute_half<D, (W > kWaves)>(KC, VC, hk, t0_ + 32 * hk, lane, L, key_end,             \
+                                        a.scale_log2, mw, qf,                                    \
                           acc, m_run, l_run);                                                    \
       }                                                                                          \
     }                                                                                            \
@@ -668,8 +732,12 @@ __global__ void __launch_bounds__(kWaves * 64, 1) attn_bf16_kernel(AttnArgs a) {
   __builtin_amdgcn_s_waitcnt(SPEC_VMCNT(0));
   __syncthreads();
   constexpr int NV4 = NDB * 4;                         // float4 per lane of acc
+  // Pair mode: the odd wave of each group hands its (m, l, O) to the even
+  // one through the idle ring (group g in a 16 KB stage buffer, the (m, l)
+  // pairs in v0).
+  static_assert(W / 2 <= 6, "merge slots");
   if (pair && wave_active && (wave & 1)) {
-    uint16_t* slot = (g == 0) ? k0 : (g == 1) ? k1 : (g == 2) ? k2 : k3;
+    uint16_t* slot = (g == 0) ? k0 : (g == 1) ? k1 : (g == 2) ? k2 : (g == 3) ? k3 : (g == 4) ? v1 : v2;
     float4* xs = reinterpret_cast<float4*>(slot);
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
@@ -685,7 +753,7 @@ __global__ void __launch_bounds__(kWaves * 64, 1) attn_bf16_kernel(AttnArgs a) {
   if (pair && (wave & 1)) return;
   if (!row_ok) return;
   if (pair) {
-    const uint16_t* slot = (g == 0) ? k0 : (g == 1) ? k1 : (g == 2) ? k2 : k3;
+    const uint16_t* slot = (g == 0) ? k0 : (g == 1) ? k1 : (g == 2) ? k2 : (g == 3) ? k3 : (g == 4) ? v1 : v2;
     const float4* xs = reinterpret_cast<const float4*>(slot);
     const float2 ml = reinterpret_cast<const float2*>(v0)[g * 64 + lane];
     const float m_new = fmaxf(m_run, ml.x);
@@ -748,9 +816,9 @@ __global__ void __launch_bounds__(kWaves * 64, 1) attn_bf16_kernel(AttnArgs a) {
 // head, row block); each thread merges one float4 column of a row over the
 // splits in one pass with a running maximum (coalesced 512-byte rows of
 // partials; weights exp2(m_s - m)).
-template <int D>
+template <int D, int W>
 __global__ void __launch_bounds__(256) attn_combine_kernel(AttnArgs a) {
-  constexpr int ROWS = kWaves * kRowsPerWave;
+  constexpr int ROWS = W * kRowsPerWave;
   constexpr int CHUNKS = ROWS / kCombineRows;
   constexpr int C4 = D / 4;                        // float4 per row
   constexpr int RPI = 256 / C4;                    // rows per pass of the block
@@ -917,8 +985,14 @@ AttnPlan plan_attention(int B, const int32_t* row_offsets_h, const int32_t* pref
   const int G = hq / hkv;
   AttnPlan p;
   // 8 waves of 32 query rows: most (request, KV head) pairs fit in one
-  // workgroup, so every KV tile is read once.
-  p.rows_per_block = kWaves * kRowsPerWave;
+  // workgroup, so every KV tile is read once.  A batch with a pair of more
+  // than 256 query rows (the 70B-shaped K-schedule trees: 46 rows x 8 heads
+  // of a group = 368) takes 12 waves (384 rows, three per SIMD) instead, so
+  // that such a pair is still one workgroup reading each tile once.
+  int max_unit_rows = 0;
+  for (int b = 0; b < B; ++b)
+    max_unit_rows = std::max(max_unit_rows, (row_offsets_h[b + 1] - row_offsets_h[b]) * G);
+  p.rows_per_block = (max_unit_rows > kWaves * kRowsPerWave ? kWideWaves : kWaves) * kRowsPerWave;
   int64_t work = 0, units = 0, max_keys = 0, min_keys = INT64_MAX;
   for (int b = 0; b < B; ++b) {
     const int n = row_offsets_h[b + 1] - row_offsets_h[b];
@@ -1045,15 +1119,26 @@ hipError_t launch_attention_bf16(const LaunchCtx& cx, const AttnPlan& plan, cons
   if (plan.lpt) std::copy(plan.order, plan.order + cx.B, a.order);
   if (plan.items <= 0 || plan.items > 0x7fffffff) return hipErrorInvalidValue;
   const dim3 grid((unsigned)plan.items);
-  if (plan.rows_per_block != kWaves * kRowsPerWave) return hipErrorInvalidValue;
-  if (addr.d == 128) {
-    hipLaunchKernelGGL(attn_bf16_kernel<128>, grid, dim3(kWaves * 64), 0, cx.stream, a);
+  const int W = plan.rows_per_block / kRowsPerWave;
+  if (W * kRowsPerWave != plan.rows_per_block || (W != kWaves && W != kWideWaves))
+    return hipErrorInvalidValue;
+  const dim3 cgrid((unsigned)(plan.units * (plan.rows_per_block / kCombineRows)));
+  if (addr.d == 128 && W == kWaves) {
+    hipLaunchKernelGGL((attn_bf16_kernel<128, kWaves>), grid, dim3(W * 64), 0, cx.stream, a);
     if (plan.partial_items)
-      hipLaunchKernelGGL(attn_combine_kernel<128>, dim3((unsigned)(plan.units * (kWaves * kRowsPerWave / kCombineRows))), dim3(256), 0, cx.stream, a);
+      hipLaunchKernelGGL((attn_combine_kernel<128, kWaves>), cgrid, dim3(256), 0, cx.stream, a);
+  } else if (addr.d == 128) {
+    hipLaunchKernelGGL((attn_bf16_kernel<128, kWideWaves>), grid, dim3(W * 64), 0, cx.stream, a);
+    if (plan.partial_items)
+      hipLaunchKernelGGL((attn_combine_kernel<128, kWideWaves>), cgrid, dim3(256), 0, cx.stream, a);
+  } else if (W == kWaves) {
+    hipLaunchKernelGGL((attn_bf16_kernel<64, kWaves>), grid, dim3(W * 64), 0, cx.stream, a);
+    if (plan.partial_items)
+      hipLaunchKernelGGL((attn_combine_kernel<64, kWaves>), cgrid, dim3(256), 0, cx.stream, a);
   } else {
-    hipLaunchKernelGGL(attn_bf16_kernel<64>, grid, dim3(kWaves * 64), 0, cx.stream, a);
+    hipLaunchKernelGGL((attn_bf16_kernel<64, kWideWaves>), grid, dim3(W * 64), 0, cx.stream, a);
     if (plan.partial_items)
-      hipLaunchKernelGGL(attn_combine_kernel<64>, dim3((unsigned)(plan.units * (kWaves * kRowsPerWave / kCombineRows))), dim3(256), 0, cx.stream, a);
+      hipLaunchKernelGGL((attn_combine_kernel<64, kWideWaves>), cgrid, dim3(256), 0, cx.stream, a);
   }
   return hipGetLastError();
 }
