@@ -272,6 +272,17 @@ spec_status spec_accept_sample_noalloc(const spec_batch *batch, const int32_t *p
                                        uint64_t step, int32_t path_stride,
                                        const spec_accept_out *out, hipStream_t stream);
 
+/* spec_test_exp_f64 -- for tests of the library's double-precision
+ * exponential, which every acceptance decision rests on (the probabilities
+ * P_u(x) = exp(p_u(x)/T - lse) of [MATH] 7.1 and every residual and draw
+ * weight): y_d[i] = f(x_d[i]) for i < n, both f64 device arrays, with
+ *   variant 0  exp_f64:          e^x for -708 <= x <= 709, exactly 0 below -708
+ *   variant 1  exp_f64_clamped:  e^max(x, -708) (sums of probability mass)
+ *   variant 2  exp_f64_stream:   the unguarded core, -745 <= x <= 709
+ * Errors: NULL pointers, n outside 1..2^32, another variant. */
+spec_status spec_test_exp_f64(const double *x_d, double *y_d, int64_t n, int32_t variant,
+                              hipStream_t stream);
+
 /* spec_accept_sample with the sampling walk's two launch knobs exposed, for
  * tests of its cross-workgroup meetings (the outputs do not depend on them
  * except through SPEC_FLAG_SYNC_TIMEOUT):

@@ -30,7 +30,7 @@ def _declared():
 
 def test_header_declarations_are_all_exported():
     names = _declared()
-    assert "spec_tree_attn_verify" in names and len(names) == 19
+    assert "spec_tree_attn_verify" in names and len(names) == 20
     assert sorted(L.EXPORTS) == names
     lib = ctypes.CDLL(L.LIB_PATH)
     for n in names:
@@ -326,6 +326,13 @@ def test_lm_head_accept_validation():
     assert call(head=L.CLmHead(FAKE, FAKE, 256, None), q=None, T=0.0, ws=0) == 8
     # deterministic children: no draft rows
     assert call(q=None, children=1, ws=0) == 8
+
+
+def test_exp_probe_validation():
+    f = L.LIB.spec_test_exp_f64
+    assert f(None, FAKE, 10, 0, None) == 1
+    assert f(FAKE, FAKE, 0, 0, None) == 2
+    assert f(FAKE, FAKE, 10, 3, None) == 2 and "variant" in _err()
 
 
 def test_accept_walk_knobs_validation():

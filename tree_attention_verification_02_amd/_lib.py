@@ -31,7 +31,7 @@ STATUS_NAMES = {0: "SPEC_OK", 1: "SPEC_ERR_NULL", 2: "SPEC_ERR_SHAPE", 3: "SPEC_
 
 EXPORTS = ["spec_tree_build_mask", "spec_kv_append", "spec_tree_attn_workspace_bytes",
            "spec_tree_attn_verify", "spec_accept_workspace_bytes", "spec_accept_sample",
-           "spec_accept_sample_walk_knobs", "spec_accept_sample_noalloc",
+           "spec_accept_sample_walk_knobs", "spec_accept_sample_noalloc", "spec_test_exp_f64",
            "spec_accept_topk", "spec_kv_commit", "spec_draft_begin", "spec_draft_expand",
            "spec_draft_select_workspace_bytes", "spec_draft_select", "spec_lm_head_accept_workspace_bytes",
            "spec_lm_head_accept", "spec_status_string", "spec_last_error", "spec_abi_version"]
@@ -100,6 +100,7 @@ def _load():
                                           ctypes.c_int),
         "spec_accept_sample_noalloc": ([P(CBatch), vp, vp, vp, vp, i64, i32, f32, u64, u64, i32,
                                         P(CAcceptOut), vp], ctypes.c_int),
+        "spec_test_exp_f64": ([vp, vp, i64, i32, vp], ctypes.c_int),
         "spec_accept_topk": ([P(CBatch), vp, vp, vp, i64, i32, f32, u64, u64, i32,
                               P(CAcceptOut), vp, sz, vp], ctypes.c_int),
         "spec_kv_commit": ([P(CBatch), P(CKv), vp, vp, i32, vp, vp, vp], ctypes.c_int),
@@ -274,6 +275,13 @@ def spec_accept_sample(batch, parents, tokens, p_logits, q_logits, vocab, temper
                                   _ptr(p_logits), _ptr(q_logits), int(logits_ld), int(vocab),
                                   float(temperature), int(seed), int(step), out.path_stride,
                                   ctypes.byref(out.c), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def spec_test_exp_f64(x, y, variant=0, stream=None):
+    """y = the library's fp64 exponential of x (float64 device tensors);
+    variant 0 exp_f64, 1 exp_f64_clamped, 2 exp_f64_stream."""
+    _check(LIB.spec_test_exp_f64(_ptr(x), _ptr(y), int(x.numel()), int(variant),
+                                 _stream(stream)))
 
 
 SPEC_ACCEPT_SCRATCH_BYTES = 8 << 20

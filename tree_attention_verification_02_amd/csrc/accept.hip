@@ -1106,6 +1106,27 @@ hipError_t accept_scratch(void** ptr) {
   return hipSuccess;
 }
 
+// The fp64 exponentials every decision rests on, evaluated element by element
+// for tests: variant 0 exp_f64, 1 exp_f64_clamped, 2 exp_f64_stream.
+__global__ void __launch_bounds__(256)
+exp64_probe_kernel(const double* __restrict__ x, double* __restrict__ y, int64_t n, int variant) {
+  __shared__ double tab[256];
+  load_exp_table(tab);
+  __syncthreads();
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  const double v = x[i];
+  y[i] = (variant == 0) ? exp_f64(v, tab) : (variant == 1) ? exp_f64_clamped(v, tab)
+                                                            : exp_f64_stream(v, tab);
+}
+
+hipError_t launch_exp64_probe(const double* x, double* y, int64_t n, int variant,
+                              hipStream_t stream) {
+  hipLaunchKernelGGL(exp64_probe_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream,
+                     x, y, n, variant);
+  return hipGetLastError();
+}
+
 // Walk workgroups that fit on device `dev` at once (CUs x occupancy),
 // queried once per device.
 static hipError_t walk_capacity(int dev, int* capacity) {

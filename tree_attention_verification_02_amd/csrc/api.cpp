@@ -320,6 +320,14 @@ spec_status spec_accept_sample_walk_knobs(const spec_batch* batch, const int32_t
                      "spec_accept_sample_walk_knobs", k);
 }
 
+spec_status spec_test_exp_f64(const double* x_d, double* y_d, int64_t n, int32_t variant,
+                              hipStream_t stream) {
+  if (!x_d || !y_d) return fail(SPEC_ERR_NULL, "x_d and y_d are required");
+  if (n < 1 || n > (int64_t)1 << 32) return fail(SPEC_ERR_SHAPE, "n = %lld, need 1..2^32", (long long)n);
+  if (variant < 0 || variant > 2) return fail(SPEC_ERR_SHAPE, "variant = %d, need 0, 1 or 2", variant);
+  return launched(spec::launch_exp64_probe(x_d, y_d, n, variant, stream), "spec_test_exp_f64");
+}
+
 spec_status spec_accept_topk(const spec_batch* batch, const int32_t* parents_d, const int32_t* tokens_d,
                              const float* p_logits_d, int64_t logits_ld, int32_t vocab,
                              float temperature, uint64_t seed, uint64_t step, int32_t path_stride,

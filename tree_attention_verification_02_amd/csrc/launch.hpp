@@ -92,6 +92,8 @@ struct WalkKnobs {
   int max_spins = -1;
 };
 size_t accept_workspace_bytes(int R, int B, int vocab);
+hipError_t launch_exp64_probe(const double* x, double* y, int64_t n, int variant,
+                              hipStream_t stream);
 // The no-allocation entry point's workspace: a device array of this many
 // bytes in accept.hip, its address on the current device.
 constexpr size_t kAcceptScratchBytes = (size_t)8 << 20;
