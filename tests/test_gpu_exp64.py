@@ -4,7 +4,8 @@ Every accept test and draw of the acceptance walk compares probabilities
 P_u(x) = exp(p_u(x)/T - lse) (CSDN page "推理加速：推测解码与级联推理",
 section 7.1) that the library evaluates with its own table-driven fp64
 exponential.  Here it runs through spec_test_exp_f64 on a dense grid over
-[-745, 709], on every table boundary k ln2/256 and its neighbours, and on
+[-745, 709], on table boundaries k ln2/256 (every 7th k, which meets every
+one of the 256 table entries) with their neighbours and midpoints, and on
 values around the -708 guard, against exp in x86 extended precision (64-bit
 mantissa, then rounded to double -- numpy's own float64 exp does not enter
 the bound).
