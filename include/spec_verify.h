@@ -279,6 +279,10 @@ spec_status spec_accept_sample_noalloc(const spec_batch *batch, const int32_t *p
  *   variant 0  exp_f64:          e^x for -708 <= x <= 709, exactly 0 below -708
  *   variant 1  exp_f64_clamped:  e^max(x, -708) (sums of probability mass)
  *   variant 2  exp_f64_stream:   the unguarded core, -745 <= x <= 709
+ *   variant 3  exp_f64 evaluated two at a time (elements 2k, 2k+1 together;
+ *              a last odd element paired with itself), as the walk's sums do
+ *   variant 4  exp_f64_clamped two at a time, as the statistics sums do
+ * Variants 3 and 4 must equal 0 and 1 bit for bit.
  * Errors: NULL pointers, n outside 1..2^32, another variant. */
 spec_status spec_test_exp_f64(const double *x_d, double *y_d, int64_t n, int32_t variant,
                               hipStream_t stream);

@@ -332,7 +332,8 @@ def test_exp_probe_validation():
     f = L.LIB.spec_test_exp_f64
     assert f(None, FAKE, 10, 0, None) == 1
     assert f(FAKE, FAKE, 0, 0, None) == 2
-    assert f(FAKE, FAKE, 10, 3, None) == 2 and "variant" in _err()
+    assert f(FAKE, FAKE, 10, 5, None) == 2 and "variant" in _err()
+    assert f(FAKE, FAKE, 10, -1, None) == 2 and "variant" in _err()
 
 
 def test_accept_walk_knobs_validation():

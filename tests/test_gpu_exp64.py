@@ -95,3 +95,18 @@ def test_clamped_and_stream_variants(lib):
     log(f"[exp64] exp_f64_stream on {int(below.sum())} points in [-745, -708): "
         f"max error {float(sub.max() / tiny):.1f} x the smallest subnormal")
     assert (sub <= ULP_BOUND * tiny + ULP_BOUND * np.spacing(_reference(x[below]))).all()
+
+
+def test_paired_evaluation_is_bit_identical(lib):
+    """The walk's and the statistics' sums evaluate their exponentials two at
+    a time (both table reads issued first); that must not change a bit.  The
+    grid is shuffled so pairs mix arguments from far apart, and has odd
+    length so the last element is paired with itself."""
+    x = _grid()
+    x = np.random.default_rng(5).permutation(x)[: (len(x) // 2) * 2 - 1]
+    y0 = _run(lib, x, 0)
+    y1 = _run(lib, x, 1)
+    y3 = _run(lib, x, 3)
+    y4 = _run(lib, x, 4)
+    assert np.array_equal(y3.view(np.uint64), y0.view(np.uint64))
+    assert np.array_equal(y4.view(np.uint64), y1.view(np.uint64))

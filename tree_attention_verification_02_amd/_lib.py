@@ -279,7 +279,8 @@ def spec_accept_sample(batch, parents, tokens, p_logits, q_logits, vocab, temper
 
 def spec_test_exp_f64(x, y, variant=0, stream=None):
     """y = the library's fp64 exponential of x (float64 device tensors);
-    variant 0 exp_f64, 1 exp_f64_clamped, 2 exp_f64_stream."""
+    variant 0 exp_f64, 1 exp_f64_clamped, 2 exp_f64_stream, 3 and 4 the first
+    two evaluated two elements at a time."""
     _check(LIB.spec_test_exp_f64(_ptr(x), _ptr(y), int(x.numel()), int(variant),
                                  _stream(stream)))
 

@@ -240,12 +240,17 @@ accept_stats_kernel(const int32_t* __restrict__ row_offsets, int B, int R,
   double s = 0.0;
 #pragma unroll
   for (int k = 0; k < kStatF4; ++k) {
-    s += exp_f64_clamped(fma((double)x[k].x, invT, -ref), s_tab);
-    s += exp_f64_clamped(fma((double)x[k].y, invT, -ref), s_tab);
-    s += exp_f64_clamped(fma((double)x[k].z, invT, -ref), s_tab);
-    s += exp_f64_clamped(fma((double)x[k].w, invT, -ref), s_tab);
+    double e0, e1, e2, e3;
+    exp_f64_clamped2(fma((double)x[k].x, invT, -ref), fma((double)x[k].y, invT, -ref), s_tab,
+                     e0, e1);
+    exp_f64_clamped2(fma((double)x[k].z, invT, -ref), fma((double)x[k].w, invT, -ref), s_tab,
+                     e2, e3);
+    s += e0;
+    s += e1;
+    s += e2;
+    s += e3;
   }
-  s = wave_sum(s);
+  s = wave_sum_f64(s);
   if (lane == 0) red_s[wave] = s;
   __syncthreads();
   if (tid == 0) {
@@ -392,9 +397,9 @@ struct WalkShared {
 // need_q is false (t = 0 at a leaf).
 SPEC_DEVICE double walk_weight(float py, float qy, double invT, double lse_p, double lse_q,
                                double t, bool need_q, const double* tab) {
-  const double P = exp_f64((double)py * invT - lse_p, tab);
+  double P, Q;
+  exp_f64_2((double)py * invT - lse_p, need_q ? (double)qy * invT - lse_q : -INFINITY, tab, P, Q);
   if (!need_q) return P;
-  const double Q = exp_f64((double)qy * invT - lse_q, tab);
   return fmax(0.0, fma(-t, Q, P));
 }
 
@@ -483,15 +488,25 @@ SPEC_DEVICE double weight4(const WalkCtx& c, float4 pv, float4 qv, int y0, doubl
   const float qa[4] = {qv.x, qv.y, qv.z, qv.w};
   const int ex = kQ ? 0 : excluded4(c, y0);
   double acc = 0.0;
+  if (kQ) {
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const bool in = y0 + j < c.vocab && !((ex >> j) & 1);   // ragged end, excluded tokens
-    const double P = exp_f64_clamped((double)(in ? pa[j] : -INFINITY) * c.invT - c.lse_p, tab);
-    if (kQ) {
-      const double Q = exp_f64_clamped((double)(in ? qa[j] : -INFINITY) * c.invT - c.lse_q, tab);
+    for (int j = 0; j < 4; ++j) {
+      const bool in = y0 + j < c.vocab;                 // ragged end
+      double P, Q;
+      exp_f64_clamped2((double)(in ? pa[j] : -INFINITY) * c.invT - c.lse_p,
+                       (double)(in ? qa[j] : -INFINITY) * c.invT - c.lse_q, tab, P, Q);
       acc += fmax(0.0, fma(-t, Q, P));
-    } else {
-      acc += P;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; j += 2) {
+      const bool in0 = y0 + j < c.vocab && !((ex >> j) & 1);   // ragged end, excluded tokens
+      const bool in1 = y0 + j + 1 < c.vocab && !((ex >> (j + 1)) & 1);
+      double P0, P1;
+      exp_f64_clamped2((double)(in0 ? pa[j] : -INFINITY) * c.invT - c.lse_p,
+                       (double)(in1 ? pa[j + 1] : -INFINITY) * c.invT - c.lse_p, tab, P0, P1);
+      acc += P0;
+      acc += P1;
     }
   }
   return acc;
@@ -515,7 +530,7 @@ SPEC_DEVICE void pass_round(WalkShared& sh, const WalkCtx& c, int s0, int base, 
   }
 #pragma unroll
   for (int i = 0; i < NR; ++i) {
-    const double w = wave_sum(weight4<kQ>(c, pb[i], qb[i], (s0 + i) * kSeg + 4 * tid, t, sh.tab));
+    const double w = wave_sum_f64(weight4<kQ>(c, pb[i], qb[i], (s0 + i) * kSeg + 4 * tid, t, sh.tab));
     if (lane == 0) sh.part[s0 - base + i][wave] = w;
   }
 }
@@ -1107,7 +1122,8 @@ hipError_t accept_scratch(void** ptr) {
 }
 
 // The fp64 exponentials every decision rests on, evaluated element by element
-// for tests: variant 0 exp_f64, 1 exp_f64_clamped, 2 exp_f64_stream.
+// for tests: variant 0 exp_f64, 1 exp_f64_clamped, 2 exp_f64_stream; 3 and 4
+// the first two evaluated two at a time (elements 2k and 2k + 1 together).
 __global__ void __launch_bounds__(256)
 exp64_probe_kernel(const double* __restrict__ x, double* __restrict__ y, int64_t n, int variant) {
   __shared__ double tab[256];
@@ -1116,6 +1132,17 @@ exp64_probe_kernel(const double* __restrict__ x, double* __restrict__ y, int64_t
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= n) return;
   const double v = x[i];
+  if (variant >= 3) {
+    const int64_t j = (i ^ 1) < n ? (i ^ 1) : i;     // the pair's other element
+    const double a = (i & 1) ? x[j] : v, b = (i & 1) ? v : x[j];
+    double ya, yb;
+    if (variant == 3)
+      exp_f64_2(a, b, tab, ya, yb);
+    else
+      exp_f64_clamped2(a, b, tab, ya, yb);
+    y[i] = (i & 1) ? yb : ya;
+    return;
+  }
   y[i] = (variant == 0) ? exp_f64(v, tab) : (variant == 1) ? exp_f64_clamped(v, tab)
                                                             : exp_f64_stream(v, tab);
 }

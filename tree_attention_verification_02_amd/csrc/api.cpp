@@ -324,7 +324,7 @@ spec_status spec_test_exp_f64(const double* x_d, double* y_d, int64_t n, int32_t
                               hipStream_t stream) {
   if (!x_d || !y_d) return fail(SPEC_ERR_NULL, "x_d and y_d are required");
   if (n < 1 || n > (int64_t)1 << 32) return fail(SPEC_ERR_SHAPE, "n = %lld, need 1..2^32", (long long)n);
-  if (variant < 0 || variant > 2) return fail(SPEC_ERR_SHAPE, "variant = %d, need 0, 1 or 2", variant);
+  if (variant < 0 || variant > 4) return fail(SPEC_ERR_SHAPE, "variant = %d, need 0..4", variant);
   return launched(spec::launch_exp64_probe(x_d, y_d, n, variant, stream), "spec_test_exp_f64");
 }
 

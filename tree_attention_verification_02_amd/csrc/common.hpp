@@ -41,6 +41,32 @@ SPEC_DEVICE T wave_sum(T v) {
   return v;
 }
 
+// Sum of a double over the wave without the LDS crossbar: a butterfly within
+// each 16-lane row by DPP moves (quad_perm [1,0,3,2], quad_perm [2,3,0,1],
+// row_ror 4, row_ror 8), then the four row totals read from lanes 0, 16, 32
+// and 48 and added in a fixed order.  Every lane returns the same value.
+template <int kCtrl>
+SPEC_DEVICE double dpp_f64(double v) {
+  const unsigned long long b = (unsigned long long)__double_as_longlong(v);
+  const int lo = __builtin_amdgcn_mov_dpp((int)(unsigned)b, kCtrl, 0xf, 0xf, false);
+  const int hi = __builtin_amdgcn_mov_dpp((int)(unsigned)(b >> 32), kCtrl, 0xf, 0xf, false);
+  return __longlong_as_double(
+      (long long)(((unsigned long long)(unsigned)hi << 32) | (unsigned long long)(unsigned)lo));
+}
+SPEC_DEVICE double readlane_f64(double v, int lane) {
+  const unsigned long long b = (unsigned long long)__double_as_longlong(v);
+  const unsigned lo = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)b, lane);
+  const unsigned hi = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)(b >> 32), lane);
+  return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
+}
+SPEC_DEVICE double wave_sum_f64(double v) {
+  v += dpp_f64<0xB1>(v);
+  v += dpp_f64<0x4E>(v);
+  v += dpp_f64<0x124>(v);
+  v += dpp_f64<0x128>(v);
+  return (readlane_f64(v, 0) + readlane_f64(v, 16)) + (readlane_f64(v, 32) + readlane_f64(v, 48));
+}
+
 SPEC_DEVICE float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));

@@ -109,6 +109,39 @@ SPEC_DEVICE double exp_f64(double x, const double* tab) {
 SPEC_DEVICE double exp_f64_clamped(double x, const double* tab) {
   return exp_f64_stream(fmax(x, -708.0), tab);
 }
+// Two exponentials in lockstep, each with exactly the operations of
+// exp_f64_stream (so the results are bit-identical): both table reads are
+// issued before either reduction and polynomial, which then hide the LDS
+// latency that a single evaluation waits out.
+SPEC_DEVICE void exp_f64_stream2(double x0, double x1, const double* tab, double& y0,
+                                 double& y1) {
+  constexpr double kShift = 0x1.8p52;
+  const double t0 = fma(x0, kInvLn2x256, kShift);
+  const double t1 = fma(x1, kInvLn2x256, kShift);
+  const int i0 = (int)(uint32_t)__double_as_longlong(t0);
+  const int i1 = (int)(uint32_t)__double_as_longlong(t1);
+  const double s0 = tab[i0 & 255];
+  const double s1 = tab[i1 & 255];
+  __builtin_amdgcn_sched_barrier(0);
+  const double k0 = t0 - kShift;
+  const double k1 = t1 - kShift;
+  const double r0 = fma(-k0, kLn2by256Lo, fma(-k0, kLn2by256Hi, x0));
+  const double r1 = fma(-k1, kLn2by256Lo, fma(-k1, kLn2by256Hi, x1));
+  const double p0 = r0 * fma(r0, fma(r0, fma(r0, 1.0 / 24, 1.0 / 6), 0.5), 1.0);
+  const double p1 = r1 * fma(r1, fma(r1, fma(r1, 1.0 / 24, 1.0 / 6), 0.5), 1.0);
+  y0 = ldexp(fma(s0, p0, s0), i0 >> 8);
+  y1 = ldexp(fma(s1, p1, s1), i1 >> 8);
+}
+// exp_f64 and exp_f64_clamped on two arguments at once.
+SPEC_DEVICE void exp_f64_2(double x0, double x1, const double* tab, double& y0, double& y1) {
+  exp_f64_stream2(fmax(x0, -708.0), fmax(x1, -708.0), tab, y0, y1);
+  if (!(x0 >= -708.0)) y0 = 0.0;
+  if (!(x1 >= -708.0)) y1 = 0.0;
+}
+SPEC_DEVICE void exp_f64_clamped2(double x0, double x1, const double* tab, double& y0,
+                                  double& y1) {
+  exp_f64_stream2(fmax(x0, -708.0), fmax(x1, -708.0), tab, y0, y1);
+}
 SPEC_DEVICE void load_exp_table(double* s_tab) {
   for (int i = threadIdx.x; i < 256; i += blockDim.x) s_tab[i] = kExp2Frac[i];
 }
