@@ -15,17 +15,22 @@
 // and the final draw after the last rejection reuses that pass's sums.
 //
 // Kernels:
-//  * accept_stats: one workgroup per (row, {target, draft}, 16K-logit chunk)
-//    streams its chunk once (16-byte loads) into fp64 partial sums (or the
-//    first argmax).  Draft rows of leaves are never read.  At temperature 0,
-//    accept_finalize merges the argmax partials per row.
+//  * accept_prep (T > 0): lists the rows whose statistics are read -- every
+//    target row, and the draft rows of nodes with children (draft rows of
+//    leaves are never read) -- and clears the walk's exchange area.
+//  * accept_sample_stats (T > 0): one workgroup per listed (row, 16K-logit
+//    chunk) item streams its chunk once (16-byte loads) into fp64 partial
+//    sums.
+//  * accept_argmax (T = 0): the first argmax of every target-row chunk;
+//    accept_finalize merges them per row.
 //  * accept_walk: S workgroups ("slices", taken by ticket in start order) per
 //    request; each merges its request's partials into the rows' log-sum-exps
-//    of logits/T and the child probabilities P_u(x_c), Q_u(x_c) itself.  Each pass is split over the S slices by 1024-element
-//    segments; segment sums go to global memory and the S slices meet at a
-//    per-request counter barrier (bounded spin).  Every slice then sums the
-//    segments in the same order and replays the same scalar decisions, so no
-//    further broadcast is needed; the owner of the drawn segment rescans it.
+//    of logits/T and the child probabilities P_u(x_c), Q_u(x_c) itself.
+//    Each pass is split over the S slices by 1024-element segments; segment
+//    sums go to global memory carrying their pass tag, and every slice reads
+//    all of them (bounded polls), sums them in the same order and replays
+//    the same scalar decisions, so no further broadcast is needed; slice 0
+//    rescans the drawn segment and writes the outputs.
 //  * accept_greedy: temperature 0, one workgroup per request.
 //
 // Deterministic children (no draft rows): each child is a draft from the
@@ -42,6 +47,7 @@
 // ~1e-11 of a threshold.
 #include <math.h>
 
+#include <algorithm>
 #include <atomic>
 #include <mutex>
 
@@ -73,7 +79,9 @@ struct AcceptWs {
   double* part_s;   //                     and sum of exp(z - reference)
   float* part_m;    // [R][nch]    chunk max (greedy)
   int32_t* part_am; //                     and its first index
-  int32_t* sync;    // [64]: [0] the walk's ticket counter (zeroed with seg), own 256 B
+  int32_t* order;   // [2R] rows whose statistics are streamed: rr = r (target), R + r (draft)
+  int32_t* sync;    // [64], own 256 B: [0] the walk's ticket counter (zeroed with seg),
+                    // [2] entries in `order`
   double* seg;      // [B][2][nseg] per-pass segment sums carrying their pass tag
                     // (double-buffered by pass parity; zeroed before every walk)
 };
@@ -99,6 +107,8 @@ __host__ __device__ inline AcceptWs accept_ws(void* base, int R, int B, int voca
   p += align256((size_t)R * nch * sizeof(float));
   w.part_am = (int32_t*)p;
   p += align256((size_t)R * nch * sizeof(int32_t));
+  w.order = (int32_t*)p;
+  p += align256(2 * (size_t)R * sizeof(int32_t));
   w.sync = (int32_t*)p;
   p += 256;
   w.seg = (double*)p;
@@ -115,117 +125,191 @@ size_t accept_workspace_bytes(int R, int B, int vocab) {
          2 * align256(2 * (size_t)R * nch * sizeof(double)) +
          align256((size_t)R * nch * sizeof(float)) +
          align256((size_t)R * nch * sizeof(int32_t)) +
+         align256(2 * (size_t)R * sizeof(int32_t)) +
          256 +
          align256((size_t)B * 2 * nseg * sizeof(double));
 }
 
-// The walk's exchange area starts every call cleared: its ticket counter at
-// 0 and every segment sum with tag 0, which no pass uses.  Spread over the
-// first blocks of the kernel that runs before the walk.
-SPEC_DEVICE void clear_walk_state(const AcceptWs& ws, int B, int vocab) {
-  const int64_t nseg_all = (int64_t)B * 2 * ((vocab + kSeg - 1) / kSeg);
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < nseg_all) ws.seg[i] = 0.0;
-  if (i == 0) ws.sync[0] = 0;
+// Before the statistics at T > 0 (accept_prep_kernel): blocks 1.. clear the
+// walk's exchange area (every segment sum to tag 0, which no pass uses) and
+// block 0 resets the walk's ticket counter and lists the rows whose statistics are streamed
+// -- every target row (unless the LM head has produced their partials),
+// then the draft rows of the nodes that have children (draft rows of leaves
+// are never read).  The children marks live in LDS; beyond its tables every
+// draft row is listed.
+constexpr int kPrepThreads = 1024;
+constexpr int kPrepMaxRows = 16384;
+constexpr int kPrepMaxBatch = 4096;
+
+SPEC_DEVICE int find_request(const int* off, int B, int r) {   // off[b] <= r < off[b + 1]
+  int lo = 0, hi = B;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (off[mid] <= r) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+__global__ void __launch_bounds__(kPrepThreads)
+accept_prep_kernel(const int32_t* __restrict__ row_offsets, int B, int R,
+                   const int32_t* __restrict__ parents, AcceptWs ws, int vocab, int list_p,
+                   int list_q) {
+  __shared__ int s_off[kPrepMaxBatch + 1];
+  __shared__ unsigned char s_kids[kPrepMaxRows];
+  __shared__ int s_wave[kPrepThreads / 64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (blockIdx.x > 0) {
+    const int64_t nseg_all = (int64_t)B * 2 * ((vocab + kSeg - 1) / kSeg);
+    for (int64_t i = (int64_t)(blockIdx.x - 1) * kPrepThreads + tid; i < nseg_all;
+         i += (int64_t)(gridDim.x - 1) * kPrepThreads)
+      ws.seg[i] = 0.0;
+    return;
+  }
+  const int np = list_p ? R : 0;
+  for (int r = tid; r < np; r += kPrepThreads) ws.order[r] = r;
+  if (!list_q) {
+    if (tid == 0) ws.sync[2] = np;
+  } else if (R > kPrepMaxRows || B > kPrepMaxBatch) {
+    for (int r = tid; r < R; r += kPrepThreads) ws.order[np + r] = R + r;
+    if (tid == 0) ws.sync[2] = np + R;
+  } else {
+    for (int i = tid; i <= B; i += kPrepThreads) s_off[i] = row_offsets[i];
+    for (int r = tid; r < R; r += kPrepThreads) s_kids[r] = 0;
+    __syncthreads();
+    for (int r = tid; r < R; r += kPrepThreads) {        // mark every node that has a child
+      const int b = find_request(s_off, B, r);
+      const int u = r - s_off[b], pu = parents[r];
+      if (u > 0 && pu >= 0 && pu < u) s_kids[s_off[b] + pu] = 1;
+    }
+    __syncthreads();
+    // thread t lists the marked rows of [t * per, (t + 1) * per) after those
+    // of the threads before it (block-wide exclusive prefix of the counts)
+    const int per = (R + kPrepThreads - 1) / kPrepThreads;
+    const int r0 = min(R, tid * per), r1 = min(R, r0 + per);
+    int cnt = 0;
+    for (int r = r0; r < r1; ++r) cnt += s_kids[r];
+    int incl = cnt;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int x = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += x;
+    }
+    if (lane == 63) s_wave[wave] = incl;
+    __syncthreads();
+    int base = 0, total = 0;
+    for (int w = 0; w < kPrepThreads / 64; ++w) {
+      if (w < wave) base += s_wave[w];
+      total += s_wave[w];
+    }
+    int pos = np + base + incl - cnt;
+    for (int r = r0; r < r1; ++r)
+      if (s_kids[r]) ws.order[pos++] = R + r;
+    if (tid == 0) ws.sync[2] = np + total;
+  }
+  if (tid == 0) ws.sync[0] = 0;
 }
 
 // ---------------------------------------------------------------------------
 // Statistics.
 
-// Partial statistics of one (row, chunk).  A chunk is kStatF4 float4 per
-// thread (16K logits), held in registers: the row is cut into
-// ws.nch = ceil(V / 16K) chunks so that rows of 128K logits spread over the
-// CUs, and every load of a chunk is in flight at once.
-//  * sampling: (reference, sum of exp(z - reference)) with z = logit / T in
-//    fp64 and the chunk's maximum as the reference, so every exponent is
-//    <= 0 and the per-logit work is branch-free.
-//  * greedy: (max, first argmax) of the target row.
-// Draft rows of leaves are not read (their partials are left empty).
-template <bool kGreedy>
+// Greedy statistics: (max, first argmax) of one target-row chunk per
+// workgroup.  A chunk is kStatF4 float4 per thread (16K logits), held in
+// registers: rows are cut into ws.nch = ceil(V / 16K) chunks so that rows of
+// 128K logits spread over the CUs, and every load of a chunk is in flight at
+// once.
 __global__ void __launch_bounds__(kStatThreads)
-accept_stats_kernel(const int32_t* __restrict__ row_offsets, int B, int R,
-                    const int32_t* __restrict__ parents, const float* __restrict__ p_logits,
-                    const float* __restrict__ q_logits, int64_t ld, int vocab, float temperature,
-                    AcceptWs ws, int row_base) {
-  __shared__ double s_tab[256];
+accept_argmax_kernel(const float* __restrict__ p_logits, int64_t ld, int vocab, AcceptWs ws) {
   __shared__ float red_m[kStatThreads / 64];
   __shared__ int red_a[kStatThreads / 64];
-  __shared__ double red_s[kStatThreads / 64];
-  __shared__ int has_kids;
   const int nch = ws.nch;
   const int chunk = blockIdx.x % nch;
-  const int rr = row_base + blockIdx.x / nch;
-  const int which = rr >= R ? 1 : 0;                   // 0: target p, 1: draft q
-  const int r = rr - which * R;
+  const int r = blockIdx.x / nch;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int slot = rr * nch + chunk;
-  clear_walk_state(ws, B, vocab);
-  if (!kGreedy) load_exp_table(s_tab);
-  if (which == 1) {
-    const int b = request_of_row(row_offsets, B, r);
-    const int o = row_offsets[b];
-    const int n = row_offsets[b + 1] - o;
-    const int u = r - o;
-    if (tid == 0) has_kids = 0;
-    __syncthreads();
-    for (int i = tid; i < n; i += kStatThreads)
-      if (i > 0 && parents[o + i] == u) has_kids = 1;
-    __syncthreads();
-    if (!has_kids) {
-      if (tid == 0) {
-        ws.part_ref[slot] = 0.0;
-        ws.part_s[slot] = 0.0;
-      }
-      return;
+  const float4* row4 = reinterpret_cast<const float4*>(p_logits + (int64_t)r * ld);
+  const int v4 = (vocab + 3) >> 2;
+  const int f_begin = chunk * (kStatThreads * kStatF4);
+  float4 x[kStatF4];
+#pragma unroll
+  for (int k = 0; k < kStatF4; ++k) x[k] = row4[min(f_begin + k * kStatThreads + tid, v4 - 1)];
+  float m = -INFINITY;
+  int am = -1;
+#pragma unroll
+  for (int k = 0; k < kStatF4; ++k) {              // a thread's indices increase with k
+    const int y0 = (f_begin + k * kStatThreads + tid) * 4;
+    const float xs[4] = {x[k].x, x[k].y, x[k].z, x[k].w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const bool gt = y0 + j < vocab && xs[j] > m;   // strict: the first index wins ties
+      m = gt ? xs[j] : m;
+      am = gt ? y0 + j : am;
     }
   }
-  const float* row = (which ? q_logits : p_logits) + (int64_t)r * ld;
-  const float4* row4 = reinterpret_cast<const float4*>(row);
-  const int v4 = (vocab + 3) >> 2;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1)
+    merge_arg(m, am, __shfl_xor(m, off, 64), __shfl_xor(am, off, 64));
+  if (lane == 0) {
+    red_m[wave] = m;
+    red_a[wave] = am;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    for (int w = 1; w < kStatThreads / 64; ++w) merge_arg(m, am, red_m[w], red_a[w]);
+    ws.part_m[r * nch + chunk] = m;
+    ws.part_am[r * nch + chunk] = am;
+  }
+}
+
+// Sampling statistics: one workgroup per (listed row, chunk) item, the
+// listed target rows first (item it < np * nch is target row it / nch, no
+// lookup), then the listed draft rows.  The grid covers every draft row;
+// workgroups past the list end at once, after all the others were
+// dispatched, so they hold no slot while the streaming is under way.  Each
+// item: (reference, sum of exp(z - reference)) with z = logit / T in fp64
+// and the chunk's maximum as the reference, so every exponent is <= 0 and
+// the per-logit work is branch-free.
+struct StatsArgs {
+  const float* p_logits;
+  const float* q_logits;
+  int64_t ld;
+  int vocab, R, np;   // np: target rows listed (R, or 0 when the LM head made their partials)
+  double invT;
+};
+
+__global__ void __launch_bounds__(kStatThreads)
+accept_sample_stats_kernel(StatsArgs a, AcceptWs ws) {
+  __shared__ double s_tab[256];
+  __shared__ float red_m[kStatThreads / 64];
+  __shared__ double red_s[kStatThreads / 64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nch = ws.nch;
+  const int it = blockIdx.x;
+  int e = it / nch;
+  const int chunk = it - e * nch;
+  int rr = e;
+  if (e >= a.np) {
+    if (e >= ws.sync[2]) return;                     // past the listed draft rows
+    rr = ws.order[e];
+  }
+  load_exp_table(s_tab);
+  const int which = rr >= a.R ? 1 : 0;
+  const float4* row4 = reinterpret_cast<const float4*>((which ? a.q_logits : a.p_logits) +
+                                                       (int64_t)(rr - which * a.R) * a.ld);
+  const int v4 = (a.vocab + 3) >> 2;
   const int f_begin = chunk * (kStatThreads * kStatF4);
   // the whole chunk in flight: clamped (in-bounds) loads, masked to -inf
   // (only the row's last chunk can reach past it)
   float4 x[kStatF4];
 #pragma unroll
   for (int k = 0; k < kStatF4; ++k) x[k] = row4[min(f_begin + k * kStatThreads + tid, v4 - 1)];
-  if ((chunk + 1) * kStatChunkLen > vocab) {
+  if ((chunk + 1) * kStatChunkLen > a.vocab) {
 #pragma unroll
     for (int k = 0; k < kStatF4; ++k) {
       const int y0 = (f_begin + k * kStatThreads + tid) * 4;
-      if (y0 + 0 >= vocab) x[k].x = -INFINITY;
-      if (y0 + 1 >= vocab) x[k].y = -INFINITY;
-      if (y0 + 2 >= vocab) x[k].z = -INFINITY;
-      if (y0 + 3 >= vocab) x[k].w = -INFINITY;
+      if (y0 + 0 >= a.vocab) x[k].x = -INFINITY;
+      if (y0 + 1 >= a.vocab) x[k].y = -INFINITY;
+      if (y0 + 2 >= a.vocab) x[k].z = -INFINITY;
+      if (y0 + 3 >= a.vocab) x[k].w = -INFINITY;
     }
-  }
-  if (kGreedy) {
-    float m = -INFINITY;
-    int am = -1;
-#pragma unroll
-    for (int k = 0; k < kStatF4; ++k) {              // a thread's indices increase with k
-      const int y0 = (f_begin + k * kStatThreads + tid) * 4;
-      const float xs[4] = {x[k].x, x[k].y, x[k].z, x[k].w};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const bool gt = xs[j] > m;                   // strict: the first index wins ties
-        m = gt ? xs[j] : m;
-        am = gt ? y0 + j : am;
-      }
-    }
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1)
-      merge_arg(m, am, __shfl_xor(m, off, 64), __shfl_xor(am, off, 64));
-    if (lane == 0) {
-      red_m[wave] = m;
-      red_a[wave] = am;
-    }
-    __syncthreads();
-    if (tid == 0) {
-      for (int w = 1; w < kStatThreads / 64; ++w) merge_arg(m, am, red_m[w], red_a[w]);
-      ws.part_m[slot] = m;
-      ws.part_am[slot] = am;
-    }
-    return;
   }
   float cm = -INFINITY;
 #pragma unroll
@@ -235,15 +319,14 @@ accept_stats_kernel(const int32_t* __restrict__ row_offsets, int B, int R,
   if (lane == 0) red_m[wave] = cm;
   __syncthreads();
   for (int w = 0; w < kStatThreads / 64; ++w) cm = fmaxf(cm, red_m[w]);
-  const double invT = 1.0 / (double)temperature;
-  const double ref = (cm == -INFINITY) ? 0.0 : (double)cm * invT;
+  const double ref = (cm == -INFINITY) ? 0.0 : (double)cm * a.invT;
   double s = 0.0;
 #pragma unroll
   for (int k = 0; k < kStatF4; ++k) {
     double e0, e1, e2, e3;
-    exp_f64_clamped2(fma((double)x[k].x, invT, -ref), fma((double)x[k].y, invT, -ref), s_tab,
+    exp_f64_clamped2(fma((double)x[k].x, a.invT, -ref), fma((double)x[k].y, a.invT, -ref), s_tab,
                      e0, e1);
-    exp_f64_clamped2(fma((double)x[k].z, invT, -ref), fma((double)x[k].w, invT, -ref), s_tab,
+    exp_f64_clamped2(fma((double)x[k].z, a.invT, -ref), fma((double)x[k].w, a.invT, -ref), s_tab,
                      e2, e3);
     s += e0;
     s += e1;
@@ -256,15 +339,15 @@ accept_stats_kernel(const int32_t* __restrict__ row_offsets, int B, int R,
   if (tid == 0) {
     double tot = 0.0;
     for (int w = 0; w < kStatThreads / 64; ++w) tot += red_s[w];
-    ws.part_ref[slot] = ref;
-    ws.part_s[slot] = tot;
+    ws.part_ref[rr * nch + chunk] = ref;
+    ws.part_s[rr * nch + chunk] = tot;
   }
 }
 
 // Target-row chunk partials from the LM head's tile partials: one wave per
 // (row, chunk), one lane per tile of the chunk, merged by a wave reduction
 // into the (reference, sum) / (max, first argmax) forms the statistics pass
-// writes.  Also clears the walk's counters (the statistics pass may not run).
+// writes.
 constexpr int kTilesPerChunk = kStatChunkLen / kHeadTileV;
 static_assert(kStatChunkLen % kHeadTileV == 0 && kTilesPerChunk == kWave,
               "a statistics chunk is one wave of head tiles");
@@ -273,7 +356,6 @@ __global__ void __launch_bounds__(256)
 accept_head_merge_kernel(int B, int R, HeadTiles t, int greedy, AcceptWs ws, int vocab) {
   __shared__ double s_tab[256];
   const int tid = threadIdx.x, lane = tid & 63;
-  clear_walk_state(ws, B, vocab);
   if (!greedy) load_exp_table(s_tab);
   __syncthreads();
   const int nch = ws.nch;
@@ -1200,23 +1282,30 @@ hipError_t launch_accept(const LaunchCtx& cx, int R, const int32_t* parents, con
   const bool greedy = temperature == 0.0f;
   // q_logits == nullptr at T > 0: deterministic children, target rows only.
   // With the LM head's partials, the target rows are merged, not streamed.
-  const int row_base = head ? R : 0;
-  const int rows = ((greedy || !q_logits) ? R : 2 * R) - row_base;
+  hipError_t e;
+  if (!greedy) {
+    // the rows to stream (and the walk's exchange area cleared)
+    const int64_t nseg_all = (int64_t)cx.B * 2 * segs_for(vocab);
+    const int clear_blocks =
+        (int)std::max<int64_t>(1, std::min<int64_t>(256, (nseg_all + kPrepThreads - 1) / kPrepThreads));
+    hipLaunchKernelGGL(accept_prep_kernel, dim3(1 + clear_blocks), dim3(kPrepThreads), 0,
+                       cx.stream, cx.row_offsets_d, cx.B, R, parents, ws, vocab, head ? 0 : 1,
+                       q_logits ? 1 : 0);
+  }
   if (head)
     hipLaunchKernelGGL(accept_head_merge_kernel, dim3((R * nch + 3) / 4), dim3(256), 0,
                        cx.stream, cx.B, R, *head, greedy ? 1 : 0, ws, vocab);
-  if (rows > 0) {
-    if (greedy)
-      hipLaunchKernelGGL(accept_stats_kernel<true>, dim3(rows * nch), dim3(kStatThreads), 0,
-                         cx.stream, cx.row_offsets_d, cx.B, R, parents, p_logits, q_logits, ld,
-                         vocab, temperature, ws, row_base);
-    else
-      hipLaunchKernelGGL(accept_stats_kernel<false>, dim3(rows * nch), dim3(kStatThreads), 0,
-                         cx.stream, cx.row_offsets_d, cx.B, R, parents, p_logits, q_logits, ld,
-                         vocab, temperature, ws, row_base);
+  if (greedy && !head) {
+    hipLaunchKernelGGL(accept_argmax_kernel, dim3(R * nch), dim3(kStatThreads), 0, cx.stream,
+                       p_logits, ld, vocab, ws);
+  } else if (!greedy && (!head || q_logits)) {
+    const int np = head ? 0 : R;
+    const int64_t items = (int64_t)(np + (q_logits ? R : 0)) * nch;
+    StatsArgs sa{p_logits, q_logits, ld, vocab, R, np, 1.0 / (double)temperature};
+    hipLaunchKernelGGL(accept_sample_stats_kernel, dim3((unsigned)items), dim3(kStatThreads), 0,
+                       cx.stream, sa, ws);
   }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if ((e = hipGetLastError()) != hipSuccess) return e;
   WalkOut out{accept_len, path, tokens_out, accept_mask, flags, path_stride, child_p, child_q};
   if (temperature == 0.0f) {
     hipLaunchKernelGGL(accept_finalize_kernel, dim3((R + 255) / 256), dim3(256), 0, cx.stream,
