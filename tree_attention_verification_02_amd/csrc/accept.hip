@@ -17,20 +17,22 @@
 // Kernels:
 //  * accept_prep (T > 0): lists the rows whose statistics are read -- every
 //    target row, and the draft rows of nodes with children (draft rows of
-//    leaves are never read) -- and clears the walk's exchange area.
-//  * accept_sample_stats (T > 0): one workgroup per listed (row, 16K-logit
-//    chunk) item streams its chunk once (16-byte loads) into fp64 partial
-//    sums.
-//  * accept_argmax (T = 0): the first argmax of every target-row chunk;
-//    accept_finalize merges them per row.
-//  * accept_walk: S workgroups ("slices", taken by ticket in start order) per
-//    request; each merges its request's partials into the rows' log-sum-exps
-//    of logits/T and the child probabilities P_u(x_c), Q_u(x_c) itself.
+//    leaves are never read) -- and clears the walk's exchange area and the
+//    statistics partials.
+//  * accept_sample (T > 0), one launch in two parts.  First one workgroup per
+//    listed (row, 16K-logit chunk) item streams its chunk once (16-byte
+//    loads) into fp64 partial sums, published with a tag.  After them come
+//    S workgroups ("slices", taken by ticket in start order) per request,
+//    dispatched as the statistics drain: each loads its tree, merges its
+//    request's partials (polling each until it shows its tag) into the rows'
+//    log-sum-exps of logits/T and the child probabilities P_u(x_c), Q_u(x_c).
 //    Each pass is split over the S slices by 1024-element segments; segment
 //    sums go to global memory carrying their pass tag, and every slice reads
 //    all of them (bounded polls), sums them in the same order and replays
 //    the same scalar decisions, so no further broadcast is needed; slice 0
 //    rescans the drawn segment and writes the outputs.
+//  * accept_argmax (T = 0): the first argmax of every target-row chunk;
+//    accept_finalize merges them per row.
 //  * accept_greedy: temperature 0, one workgroup per request.
 //
 // Deterministic children (no draft rows): each child is a draft from the
@@ -80,8 +82,8 @@ struct AcceptWs {
   float* part_m;    // [R][nch]    chunk max (greedy)
   int32_t* part_am; //                     and its first index
   int32_t* order;   // [2R] rows whose statistics are streamed: rr = r (target), R + r (draft)
-  int32_t* sync;    // [64], own 256 B: [0] the walk's ticket counter (zeroed with seg),
-                    // [2] entries in `order`
+  int32_t* sync;    // [64], own 256 B: [0] the walk's ticket counter, [2] entries in
+                    // `order`
   double* seg;      // [B][2][nseg] per-pass segment sums carrying their pass tag
                     // (double-buffered by pass parity; zeroed before every walk)
 };
@@ -132,7 +134,8 @@ size_t accept_workspace_bytes(int R, int B, int vocab) {
 
 // Before the statistics at T > 0 (accept_prep_kernel): blocks 1.. clear the
 // walk's exchange area (every segment sum to tag 0, which no pass uses) and
-// block 0 resets the walk's ticket counter and lists the rows whose statistics are streamed
+// the statistics partials (tag 0: not yet written); block 0 resets the
+// walk's ticket and item counters and lists the rows whose statistics are streamed
 // -- every target row (unless the LM head has produced their partials),
 // then the draft rows of the nodes that have children (draft rows of leaves
 // are never read).  The children marks live in LDS; beyond its tables every
@@ -160,9 +163,14 @@ accept_prep_kernel(const int32_t* __restrict__ row_offsets, int B, int R,
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   if (blockIdx.x > 0) {
     const int64_t nseg_all = (int64_t)B * 2 * ((vocab + kSeg - 1) / kSeg);
-    for (int64_t i = (int64_t)(blockIdx.x - 1) * kPrepThreads + tid; i < nseg_all;
-         i += (int64_t)(gridDim.x - 1) * kPrepThreads)
+    const int64_t nslot = 2 * (int64_t)R * ws.nch;
+    const int64_t stride = (int64_t)(gridDim.x - 1) * kPrepThreads;
+    for (int64_t i = (int64_t)(blockIdx.x - 1) * kPrepThreads + tid; i < nseg_all; i += stride)
       ws.seg[i] = 0.0;
+    for (int64_t i = (int64_t)(blockIdx.x - 1) * kPrepThreads + tid; i < nslot; i += stride) {
+      ws.part_ref[i] = 0.0;
+      ws.part_s[i] = 0.0;
+    }
     return;
   }
   const int np = list_p ? R : 0;
@@ -275,14 +283,30 @@ struct StatsArgs {
   double invT;
 };
 
-__global__ void __launch_bounds__(kStatThreads)
-accept_sample_stats_kernel(StatsArgs a, AcceptWs ws) {
-  __shared__ double s_tab[256];
-  __shared__ float red_m[kStatThreads / 64];
-  __shared__ double red_s[kStatThreads / 64];
+// The partials are published for the walk workgroups of the same launch: each
+// value carries tag 1 in the low 8 bits of its mantissa (0: not yet written;
+// the partials are cleared before every call), the reference rounded up to
+// 44 mantissa bits before the sum is taken (so it stays >= every z of the
+// chunk and carries its tag exactly), the sum rounded to 44 bits (2^-45
+// relative).  A reader polls each partial until it shows its tag (a shared
+// counter of finished items would serialize ten thousand atomics on one
+// address).
+SPEC_DEVICE double ref_round_up(double v) {
+  const unsigned long long bits = (unsigned long long)__double_as_longlong(v);
+  const unsigned long long r = (v > 0.0) ? ((bits + 0xffull) & ~0xffull) : (bits & ~0xffull);
+  return __longlong_as_double((long long)r);
+}
+SPEC_DEVICE void publish_tagged(double* p, double v) {
+  const unsigned long long bits =
+      (((unsigned long long)__double_as_longlong(v) + 0x80ull) & ~0xffull) | 1ull;
+  __hip_atomic_store(reinterpret_cast<unsigned long long*>(p), bits, __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+
+SPEC_DEVICE void sample_stats_item(const StatsArgs& a, const AcceptWs& ws, int it, double* s_tab,
+                                   float* red_m, double* red_s) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nch = ws.nch;
-  const int it = blockIdx.x;
   int e = it / nch;
   const int chunk = it - e * nch;
   int rr = e;
@@ -319,7 +343,7 @@ accept_sample_stats_kernel(StatsArgs a, AcceptWs ws) {
   if (lane == 0) red_m[wave] = cm;
   __syncthreads();
   for (int w = 0; w < kStatThreads / 64; ++w) cm = fmaxf(cm, red_m[w]);
-  const double ref = (cm == -INFINITY) ? 0.0 : (double)cm * a.invT;
+  const double ref = (cm == -INFINITY) ? 0.0 : ref_round_up((double)cm * a.invT);
   double s = 0.0;
 #pragma unroll
   for (int k = 0; k < kStatF4; ++k) {
@@ -339,15 +363,15 @@ accept_sample_stats_kernel(StatsArgs a, AcceptWs ws) {
   if (tid == 0) {
     double tot = 0.0;
     for (int w = 0; w < kStatThreads / 64; ++w) tot += red_s[w];
-    ws.part_ref[rr * nch + chunk] = ref;
-    ws.part_s[rr * nch + chunk] = tot;
+    publish_tagged(ws.part_ref + rr * nch + chunk, ref);
+    publish_tagged(ws.part_s + rr * nch + chunk, tot);
   }
 }
 
 // Target-row chunk partials from the LM head's tile partials: one wave per
 // (row, chunk), one lane per tile of the chunk, merged by a wave reduction
-// into the (reference, sum) / (max, first argmax) forms the statistics pass
-// writes.
+// into the (reference, sum) partials of the statistics items (published
+// with their tag) or the (max, first argmax) partials of the greedy path.
 constexpr int kTilesPerChunk = kStatChunkLen / kHeadTileV;
 static_assert(kStatChunkLen % kHeadTileV == 0 && kTilesPerChunk == kWave,
               "a statistics chunk is one wave of head tiles");
@@ -381,11 +405,12 @@ accept_head_merge_kernel(int B, int R, HeadTiles t, int greedy, AcceptWs ws, int
   double top = ref;
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) top = fmax(top, __shfl_xor(top, off, 64));
-  const double s = has ? t.s[at] * exp_f64(ref - top, s_tab) : 0.0;
+  top = (top == -INFINITY) ? 0.0 : ref_round_up(top);
+  const double s = (has && ref != -INFINITY) ? t.s[at] * exp_f64(ref - top, s_tab) : 0.0;
   const double tot = wave_sum(s);
   if (lane == 0) {
-    ws.part_ref[idx] = top;
-    ws.part_s[idx] = tot;
+    publish_tagged(ws.part_ref + idx, top);
+    publish_tagged(ws.part_s + idx, tot);
   }
 }
 
@@ -394,30 +419,46 @@ accept_head_merge_kernel(int B, int R, HeadTiles t, int greedy, AcceptWs ws, int
 // own rows; the partials are loaded 8 at a time, all in flight together), or
 // the target argmax.  accept_finalize (greedy): one thread per row writes the
 // argmax and, per child, 1 if its token is the parent's argmax.
-SPEC_DEVICE void merged_ref_sum(const AcceptWs& ws, int rr, const double* tab, double& lse) {
+SPEC_DEVICE unsigned long long load_partial(const double* p) {
+  return __hip_atomic_load(reinterpret_cast<unsigned long long*>(const_cast<double*>(p)),
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// False if some partial never showed its tag (the polls gave up).
+SPEC_DEVICE bool merged_ref_sum(const AcceptWs& ws, int rr, const double* tab, double& lse) {
   const int nch = ws.nch;
   const double* pr = ws.part_ref + (int64_t)rr * nch;
   const double* ps = ws.part_s + (int64_t)rr * nch;
   double ref = 0.0, s = 0.0;
+  bool ok = true;
   for (int c0 = 0; c0 < nch; c0 += 8) {
-    double r8[8], s8[8];
+    unsigned long long r8[8], s8[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      r8[j] = (c0 + j < nch) ? pr[c0 + j] : 0.0;
-      s8[j] = (c0 + j < nch) ? ps[c0 + j] : 0.0;
+      r8[j] = (c0 + j < nch) ? load_partial(pr + c0 + j) : 1ull;
+      s8[j] = (c0 + j < nch) ? load_partial(ps + c0 + j) : 1ull;
     }
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       if (c0 + j >= nch) break;
+      int spins = 0;
+      while (((r8[j] & s8[j]) & 0xffull) == 0 && ++spins <= kWalkMaxSpins) {
+        __builtin_amdgcn_s_sleep(1);
+        r8[j] = load_partial(pr + c0 + j);
+        s8[j] = load_partial(ps + c0 + j);
+      }
+      ok &= ((r8[j] & s8[j]) & 0xffull) != 0;
+      const double rj = __longlong_as_double((long long)(r8[j] & ~0xffull));
+      const double sj = __longlong_as_double((long long)(s8[j] & ~0xffull));
       if (c0 + j == 0) {
-        ref = r8[0];
-        s = s8[0];
+        ref = rj;
+        s = sj;
       } else {
-        merge_ref(ref, s, r8[j], s8[j], tab);
+        merge_ref(ref, s, rj, sj, tab);
       }
     }
   }
   lse = ref + log(s);
+  return ok;
 }
 SPEC_DEVICE int merged_argmax(const AcceptWs& ws, int r) {
   const int nch = ws.nch;
@@ -462,7 +503,8 @@ struct WalkShared {
   double cq[kMaxRows];
   double lse[2][kMaxRows];          // log-sum-exp of logits / T: target, draft rows
   double tab[256];
-  double wave_tot[kWalkWaves];      // per wave (draw rescan)
+  double wave_tot[kWalkWaves];      // per wave (draw rescan, statistics item)
+  float red_m[kWalkWaves];          // per wave (statistics item)
   double part[kPassChunk][kWalkWaves];  // per segment and wave (pass)
   double lane_excl[64];             // prefix of the segment sums, per lane block
   double total;
@@ -976,26 +1018,37 @@ SPEC_DEVICE void walk_decide(WalkShared& sh, WalkState& st, uint64_t seed, uint6
   }
 }
 
+// Statistics and walk in one launch: blocks [0, nstat) are statistics items
+// (sample_stats_item), the B * S after them the walk's workgroups, which are
+// dispatched as the statistics drain and load their trees meanwhile; each
+// then polls the partials of its rows until they are published (a bounded
+// wait: a request whose partials never arrive reports a timeout).
 __global__ void __launch_bounds__(kWalkThreads, 4)
-accept_walk_kernel(const int32_t* __restrict__ row_offsets, int R, int S,
-                   const int32_t* __restrict__ parents, const int32_t* __restrict__ tokens,
-                   const float* __restrict__ p_logits, const float* __restrict__ q_logits,
-                   int64_t ld, int vocab, float temperature, uint64_t seed, uint64_t step,
-                   AcceptWs ws, WalkOut out, int max_spins) {
+accept_sample_kernel(StatsArgs sa, int nstat, const int32_t* __restrict__ row_offsets, int B,
+                     int R, int S, const int32_t* __restrict__ parents,
+                     const int32_t* __restrict__ tokens, const float* __restrict__ p_logits,
+                     const float* __restrict__ q_logits, int64_t ld, int vocab,
+                     float temperature, uint64_t seed, uint64_t step, AcceptWs ws, WalkOut out,
+                     int max_spins) {
   __shared__ WalkShared sh;
   __shared__ WalkState st;
+  if ((int)blockIdx.x < nstat) {
+    sample_stats_item(sa, ws, (int)blockIdx.x, sh.tab, sh.red_m, sh.wave_tot);
+    return;
+  }
   // (request, slice) by ticket, in the order the workgroups start running:
   // the lowest unfinished request then always has all its slices running
   // or next in line, so the per-request barriers make progress whenever S
   // workgroups fit on the device at once (no cooperative launch needed).
   __shared__ int s_ticket;
   if (threadIdx.x == 0)
-    s_ticket = (S == 1) ? (int)blockIdx.x
+    s_ticket = (S == 1) ? (int)blockIdx.x - nstat
                         : __hip_atomic_fetch_add(ws.sync, 1, __ATOMIC_RELAXED,
                                                  __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
   const int b = s_ticket / S;
   const int slice = s_ticket % S;
+  if (b < 0 || b >= B) return;                       // (not reached: B * S walk workgroups)
   const int o = row_offsets[b];
   const int n = row_offsets[b + 1] - o;
   const int tid = threadIdx.x;
@@ -1027,7 +1080,10 @@ accept_walk_kernel(const int32_t* __restrict__ row_offsets, int R, int S,
         cval[j] = true;
         clog[j] = ((which ? q_logits : p_logits) + (int64_t)(o + pu) * ld)[x];
       }
-      merged_ref_sum(ws, which * R + o + i, sh.tab, sh.lse[which][i]);
+      // (draft rows only of nodes with children: the others are not streamed)
+      if (!sh.bad && (!which || sh.kid_start[i + 1] > sh.kid_start[i]) &&
+          !merged_ref_sum(ws, which * R + o + i, sh.tab, sh.lse[which][i]))
+        sh.timeout = 1;
     }
   }
   __syncthreads();
@@ -1040,7 +1096,7 @@ accept_walk_kernel(const int32_t* __restrict__ row_offsets, int R, int S,
     float* dst = which ? out.child_q : out.child_p;
     const int pu = sh.par[i];
     double val = __longlong_as_double(0x7ff8000000000000LL);
-    if (i > 0 && pu >= 0 && pu < i && !(which && topk)) {
+    if (!sh.bad && i > 0 && pu >= 0 && pu < i && !(which && topk)) {   // (NaN: invalid tree)
       val = cval[j] ? exp_f64((double)clog[j] * invT - sh.lse[which][pu], sh.tab) : 0.0;
       (which ? sh.cq : sh.cp)[i] = val;
     }
@@ -1049,6 +1105,10 @@ accept_walk_kernel(const int32_t* __restrict__ row_offsets, int R, int S,
   __syncthreads();
   if (sh.bad) {
     if (slice == 0) write_abandoned(out, b, o, n, kFlagBadTree);
+    return;
+  }
+  if (sh.timeout) {
+    if (slice == 0) write_abandoned(out, b, o, n, kFlagSyncTimeout);
     return;
   }
   WalkCtx c;
@@ -1251,7 +1311,7 @@ static hipError_t walk_capacity(int dev, int* capacity) {
   hipError_t e;
   if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess)
     return e;
-  if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, accept_walk_kernel, kWalkThreads,
+  if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, accept_sample_kernel, kWalkThreads,
                                                         0)) != hipSuccess)
     return e;
   *capacity = cus * per_cu;
@@ -1276,6 +1336,7 @@ hipError_t launch_accept(const LaunchCtx& cx, int R, const int32_t* parents, con
                          uint8_t* accept_mask, float* child_p, float* child_q, int32_t* flags,
                          void* workspace, WalkKnobs walk, const HeadTiles* head) {
   static_assert(sizeof(WalkShared) < 20480, "walk LDS");
+  static_assert(kStatThreads == kWalkThreads, "statistics items run in walk-sized workgroups");
   static_assert(kWalkThreads >= kMaxRows && kWalkThreads >= 256, "load_tree: a thread per row and table entry");
   AcceptWs ws = accept_ws(workspace, R, cx.B, vocab);
   const int nch = ws.nch;
@@ -1283,6 +1344,8 @@ hipError_t launch_accept(const LaunchCtx& cx, int R, const int32_t* parents, con
   // q_logits == nullptr at T > 0: deterministic children, target rows only.
   // With the LM head's partials, the target rows are merged, not streamed.
   hipError_t e;
+  int nstat = 0;
+  StatsArgs stats_args{p_logits, q_logits, ld, vocab, R, 0, 1.0 / (double)temperature};
   if (!greedy) {
     // the rows to stream (and the walk's exchange area cleared)
     const int64_t nseg_all = (int64_t)cx.B * 2 * segs_for(vocab);
@@ -1299,11 +1362,8 @@ hipError_t launch_accept(const LaunchCtx& cx, int R, const int32_t* parents, con
     hipLaunchKernelGGL(accept_argmax_kernel, dim3(R * nch), dim3(kStatThreads), 0, cx.stream,
                        p_logits, ld, vocab, ws);
   } else if (!greedy && (!head || q_logits)) {
-    const int np = head ? 0 : R;
-    const int64_t items = (int64_t)(np + (q_logits ? R : 0)) * nch;
-    StatsArgs sa{p_logits, q_logits, ld, vocab, R, np, 1.0 / (double)temperature};
-    hipLaunchKernelGGL(accept_sample_stats_kernel, dim3((unsigned)items), dim3(kStatThreads), 0,
-                       cx.stream, sa, ws);
+    stats_args.np = head ? 0 : R;
+    nstat = (stats_args.np + (q_logits ? R : 0)) * nch;
   }
   if ((e = hipGetLastError()) != hipSuccess) return e;
   WalkOut out{accept_len, path, tokens_out, accept_mask, flags, path_stride, child_p, child_q};
@@ -1321,10 +1381,11 @@ hipError_t launch_accept(const LaunchCtx& cx, int R, const int32_t* parents, con
   int S = walk_slices(cx.B, vocab, capacity);
   if (walk.max_slices > 0) S = walk.max_slices < S ? walk.max_slices : S;
   const int max_spins = walk.max_spins >= 0 ? walk.max_spins : kWalkMaxSpins;
-  // S > 1: B * S <= capacity workgroups, which take tickets (see the kernel).
-  hipLaunchKernelGGL(accept_walk_kernel, dim3(cx.B * S), dim3(kWalkThreads), 0, cx.stream,
-                     cx.row_offsets_d, R, S, parents, tokens, p_logits, q_logits, ld, vocab,
-                     temperature, seed, step, ws, out, max_spins);
+  // nstat statistics items, then B * S <= capacity walk workgroups, which
+  // take tickets (see the kernel).
+  hipLaunchKernelGGL(accept_sample_kernel, dim3(nstat + cx.B * S), dim3(kWalkThreads), 0,
+                     cx.stream, stats_args, nstat, cx.row_offsets_d, cx.B, R, S, parents, tokens,
+                     p_logits, q_logits, ld, vocab, temperature, seed, step, ws, out, max_spins);
   return hipGetLastError();
 }
 

@@ -8,21 +8,31 @@
 // head h / G.
 //
 // bf16 path (MFMA, gfx950):
-//  * One workgroup = 4 waves = up to 128 query rows of one (request, KV head);
-//    a query row is (tree row, head within the GQA group).  All 128 rows
-//    share every K/V tile read from HBM.
+//  * A unit is (request, KV head, row block); its query rows are (tree row,
+//    head within the GQA group) pairs, 32 per wave.  One workgroup = 8 waves
+//    (256 rows); when some unit has more than 256 rows (the 46-row K-schedule
+//    tree x 8 heads of a group = 368) every workgroup takes 12 waves (384
+//    rows, three per SIMD), so such a unit still reads each K/V tile once.
 //  * Keys are cut into splits (split-KV) so long and short requests spread
-//    over all CUs; a second kernel merges split partials by log-sum-exp.
+//    over all CUs; attn_combine merges split partials by log-sum-exp.  With
+//    mixed lengths, heavy units get shorter splits, and workgroups take work
+//    items by ticket in start order: first the leading splits, then the last
+//    split of every unit longest-first, which evens out ragged prefixes.
 //  * Scores are formed transposed, S^T = K Q^T, with
-//    v_mfma_f32_32x32x16_bf16: each lane then owns one query row (column of
-//    S^T), so the online-softmax rescale of that row's output is lane-local,
-//    and P^T is already in the B-operand layout of O^T = V^T P^T.
-//  * K tiles are kept row-major in LDS; V tiles are transposed on the way in
-//    (4 keys x 8 dims per thread, repacked in registers) so the V^T operand
-//    is two 8-byte LDS reads per MFMA.  Global loads are 16 B per lane,
-//    staged in registers one tile ahead (double-buffered LDS).
-//  * Softmax is fp32 in the exp2 domain; masking costs nothing on tiles that
-//    lie wholly inside the prefix.
+//    v_mfma_f32_32x32x16_bf16: each lane owns one query row (a column of
+//    S^T), so the online-softmax rescale of that row is lane-local, and P^T
+//    is already in the B-operand layout of O^T = V^T P^T; row sums and the
+//    two 32-lane halves meet through v_permlane32_swap.
+//  * K/V tiles of 64 keys go from HBM straight into a 4-stage LDS ring
+//    (global_load_lds with 8 waves, buffer loads to LDS with 12), 16 bytes
+//    per lane, three tiles in flight while one is consumed; one barrier per
+//    tile.  V^T operands come from LDS with ds_read_tr16_b64 (a transposing
+//    read), so V needs no repacking.  Scheduling-group hints interleave the
+//    LDS reads with the MFMAs.
+//  * Softmax is fp32 in the exp2 domain with a lazy reference: a row's
+//    maximum only moves when a score exceeds it by more than kLazyMax, so
+//    the O / l rescale is rare.  Ancestor masks (packed 64-bit words per row)
+//    are applied only on tiles that reach the tree's own keys.
 #include <math.h>
 
 #include <algorithm>
