@@ -216,18 +216,22 @@ spec_status spec_tree_attn_verify(const spec_batch *batch, const spec_kv *kv,
  *                      the final (corrected or bonus) token, then -1
  *   accept_mask_d [R]  1 on rows of the accepted path (root included), else 0 (optional)
  *   child_p_d     [R]  P_parent(c)(token c); NaN at roots (optional).  At T = 0:
- *                      1 if token c is the parent's argmax, else 0.
- *   child_q_d     [R]  Q_parent(c)(token c); NaN at roots; untouched at T = 0 (optional)
+ *                      1 if token c is the parent's argmax, else 0.  At T > 0
+ *                      NaN on every row of a request whose tree is invalid.
+ *   child_q_d     [R]  Q_parent(c)(token c); NaN at roots and on every row of an
+ *                      invalid tree; untouched at T = 0 (optional)
  *   flags_d       [B]  SPEC_FLAG_* bits (optional)
  * workspace >= spec_accept_workspace_bytes(batch, vocab) bytes (no init needed).
  *
  * At T > 0 a request's walk may be shared by several workgroups that meet
  * once per vocabulary pass; the library launches only as many as fit on the
- * device together.  If other work holds the compute units so long that a
- * meeting does not complete within a bounded wait (about 2^21 polls), that
- * request comes back with accept_len = -1, path and tokens all -1, an empty
- * accept mask and SPEC_FLAG_SYNC_TIMEOUT; every kernel still ends.  Any
- * other request's outputs are complete and exact.
+ * device together, in the same launch as the vocabulary statistics they
+ * read.  If other work holds the compute units so long that a meeting, or
+ * a statistics partial the walk needs, does not complete within a bounded
+ * wait (about 2^21 polls), that request comes back with accept_len = -1,
+ * path and tokens all -1, an empty accept mask and SPEC_FLAG_SYNC_TIMEOUT;
+ * every kernel still ends.  Any other request's outputs are complete and
+ * exact.
  */
 #define SPEC_FLAG_ZERO_RESIDUAL 1   /* a residual had zero mass; R kept unchanged */
 #define SPEC_FLAG_PATH_TRUNCATED 2  /* path longer than path_stride; walk cut short */
