@@ -314,6 +314,13 @@ def test_device_side_tree_validation(lib):
     alen = vs.acc.accept_len.cpu().numpy()
     assert flags[2] == L.SPEC_FLAG_BAD_TREE and alen[2] == -1
     assert flags[4] == L.SPEC_FLAG_BAD_TREE and alen[4] == -1
+    # the child probabilities of an invalid tree are NaN (T > 0)
+    assert vs.temperature > 0
+    cp = vs.acc.child_p.cpu().numpy()
+    cq = vs.acc.child_q.cpu().numpy()
+    for b in (2, 4):
+        lo, hi = int(w.row_offsets[b]), int(w.row_offsets[b + 1])
+        assert np.isnan(cp[lo:hi]).all() and np.isnan(cq[lo:hi]).all()
 
 
 def test_path_truncation_flag(lib):
