@@ -71,6 +71,8 @@ constexpr int kPassChunk = 64;                // segments per partial-sum flush
 constexpr int kMaxSlices = 32;                // more pollers per counter cost more than they save
 constexpr int kMaxDevices = 64;
 constexpr int kWalkMaxSpins = 1 << 21;       // barrier polls before a walk gives up
+constexpr int kMaxSegs = (kMaxVocab + kSeg - 1) / kSeg;
+constexpr int kSumLoads = 2;                  // segment sums per lane whose loads go out together
 
 // ---------------------------------------------------------------------------
 // Workspace.
@@ -230,8 +232,8 @@ accept_argmax_kernel(const float* __restrict__ p_logits, int64_t ld, int vocab, 
   __shared__ float red_m[kStatThreads / 64];
   __shared__ int red_a[kStatThreads / 64];
   const int nch = ws.nch;
-  const int chunk = blockIdx.x % nch;
   const int r = blockIdx.x / nch;
+  const int chunk = (blockIdx.x - r * nch + r) % nch;    // rotated: see sample_stats_item
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const float4* row4 = reinterpret_cast<const float4*>(p_logits + (int64_t)r * ld);
   const int v4 = (vocab + 3) >> 2;
@@ -308,7 +310,10 @@ SPEC_DEVICE void sample_stats_item(const StatsArgs& a, const AcceptWs& ws, int i
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nch = ws.nch;
   int e = it / nch;
-  const int chunk = it - e * nch;
+  // Consecutive workgroups go to the eight XCDs in turn, so chunk k of every
+  // row would land on one XCD; rotating the chunk by the entry spreads each
+  // chunk position (the ragged last one in particular) over all of them.
+  const int chunk = (it - e * nch + e) % nch;
   int rr = e;
   if (e >= a.np) {
     if (e >= ws.sync[2]) return;                     // past the listed draft rows
@@ -502,6 +507,8 @@ struct WalkShared {
   double cp[kMaxRows];              // P_parent(x_c), Q_parent(x_c) of each child row
   double cq[kMaxRows];
   double lse[2][kMaxRows];          // log-sum-exp of logits / T: target, draft rows
+  double coin[2][kMaxRows];         // row k: coin of the accept test of child k, of the draw at k
+  double segsum[kMaxSegs];          // the last pass's segment sums
   double tab[256];
   double wave_tot[kWalkWaves];      // per wave (draw rescan, statistics item)
   float red_m[kWalkWaves];          // per wave (statistics item)
@@ -695,11 +702,32 @@ SPEC_DEVICE double walk_pass(WalkShared& sh, const WalkCtx& c, int pass, double 
     const int per = (c.nseg + 63) / 64;
     double part = 0.0;
     bool late = false;
-    for (int k = 0; k < per; ++k) {
+    // the first kSumLoads sums of the lane in one round trip; a slot that
+    // does not show the tag yet is polled
+    const double* mine = seg + lane * per;
+    unsigned long long first[kSumLoads];
+#pragma unroll
+    for (int k = 0; k < kSumLoads; ++k)
+      first[k] = (k < per && lane * per + k < c.nseg) ? load_tagged(mine + k) : 0ull;
+#pragma unroll
+    for (int k = 0; k < kSumLoads; ++k) {
+      const int sidx = lane * per + k;
+      if (k < per && sidx < c.nseg) {
+        double v;
+        if ((int)(first[k] & 0xffull) == tag)
+          v = tagged_value(first[k]);
+        else
+          late |= !read_sum(mine + k, tag, c.max_spins, v);
+        sh.segsum[sidx] = v;
+        part += v;
+      }
+    }
+    for (int k = kSumLoads; k < per; ++k) {
       const int sidx = lane * per + k;
       if (sidx < c.nseg) {
         double v;
         late |= !read_sum(&seg[sidx], tag, c.max_spins, v);
+        sh.segsum[sidx] = v;
         part += v;
       }
     }
@@ -712,13 +740,12 @@ SPEC_DEVICE double walk_pass(WalkShared& sh, const WalkCtx& c, int pass, double 
   return sh.total;
 }
 
-// Inverse-CDF draw from the weights of pass `pass` with coin r: every slice
-// finds the segment from the published sums; slice 0 rescans it and returns
-// the token (other slices return -1).
-SPEC_DEVICE int walk_draw(WalkShared& sh, const WalkCtx& c, int pass, double t, bool need_q,
+// Inverse-CDF draw from the weights of the last pass with coin r: every
+// slice finds the segment from that pass's sums (kept in LDS by walk_pass);
+// slice 0 rescans it and returns the token (other slices return -1).
+SPEC_DEVICE int walk_draw(WalkShared& sh, const WalkCtx& c, double t, bool need_q,
                           double r) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const double* seg = c.seg + (pass & 1) * c.nseg;
   const double target = r * sh.total;
   if (wave == 0) {
     const int per = (c.nseg + 63) / 64;
@@ -728,7 +755,7 @@ SPEC_DEVICE int walk_draw(WalkShared& sh, const WalkCtx& c, int pass, double t, 
     for (int k = 0; k < per; ++k) {
       const int sidx = lane * per + k;
       if (sidx < c.nseg) {
-        const double v = tagged_value(load_tagged(&seg[sidx]));
+        const double v = sh.segsum[sidx];
         const double nxt = cum + v;
         if (hit < 0 && nxt > target) {
           hit = sidx;
@@ -945,10 +972,9 @@ struct WalkState {
 };
 
 // Thread 0: run sibling tests and moves until a vocabulary pass (or a draw)
-// is needed.  Coins: purpose 0 for the accept test of child c, purpose 1 for
-// the draw at the node where the walk stops.
-SPEC_DEVICE void walk_decide(WalkShared& sh, WalkState& st, uint64_t seed, uint64_t step, int b,
-                             int path_stride, bool topk) {
+// is needed.  Coins (sh.coin): purpose 0 for the accept test of child c,
+// purpose 1 for the draw at the node where the walk stops.
+SPEC_DEVICE void walk_decide(WalkShared& sh, WalkState& st, int path_stride, bool topk) {
   while (true) {
     const int u = st.u;
     const int k0 = sh.kid_start[u], k1 = sh.kid_start[u + 1];
@@ -977,7 +1003,7 @@ SPEC_DEVICE void walk_decide(WalkShared& sh, WalkState& st, uint64_t seed, uint6
     const int ch = sh.kid_list[st.kidx];
     const int x = sh.tok[ch];
     const double Px = sh.cp[ch], Qx = sh.cq[ch];
-    const double r = verify_uniform(seed, step, (uint64_t)b, (uint64_t)ch, 0);
+    const double r = sh.coin[0][ch];
     bool seen = false;                   // deterministic children: x rejected before has R(x) = 0
     if (topk)
       for (int k = 0; k < sh.nrej; ++k) seen |= (sh.rej[k] == x);
@@ -1053,6 +1079,12 @@ accept_sample_kernel(StatsArgs sa, int nstat, const int32_t* __restrict__ row_of
   const int n = row_offsets[b + 1] - o;
   const int tid = threadIdx.x;
   if (tid == 0) sh.timeout = 0;
+  // Every coin the walk can use, drawn in parallel: purpose 0 for the accept
+  // test of child row k, purpose 1 for the draw at node k.
+  if (tid < n) {
+    sh.coin[0][tid] = verify_uniform(seed, step, (uint64_t)b, (uint64_t)tid, 0);
+    sh.coin[1][tid] = verify_uniform(seed, step, (uint64_t)b, (uint64_t)tid, 1);
+  }
   load_tree(sh, parents, tokens, o, n, sh.tab);
   // This request's row statistics: each row's log-sum-exp from its chunk
   // partials (in chunk order), then each child's P_u(x_c), Q_u(x_c) in fp64.
@@ -1138,7 +1170,7 @@ accept_sample_kernel(StatsArgs sa, int nstat, const int32_t* __restrict__ row_of
   int final_token = -1;
   while (true) {
     if (tid == 0)
-      walk_decide(sh, st, seed, step, b, out.path_stride, topk);
+      walk_decide(sh, st, out.path_stride, topk);
     __syncthreads();
     const int action = st.action;
     if (action == 3) break;
@@ -1170,10 +1202,10 @@ accept_sample_kernel(StatsArgs sa, int nstat, const int32_t* __restrict__ row_of
       }
     }
     // draw from the weights the last pass left
-    const double r = verify_uniform(seed, step, (uint64_t)b, (uint64_t)u, 1);
+    const double r = sh.coin[1][u];
     const double dt = (action == 2) ? st.pass_t : act_t;
     const bool dq = (action == 2) ? true : act_q;
-    final_token = walk_draw(sh, c, pass, dt, dq, r);
+    final_token = walk_draw(sh, c, dt, dq, r);
     break;
   }
   // Only slice 0 writes: it passed every barrier of the walk (then every sum
@@ -1335,7 +1367,8 @@ hipError_t launch_accept(const LaunchCtx& cx, int R, const int32_t* parents, con
                          int32_t* accept_len, int32_t* path, int32_t* tokens_out,
                          uint8_t* accept_mask, float* child_p, float* child_q, int32_t* flags,
                          void* workspace, WalkKnobs walk, const HeadTiles* head) {
-  static_assert(sizeof(WalkShared) < 20480, "walk LDS");
+  static_assert(sizeof(WalkShared) + sizeof(WalkState) <= 160 * 1024 / 4,
+                "walk LDS: four workgroups per CU (160 KB of LDS)");
   static_assert(kStatThreads == kWalkThreads, "statistics items run in walk-sized workgroups");
   static_assert(kWalkThreads >= kMaxRows && kWalkThreads >= 256, "load_tree: a thread per row and table entry");
   AcceptWs ws = accept_ws(workspace, R, cx.B, vocab);

@@ -43,7 +43,7 @@ spec_status ok() {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-constexpr int kMaxVocab = 1 << 20;
+using spec::kMaxVocab;
 
 spec_status check_batch(const spec_batch* bt, int* R_out) {
   if (!bt) return fail(SPEC_ERR_NULL, "batch is NULL");

@@ -11,6 +11,7 @@ constexpr int kWave = 64;
 constexpr int kMaxRows = 256;      // rows per request, root included
 constexpr int kMaxWords = 4;       // kMaxRows / 64
 constexpr int kBlock = 16;         // paged KV block (tokens)
+constexpr int kMaxVocab = 1 << 20;  // vocabulary entries the acceptance supports
 
 // Acceptance flags (same values as SPEC_FLAG_* in the public header).
 constexpr int kFlagZeroResidual = 1;
