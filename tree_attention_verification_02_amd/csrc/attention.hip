@@ -822,18 +822,47 @@ __global__ void __launch_bounds__(W * 64, 1) attn_bf16_kernel(AttnArgs a) {
   }
 }
 
+// Arguments of the combine: the main kernel's partials and unit tables, and
+// which (unit, 32-row chunk) each workgroup takes.
+struct CombineArgs {
+  const float* part;
+  const float* part_ml;
+  const int* unit_desc;
+  const int* unit_items;
+  int max_ns;
+  int hq;
+  int G;
+  void* out;
+  int out_f32;
+  unsigned* ticket;   // the main kernel's item counter, reset here for the next call
+  int chunks;         // workgroups per unit (enough for its rows)
+  int hkv;
+  int nreq;           // > 0: only the units of req[0 .. nreq) (unit = b * hkv + KV head)
+  uint16_t req[kLptMax];
+};
+
 // Merge split partials.  One workgroup per 32 query rows of one (request, KV
 // head, row block); each thread merges one float4 column of a row over the
 // splits in one pass with a running maximum (coalesced 512-byte rows of
-// partials; weights exp2(m_s - m)).
+// partials; weights exp2(m_s - m)).  The grid covers only chunks that can
+// hold rows (and, when the requests are listed, only units with partials),
+// so few workgroups start just to find nothing to do.
 template <int D, int W>
-__global__ void __launch_bounds__(256) attn_combine_kernel(AttnArgs a) {
-  constexpr int ROWS = W * kRowsPerWave;
-  constexpr int CHUNKS = ROWS / kCombineRows;
+__global__ void __launch_bounds__(256) attn_combine_kernel(CombineArgs a) {
   constexpr int C4 = D / 4;                        // float4 per row
   constexpr int RPI = 256 / C4;                    // rows per pass of the block
-  const int64_t unit = blockIdx.x / CHUNKS;
-  const int chunk = blockIdx.x % CHUNKS;
+  int64_t unit;
+  int chunk;
+  if (a.nreq > 0) {
+    const int per_req = a.hkv * a.chunks;
+    const int i = blockIdx.x / per_req;
+    const int rem = blockIdx.x - i * per_req;
+    unit = (int64_t)a.req[i] * a.hkv + rem / a.chunks;
+    chunk = rem % a.chunks;
+  } else {
+    unit = blockIdx.x / a.chunks;
+    chunk = blockIdx.x % a.chunks;
+  }
   const int4 d0 = *reinterpret_cast<const int4*>(a.unit_desc + unit * 8);
   const int2 d1 = *reinterpret_cast<const int2*>(a.unit_desc + unit * 8 + 4);
   const int kvh = d0.y, rb = d0.z, ns = d0.w, o = d1.x, m_blk = d1.y;
@@ -852,6 +881,7 @@ __global__ void __launch_bounds__(256) attn_combine_kernel(AttnArgs a) {
   // loads are unconditional (row index clamped) so that all of them are in
   // flight together.
   constexpr int NP = kCombineRows / RPI;
+  constexpr int ROWS = W * kRowsPerWave;
   const int c4 = threadIdx.x % C4;
   const int rsub = threadIdx.x / C4;
   float mx[NP], l[NP];
@@ -1054,16 +1084,25 @@ AttnPlan plan_attention(int B, const int32_t* row_offsets_h, const int32_t* pref
   }
   p.lpt = (B <= kLptMax) ? 1 : 0;
   p.max_ns = 1;
+  int comb_rows = 0;
+  bool one_block = B <= kLptMax;
+  p.comb_nreq = 0;
   for (int b = 0; b < B; ++b) {
     const int n = row_offsets_h[b + 1] - row_offsets_h[b];
     const int ns = attn_splits(prefix_len_h[b] + n,
                                attn_split_for(p.split_keys, n, G, p.rows_per_block, p.weighted));
     p.max_ns = std::max(p.max_ns, ns);
-    const int64_t per = (int64_t)hkv * attn_row_blocks(n, G, p.rows_per_block);
+    const int nrb = attn_row_blocks(n, G, p.rows_per_block);
+    const int64_t per = (int64_t)hkv * nrb;
     p.items += per * ns;
     p.items_a += per * (ns - p.lpt);
     if (ns > 1) p.partial_items += per * ns;
+    comb_rows = std::max(comb_rows, std::min(n * G, p.rows_per_block));
+    one_block = one_block && nrb == 1;
+    if (one_block && ns > 1) p.comb_req[p.comb_nreq++] = (uint16_t)b;
   }
+  p.comb_chunks = std::max(1, (comb_rows + kCombineRows - 1) / kCombineRows);
+  if (!one_block) p.comb_nreq = 0;
   if (p.lpt) {
     // second phase: requests by the estimated time of their last split,
     // longest first (ties by request index): its keys, 1.5x for heavy units
@@ -1132,23 +1171,41 @@ hipError_t launch_attention_bf16(const LaunchCtx& cx, const AttnPlan& plan, cons
   const int W = plan.rows_per_block / kRowsPerWave;
   if (W * kRowsPerWave != plan.rows_per_block || (W != kWaves && W != kWideWaves))
     return hipErrorInvalidValue;
-  const dim3 cgrid((unsigned)(plan.units * (plan.rows_per_block / kCombineRows)));
+  CombineArgs ca;
+  ca.part = a.part;
+  ca.part_ml = a.part_ml;
+  ca.unit_desc = a.unit_desc;
+  ca.unit_items = a.unit_items;
+  ca.max_ns = a.max_ns;
+  ca.hq = hq;
+  ca.G = a.G;
+  ca.out = out;
+  ca.out_f32 = out_f32;
+  ca.ticket = a.ticket;
+  ca.chunks = plan.comb_chunks;
+  ca.hkv = addr.hkv;
+  ca.nreq = plan.comb_nreq;
+  std::copy(plan.comb_req, plan.comb_req + plan.comb_nreq, ca.req);
+  const int64_t cwg = (plan.comb_nreq > 0 ? (int64_t)plan.comb_nreq * addr.hkv : plan.units) *
+                      plan.comb_chunks;
+  if (plan.partial_items && (cwg <= 0 || cwg > 0x7fffffff)) return hipErrorInvalidValue;
+  const dim3 cgrid((unsigned)cwg);
   if (addr.d == 128 && W == kWaves) {
     hipLaunchKernelGGL((attn_bf16_kernel<128, kWaves>), grid, dim3(W * 64), 0, cx.stream, a);
     if (plan.partial_items)
-      hipLaunchKernelGGL((attn_combine_kernel<128, kWaves>), cgrid, dim3(256), 0, cx.stream, a);
+      hipLaunchKernelGGL((attn_combine_kernel<128, kWaves>), cgrid, dim3(256), 0, cx.stream, ca);
   } else if (addr.d == 128) {
     hipLaunchKernelGGL((attn_bf16_kernel<128, kWideWaves>), grid, dim3(W * 64), 0, cx.stream, a);
     if (plan.partial_items)
-      hipLaunchKernelGGL((attn_combine_kernel<128, kWideWaves>), cgrid, dim3(256), 0, cx.stream, a);
+      hipLaunchKernelGGL((attn_combine_kernel<128, kWideWaves>), cgrid, dim3(256), 0, cx.stream, ca);
   } else if (W == kWaves) {
     hipLaunchKernelGGL((attn_bf16_kernel<64, kWaves>), grid, dim3(W * 64), 0, cx.stream, a);
     if (plan.partial_items)
-      hipLaunchKernelGGL((attn_combine_kernel<64, kWaves>), cgrid, dim3(256), 0, cx.stream, a);
+      hipLaunchKernelGGL((attn_combine_kernel<64, kWaves>), cgrid, dim3(256), 0, cx.stream, ca);
   } else {
     hipLaunchKernelGGL((attn_bf16_kernel<64, kWideWaves>), grid, dim3(W * 64), 0, cx.stream, a);
     if (plan.partial_items)
-      hipLaunchKernelGGL((attn_combine_kernel<64, kWideWaves>), cgrid, dim3(256), 0, cx.stream, a);
+      hipLaunchKernelGGL((attn_combine_kernel<64, kWideWaves>), cgrid, dim3(256), 0, cx.stream, ca);
   }
   return hipGetLastError();
 }

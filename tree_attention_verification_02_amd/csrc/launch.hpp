@@ -39,6 +39,13 @@ struct AttnPlan {
   int weighted;         // heavy units get 2/3-length splits (mixed-length batches)
   int64_t items_a;      // workgroups of the first phase
   uint16_t order[kLptMax];  // second phase: requests, longest last split first
+  // Combine grid: `comb_chunks` workgroups (32 rows each) per unit, enough
+  // for the largest unit.  With comb_nreq > 0 (every request one row block,
+  // batches of up to kLptMax), only the units of the requests listed in
+  // comb_req (those with more than one split) get workgroups.
+  int comb_chunks;
+  int comb_nreq;
+  uint16_t comb_req[kLptMax];
 };
 
 hipError_t launch_build_mask(const LaunchCtx& cx, const int32_t* parents, uint64_t* mask, int words,
