@@ -270,10 +270,9 @@ accept_argmax_kernel(const float* __restrict__ p_logits, int64_t ld, int vocab, 
 }
 
 // Sampling statistics: one workgroup per (listed row, chunk) item, the
-// listed target rows first (item it < np * nch is target row it / nch, no
-// lookup), then the listed draft rows.  The grid covers every draft row;
-// workgroups past the list end at once, after all the others were
-// dispatched, so they hold no slot while the streaming is under way.  Each
+// listed draft rows first (entry e < nq is the draft row at list position
+// np + e), then the target rows (entry nq + r is target row r, no lookup).
+// The grid covers every draft row; workgroups past the list end at once.  Each
 // item: (reference, sum of exp(z - reference)) with z = logit / T in fp64
 // and the chunk's maximum as the reference, so every exponent is <= 0 and
 // the per-logit work is branch-free.
@@ -282,6 +281,7 @@ struct StatsArgs {
   const float* q_logits;
   int64_t ld;
   int vocab, R, np;   // np: target rows listed (R, or 0 when the LM head made their partials)
+  int nq;             // draft-row entries in the grid (R, or 0 without draft rows)
   double invT;
 };
 
@@ -314,10 +314,15 @@ SPEC_DEVICE void sample_stats_item(const StatsArgs& a, const AcceptWs& ws, int i
   // row would land on one XCD; rotating the chunk by the entry spreads each
   // chunk position (the ragged last one in particular) over all of them.
   const int chunk = (it - e * nch + e) % nch;
-  int rr = e;
-  if (e >= a.np) {
-    if (e >= ws.sync[2]) return;                     // past the listed draft rows
-    rr = ws.order[e];
+  // Draft-row entries come first in the grid: the entries past the list
+  // (draft rows of leaves) then end at once early on, instead of sitting
+  // between the last statistics and the walk workgroups in dispatch order.
+  int rr;
+  if (e < a.nq) {
+    if (a.np + e >= ws.sync[2]) return;              // past the listed draft rows
+    rr = ws.order[a.np + e];
+  } else {
+    rr = e - a.nq;                                   // target row
   }
   load_exp_table(s_tab);
   const int which = rr >= a.R ? 1 : 0;
@@ -1378,7 +1383,7 @@ hipError_t launch_accept(const LaunchCtx& cx, int R, const int32_t* parents, con
   // With the LM head's partials, the target rows are merged, not streamed.
   hipError_t e;
   int nstat = 0;
-  StatsArgs stats_args{p_logits, q_logits, ld, vocab, R, 0, 1.0 / (double)temperature};
+  StatsArgs stats_args{p_logits, q_logits, ld, vocab, R, 0, 0, 1.0 / (double)temperature};
   if (!greedy) {
     // the rows to stream (and the walk's exchange area cleared)
     const int64_t nseg_all = (int64_t)cx.B * 2 * segs_for(vocab);
@@ -1396,7 +1401,8 @@ hipError_t launch_accept(const LaunchCtx& cx, int R, const int32_t* parents, con
                        p_logits, ld, vocab, ws);
   } else if (!greedy && (!head || q_logits)) {
     stats_args.np = head ? 0 : R;
-    nstat = (stats_args.np + (q_logits ? R : 0)) * nch;
+    stats_args.nq = q_logits ? R : 0;
+    nstat = (stats_args.np + stats_args.nq) * nch;
   }
   if ((e = hipGetLastError()) != hipSuccess) return e;
   WalkOut out{accept_len, path, tokens_out, accept_mask, flags, path_stride, child_p, child_q};
