@@ -1,8 +1,8 @@
 """GPU parity: the HIP library against the oracle on seeded workloads.
 
 Reduced sizes span several 64-key tiles, several key splits and ragged tails;
-full sizes are the five stated workloads, checked on sampled requests for
-attention and on every request for acceptance.  Tolerances: masks, commits,
+full sizes are the five stated workloads, checked on every request (every
+row and head for attention).  Tolerances: masks, commits,
 paths and tokens bit-exact (near-threshold sampling decisions are reported,
 not failed); attention max |d| <= 1e-2 for bf16 inputs (1e-4 for fp32);
 child probabilities within 1e-5 relative.
