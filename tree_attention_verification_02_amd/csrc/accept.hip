@@ -521,6 +521,8 @@ struct WalkShared {
   double lane_excl[64];             // prefix of the segment sums, per lane block
   double total;
   double c0;
+  double chunk_base, chunk_target;   // P-only draw: mass before the drawn chunk, the target
+  int chunk;                         // P-only draw: the chunk holding the target (-1: none)
   int found_seg;
   int pick;
   int bad;
@@ -599,6 +601,7 @@ struct WalkCtx {
   const float* q;     // draft row of the current node
   double invT, lse_p, lse_q;
   int vocab, nseg, seg_lo, seg_hi, slice, S, max_spins;
+  int rd_lo, rd_n;    // segments whose sums the pass exchanges (all, or one chunk's)
   double* seg;        // this request's [2][nseg]
   const int* rej;     // tokens whose weight is 0 (LDS), nrej of them
   int nrej;
@@ -704,20 +707,20 @@ SPEC_DEVICE double walk_pass(WalkShared& sh, const WalkCtx& c, int pass, double 
   else
     pass_segments<false>(sh, c, seg, t, tag);
   if (wave == 0) {
-    const int per = (c.nseg + 63) / 64;
+    const int per = (c.rd_n + 63) / 64;
     double part = 0.0;
     bool late = false;
     // the first kSumLoads sums of the lane in one round trip; a slot that
     // does not show the tag yet is polled
-    const double* mine = seg + lane * per;
+    const double* mine = seg + c.rd_lo + lane * per;
     unsigned long long first[kSumLoads];
 #pragma unroll
     for (int k = 0; k < kSumLoads; ++k)
-      first[k] = (k < per && lane * per + k < c.nseg) ? load_tagged(mine + k) : 0ull;
+      first[k] = (k < per && lane * per + k < c.rd_n) ? load_tagged(mine + k) : 0ull;
 #pragma unroll
     for (int k = 0; k < kSumLoads; ++k) {
-      const int sidx = lane * per + k;
-      if (k < per && sidx < c.nseg) {
+      const int sidx = c.rd_lo + lane * per + k;
+      if (k < per && lane * per + k < c.rd_n) {
         double v;
         if ((int)(first[k] & 0xffull) == tag)
           v = tagged_value(first[k]);
@@ -728,8 +731,8 @@ SPEC_DEVICE double walk_pass(WalkShared& sh, const WalkCtx& c, int pass, double 
       }
     }
     for (int k = kSumLoads; k < per; ++k) {
-      const int sidx = lane * per + k;
-      if (sidx < c.nseg) {
+      const int sidx = c.rd_lo + lane * per + k;
+      if (lane * per + k < c.rd_n) {
         double v;
         late |= !read_sum(&seg[sidx], tag, c.max_spins, v);
         sh.segsum[sidx] = v;
@@ -745,21 +748,22 @@ SPEC_DEVICE double walk_pass(WalkShared& sh, const WalkCtx& c, int pass, double 
   return sh.total;
 }
 
-// Inverse-CDF draw from the weights of the last pass with coin r: every
-// slice finds the segment from that pass's sums (kept in LDS by walk_pass);
-// slice 0 rescans it and returns the token (other slices return -1).
+// Inverse-CDF draw from the weights of the last pass: the first entry whose
+// cumulative weight (over the pass's segments, in order) exceeds `target`.
+// Every slice finds the segment from that pass's sums (kept in LDS by
+// walk_pass); slice 0 rescans it and returns the token (other slices
+// return -1).
 SPEC_DEVICE int walk_draw(WalkShared& sh, const WalkCtx& c, double t, bool need_q,
-                          double r) {
+                          double target) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const double target = r * sh.total;
   if (wave == 0) {
-    const int per = (c.nseg + 63) / 64;
+    const int per = (c.rd_n + 63) / 64;
     double cum = sh.lane_excl[lane];
     int hit = -1, pos = -1;
     double hit_c0 = 0.0, pos_c0 = 0.0;
     for (int k = 0; k < per; ++k) {
-      const int sidx = lane * per + k;
-      if (sidx < c.nseg) {
+      const int sidx = c.rd_lo + lane * per + k;
+      if (lane * per + k < c.rd_n) {
         const double v = sh.segsum[sidx];
         const double nxt = cum + v;
         if (hit < 0 && nxt > target) {
@@ -965,6 +969,59 @@ SPEC_DEVICE void write_abandoned(const WalkOut& w, int b, int o, int n, int flag
   }
 }
 
+// A draw from P_u alone (at a leaf, or from P_u without the rejected tokens
+// once every deterministic child is rejected) locates its chunk of the
+// vocabulary from the statistics partials of row u: chunk k holds mass
+// s_k exp(ref_k - lse_u), less the P_u of the excluded tokens in it.  The
+// target is r times their total; the drawn chunk is the first whose
+// cumulative mass exceeds it (rounding past the end: the last chunk with
+// mass).  Only that chunk's segments are then passed over, against the
+// target less the mass before the chunk.  Wave 0 of every slice computes the
+// same values; sh.chunk = -1 (no chunk with mass) falls back to a full pass.
+static_assert(kStatChunkLen % kSeg == 0, "a chunk is whole segments");
+constexpr int kSegsPerChunk = kStatChunkLen / kSeg;
+SPEC_DEVICE void locate_chunk(WalkShared& sh, const AcceptWs& ws, const WalkCtx& c, int row,
+                              double r) {
+  const int lane = threadIdx.x & 63;
+  const int nch = ws.nch;                              // <= 64 (vocabulary <= 2^20)
+  double m = 0.0;
+  if (lane < nch) {
+    const double ref = tagged_value(load_partial(ws.part_ref + (int64_t)row * nch + lane));
+    const double sum = tagged_value(load_partial(ws.part_s + (int64_t)row * nch + lane));
+    m = sum * exp_f64(ref - c.lse_p, sh.tab);
+  }
+  // excluded tokens, 64 at a time: lane k loads token k's logit (one round
+  // trip for all of them), then each is taken off its chunk in list order
+  for (int k0 = 0; k0 < c.nrej; k0 += 64) {
+    const int k = k0 + lane;
+    const int x = (k < c.nrej) ? c.rej[k] : -1;
+    const bool in = x >= 0 && x < c.vocab;
+    const double px = in ? exp_f64((double)c.p[x] * c.invT - c.lse_p, sh.tab) : 0.0;
+    const int xc = in ? x / kStatChunkLen : -1;
+    for (int j = 0; j < 64 && k0 + j < c.nrej; ++j) {
+      const int cj = __shfl(xc, j, 64);
+      const double pj = __shfl(px, j, 64);
+      if (lane == cj) m -= pj;
+    }
+  }
+  m = fmax(m, 0.0);
+  const double incl = wave_incl_scan(m, lane);
+  const double total = __shfl(incl, 63, 64);
+  const double target = r * total;
+  const uint64_t hit = __ballot(lane < nch && incl > target && m > 0.0);
+  const uint64_t pos = __ballot(m > 0.0);
+  int ck = -1;
+  if (total > 0.0) ck = hit ? __ffsll((long long)hit) - 1 : 63 - __clzll((long long)pos);
+  if (lane == 0) {
+    sh.chunk = -1;
+    sh.chunk_target = target;
+  }
+  if (ck >= 0 && lane == ck) {
+    sh.chunk = ck;
+    sh.chunk_base = incl - m;
+  }
+}
+
 // Per-request walk state, kept in LDS and advanced by thread 0.
 struct WalkState {
   int u;            // current node (local row)
@@ -1159,6 +1216,8 @@ accept_sample_kernel(StatsArgs sa, int nstat, const int32_t* __restrict__ row_of
   c.S = S;
   c.max_spins = max_spins;
   c.seg = ws.seg + (size_t)b * 2 * c.nseg;
+  c.rd_lo = 0;
+  c.rd_n = c.nseg;
   if (tid == 0) {
     sh.len = 1;
     sh.ntok = 0;
@@ -1188,6 +1247,23 @@ accept_sample_kernel(StatsArgs sa, int nstat, const int32_t* __restrict__ row_of
     c.nrej = topk ? sh.nrej : 0;
     const double act_t = st.act_t;
     const bool act_q = st.act_q != 0;
+    if (action == 1 && !act_q) {                     // a draw from P_u alone
+      if ((tid >> 6) == 0) locate_chunk(sh, ws, c, o + u, sh.coin[1][u]);
+      __syncthreads();
+      const int ck = sh.chunk;
+      if (ck >= 0) {
+        const int a0 = ck * kSegsPerChunk, a1 = min(c.nseg, a0 + kSegsPerChunk);
+        const int per = (a1 - a0 + S - 1) / S;
+        c.seg_lo = min(a1, a0 + slice * per);
+        c.seg_hi = min(a1, c.seg_lo + per);
+        c.rd_lo = a0;
+        c.rd_n = a1 - a0;
+        walk_pass(sh, c, ++pass, 0.0, false);
+        if (sh.timeout) break;
+        final_token = walk_draw(sh, c, 0.0, false, sh.chunk_target - sh.chunk_base);
+        break;
+      }
+    }
     if (action != 2) {
       const double G = walk_pass(sh, c, ++pass, act_t, act_q);
       if (sh.timeout) break;
@@ -1210,7 +1286,7 @@ accept_sample_kernel(StatsArgs sa, int nstat, const int32_t* __restrict__ row_of
     const double r = sh.coin[1][u];
     const double dt = (action == 2) ? st.pass_t : act_t;
     const bool dq = (action == 2) ? true : act_q;
-    final_token = walk_draw(sh, c, dt, dq, r);
+    final_token = walk_draw(sh, c, dt, dq, r * sh.total);
     break;
   }
   // Only slice 0 writes: it passed every barrier of the walk (then every sum
