@@ -12,7 +12,9 @@
 // starting from (t, N) = (0, 1), a rejection moves to t' = t + N and
 // N' = G(t') with G(t) = sum_y max(0, P_y - t Q_y) (and keeps (t, N) when
 // G(t') = 0).  So every rejection costs one vocabulary pass at a scalar t,
-// and the final draw after the last rejection reuses that pass's sums.
+// and the final draw after the last rejection reuses that pass's sums.  A
+// draw from P alone (at a leaf) needs no full pass: the statistics partials
+// give each chunk's mass, and only the drawn chunk is passed over.
 //
 // Kernels:
 //  * accept_prep (T > 0): lists the rows whose statistics are read -- every
