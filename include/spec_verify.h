@@ -183,7 +183,9 @@ spec_status spec_tree_attn_verify(const spec_batch *batch, const spec_kv *kv,
  *
  * Row u's target logits p_u give the distribution of u's children; row u's
  * draft logits q_u the distribution u's children were drafted from (only
- * rows that have children are read).  With T = temperature > 0,
+ * rows that have children are read).  At T > 0 the target row of a leaf is
+ * read only if the walk ends at that leaf (its bonus draw); no output needs
+ * it otherwise.  With T = temperature > 0,
  * P_u = softmax(p_u/T), Q_u = softmax(q_u/T).  For each request, starting at
  * the root: the children c of the current node u are tried in ascending row
  * order; child c (token x = tokens[c], coin r) is accepted iff

@@ -40,3 +40,24 @@ def test_algorithmic_work_of_the_toy_step():
     # deterministic children read no draft rows
     assert _bench().algorithmic(w, topk=True)[2] == n * 1000 * 4
     assert np.array_equal(w.parents, [-1, 0, 0, 1, 1, 2])
+
+
+def test_accept_bytes_count_the_rows_the_walk_can_need():
+    """Toy tree: rows 0, 1 and 2 have children.  A walk ending at a leaf
+    (path 0 -> 1 -> 3) adds that leaf's target row; one stopping at a node
+    with children (path 0 -> 2 after rejecting 2's child) adds nothing."""
+    import torch
+    w = W.make("toy")
+    bench = _bench()
+    V = 1000
+    path = torch.full((1, 9), -1, dtype=torch.int32)
+    path[0, :3] = torch.tensor([0, 1, 3])
+    assert bench.accept_bytes(w, False, path, torch.tensor([2])) == (3 + 3 + 1) * V * 4
+    assert bench.accept_bytes(w, True, path, torch.tensor([2])) == (3 + 1) * V * 4
+    path[0, :3] = torch.tensor([0, 2, -1])
+    assert bench.accept_bytes(w, False, path, torch.tensor([1])) == (3 + 3) * V * 4
+    # an abandoned request (accept_len -1) adds no leaf row
+    assert bench.accept_bytes(w, False, path, torch.tensor([-1])) == (3 + 3) * V * 4
+    f = bench.attn_plus_accept(10.0, 4.0, 6.0, 1e-3, 1e-3, 6)
+    assert f["bytes"] == 14.0 and f["bytes_every_target_row"] == 16.0
+    assert abs(f["hbm_frac"] * bench.HBM_PEAK_GBS * 1e9 * 2e-3 - 14.0) < 1e-9

@@ -17,9 +17,10 @@
 // give each chunk's mass, and only the drawn chunk is passed over.
 //
 // Kernels:
-//  * accept_prep (T > 0): lists the rows whose statistics are read -- every
-//    target row, and the draft rows of nodes with children (draft rows of
-//    leaves are never read) -- and clears the walk's exchange area and the
+//  * accept_prep (T > 0): lists the rows whose statistics are read -- the
+//    target and draft rows of nodes with children (no output needs a leaf's
+//    statistics; a walk that ends at a leaf makes its own pass over the
+//    leaf's target row) -- and clears the walk's exchange area and the
 //    statistics partials.
 //  * accept_sample (T > 0), one launch in two parts.  First one workgroup per
 //    listed (row, 16K-logit chunk) item streams its chunk once (16-byte
@@ -85,11 +86,14 @@ struct AcceptWs {
   double* part_s;   //                     and sum of exp(z - reference)
   float* part_m;    // [R][nch]    chunk max (greedy)
   int32_t* part_am; //                     and its first index
-  int32_t* order;   // [2R] rows whose statistics are streamed: rr = r (target), R + r (draft)
-  int32_t* sync;    // [64], own 256 B: [0] the walk's ticket counter, [2] entries in
-                    // `order`
+  int32_t* order;   // [2R] rows whose statistics are streamed: [0, R) draft rows (R + r),
+                    // [R, 2R) target rows (r), each list in row order
+  int32_t* sync;    // [64], own 256 B: [0] the walk's ticket counter, [2] draft rows
+                    // listed, [3] target rows listed
   double* seg;      // [B][2][nseg] per-pass segment sums carrying their pass tag
                     // (double-buffered by pass parity; zeroed before every walk)
+  double* sref;     // [B][2][kMaxSlices] per-slice references of a leaf's pass (tagged
+                    // like the sums, same parity buffers; zeroed before every walk)
 };
 
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -118,6 +122,8 @@ __host__ __device__ inline AcceptWs accept_ws(void* base, int R, int B, int voca
   w.sync = (int32_t*)p;
   p += 256;
   w.seg = (double*)p;
+  p += align256((size_t)B * 2 * ((vocab + kSeg - 1) / kSeg) * sizeof(double));
+  w.sref = (double*)p;
   return w;
 }
 
@@ -133,17 +139,18 @@ size_t accept_workspace_bytes(int R, int B, int vocab) {
          align256((size_t)R * nch * sizeof(int32_t)) +
          align256(2 * (size_t)R * sizeof(int32_t)) +
          256 +
-         align256((size_t)B * 2 * nseg * sizeof(double));
+         align256((size_t)B * 2 * nseg * sizeof(double)) +
+         align256((size_t)B * 2 * kMaxSlices * sizeof(double));
 }
 
 // Before the statistics at T > 0 (accept_prep_kernel): blocks 1.. clear the
 // walk's exchange area (every segment sum to tag 0, which no pass uses) and
 // the statistics partials (tag 0: not yet written); block 0 resets the
-// walk's ticket and item counters and lists the rows whose statistics are streamed
-// -- every target row (unless the LM head has produced their partials),
-// then the draft rows of the nodes that have children (draft rows of leaves
-// are never read).  The children marks live in LDS; beyond its tables every
-// draft row is listed.
+// walk's ticket counter and lists the rows whose statistics are streamed:
+// the draft rows (order[0, R)) and the target rows (order[R, 2R)) of the
+// nodes that have children (no target rows when the LM head has produced
+// their partials).  The children marks live in LDS; beyond its tables every
+// row is listed.
 constexpr int kPrepThreads = 1024;
 constexpr int kPrepMaxRows = 16384;
 constexpr int kPrepMaxBatch = 4096;
@@ -167,23 +174,30 @@ accept_prep_kernel(const int32_t* __restrict__ row_offsets, int B, int R,
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   if (blockIdx.x > 0) {
     const int64_t nseg_all = (int64_t)B * 2 * ((vocab + kSeg - 1) / kSeg);
+    const int64_t nsref = (int64_t)B * 2 * kMaxSlices;
     const int64_t nslot = 2 * (int64_t)R * ws.nch;
     const int64_t stride = (int64_t)(gridDim.x - 1) * kPrepThreads;
     for (int64_t i = (int64_t)(blockIdx.x - 1) * kPrepThreads + tid; i < nseg_all; i += stride)
       ws.seg[i] = 0.0;
+    for (int64_t i = (int64_t)(blockIdx.x - 1) * kPrepThreads + tid; i < nsref; i += stride)
+      ws.sref[i] = 0.0;
     for (int64_t i = (int64_t)(blockIdx.x - 1) * kPrepThreads + tid; i < nslot; i += stride) {
       ws.part_ref[i] = 0.0;
       ws.part_s[i] = 0.0;
     }
     return;
   }
-  const int np = list_p ? R : 0;
-  for (int r = tid; r < np; r += kPrepThreads) ws.order[r] = r;
-  if (!list_q) {
-    if (tid == 0) ws.sync[2] = np;
+  if (!list_p && !list_q) {
+    if (tid == 0) ws.sync[2] = ws.sync[3] = 0;
   } else if (R > kPrepMaxRows || B > kPrepMaxBatch) {
-    for (int r = tid; r < R; r += kPrepThreads) ws.order[np + r] = R + r;
-    if (tid == 0) ws.sync[2] = np + R;
+    for (int r = tid; r < R; r += kPrepThreads) {
+      ws.order[r] = R + r;
+      ws.order[R + r] = r;
+    }
+    if (tid == 0) {
+      ws.sync[2] = list_q ? R : 0;
+      ws.sync[3] = list_p ? R : 0;
+    }
   } else {
     for (int i = tid; i <= B; i += kPrepThreads) s_off[i] = row_offsets[i];
     for (int r = tid; r < R; r += kPrepThreads) s_kids[r] = 0;
@@ -213,10 +227,17 @@ accept_prep_kernel(const int32_t* __restrict__ row_offsets, int B, int R,
       if (w < wave) base += s_wave[w];
       total += s_wave[w];
     }
-    int pos = np + base + incl - cnt;
+    int pos = base + incl - cnt;
     for (int r = r0; r < r1; ++r)
-      if (s_kids[r]) ws.order[pos++] = R + r;
-    if (tid == 0) ws.sync[2] = np + total;
+      if (s_kids[r]) {
+        ws.order[pos] = R + r;
+        ws.order[R + pos] = r;
+        ++pos;
+      }
+    if (tid == 0) {
+      ws.sync[2] = list_q ? total : 0;
+      ws.sync[3] = list_p ? total : 0;
+    }
   }
   if (tid == 0) ws.sync[0] = 0;
 }
@@ -284,6 +305,7 @@ struct StatsArgs {
   int64_t ld;
   int vocab, R, np;   // np: target rows listed (R, or 0 when the LM head made their partials)
   int nq;             // draft-row entries in the grid (R, or 0 without draft rows)
+  int leafp;          // 1: target partials of leaf rows exist too (the LM head's)
   double invT;
 };
 
@@ -319,12 +341,18 @@ SPEC_DEVICE void sample_stats_item(const StatsArgs& a, const AcceptWs& ws, int i
   // Draft-row entries come first in the grid: the entries past the list
   // (draft rows of leaves) then end at once early on, instead of sitting
   // between the last statistics and the walk workgroups in dispatch order.
+  // Target-row entries are taken from the end of their range, so the
+  // entries past that list end at once before the live ones, not between
+  // the last statistics and the walk workgroups.
   int rr;
   if (e < a.nq) {
-    if (a.np + e >= ws.sync[2]) return;              // past the listed draft rows
-    rr = ws.order[a.np + e];
+    if (e >= ws.sync[2]) return;                     // past the listed draft rows
+    rr = ws.order[e];
   } else {
-    rr = e - a.nq;                                   // target row
+    const int skip = a.np - ws.sync[3];
+    const int ep = e - a.nq;
+    if (ep < skip) return;                           // past the listed target rows
+    rr = ws.order[a.R + ep - skip];
   }
   load_exp_table(s_tab);
   const int which = rr >= a.R ? 1 : 0;
@@ -524,6 +552,7 @@ struct WalkShared {
   double total;
   double c0;
   double chunk_base, chunk_target;   // P-only draw: mass before the drawn chunk, the target
+  double frame;                      // leaf pass: the reference its sums were rescaled to
   int chunk;                         // P-only draw: the chunk holding the target (-1: none)
   int found_seg;
   int pick;
@@ -971,6 +1000,114 @@ SPEC_DEVICE void write_abandoned(const WalkOut& w, int b, int o, int n, int flag
   }
 }
 
+SPEC_DEVICE double wave_max_f64(double v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmax(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// The draw at a leaf whose target row was never streamed (its statistics
+// are needed for nothing else): one pass in two steps.  Each slice takes
+// the largest logit / T of its segments as its reference (rounded up to 44
+// bits, published with the pass tag; -1e300 for a slice with nothing in
+// range), then publishes its segment sums of exp(z/T - reference).  Every
+// slice reads all sums and the references of the slices that made them,
+// rescales the sums to the largest reference R and leaves them in LDS for
+// walk_draw, whose weights are then exp(z/T - R).  Returns R.
+SPEC_DEVICE double leaf_pass(WalkShared& sh, WalkCtx& c, int pass, double* sref_req) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tag = pass_tag(pass);
+  double* seg = c.seg + (pass & 1) * c.nseg;
+  double* sr = sref_req + (pass & 1) * kMaxSlices;
+  const float4* p4 = reinterpret_cast<const float4*>(c.p);
+  const int v4 = (c.vocab + 3) >> 2;
+  float mx = -INFINITY;
+  for (int s0 = c.seg_lo; s0 < c.seg_hi; s0 += kPassF) {
+    float4 v[kPassF];
+#pragma unroll
+    for (int i = 0; i < kPassF; ++i)
+      v[i] = p4[min((min(s0 + i, c.seg_hi - 1)) * (kSeg / 4) + tid, v4 - 1)];
+#pragma unroll
+    for (int i = 0; i < kPassF; ++i) {
+      const int y0 = (min(s0 + i, c.seg_hi - 1)) * kSeg + 4 * tid;
+      const float a = (y0 + 0 < c.vocab) ? v[i].x : -INFINITY;
+      const float b = (y0 + 1 < c.vocab) ? v[i].y : -INFINITY;
+      const float d = (y0 + 2 < c.vocab) ? v[i].z : -INFINITY;
+      const float e = (y0 + 3 < c.vocab) ? v[i].w : -INFINITY;
+      mx = fmaxf(mx, fmaxf(fmaxf(a, b), fmaxf(d, e)));
+    }
+  }
+  mx = wave_max(mx);
+  if (lane == 0) sh.red_m[wave] = mx;
+  __syncthreads();
+  float m = sh.red_m[0];
+  for (int w = 1; w < kWalkWaves; ++w) m = fmaxf(m, sh.red_m[w]);
+  const double ref = (m == -INFINITY) ? -1e300 : ref_round_up((double)m * c.invT);
+  c.lse_p = ref;
+  pass_segments<false>(sh, c, seg, 0.0, tag);
+  if (tid == 0 && c.seg_lo < c.seg_hi) publish_sum(sr + c.slice, ref, tag);
+  if (wave == 0) {
+    // the slices' references (lane k < S: slice k's) and this lane's sums,
+    // all loads issued together; a slot without the tag yet is polled
+    const int per_slice = (c.nseg + c.S - 1) / c.S;
+    const bool owns = lane < c.S && lane * per_slice < c.nseg;
+    const int per = (c.nseg + 63) / 64;
+    const double* mine = seg + lane * per;
+    const unsigned long long rbits = owns ? load_tagged(sr + lane) : 0ull;
+    unsigned long long first[kSumLoads];
+#pragma unroll
+    for (int k = 0; k < kSumLoads; ++k)
+      first[k] = (k < per && lane * per + k < c.nseg) ? load_tagged(mine + k) : 0ull;
+    bool late = false;
+    double rf = -INFINITY;
+    if (owns) {
+      if ((int)(rbits & 0xffull) == tag)
+        rf = tagged_value(rbits);
+      else
+        late |= !read_sum(sr + lane, tag, c.max_spins, rf);
+    }
+#pragma unroll
+    for (int k = 0; k < kSumLoads; ++k) {
+      const int sidx = lane * per + k;
+      if (k < per && sidx < c.nseg) {
+        double v;
+        if ((int)(first[k] & 0xffull) == tag)
+          v = tagged_value(first[k]);
+        else
+          late |= !read_sum(mine + k, tag, c.max_spins, v);
+        sh.segsum[sidx] = v;
+      }
+    }
+    for (int k = kSumLoads; k < per; ++k) {
+      const int sidx = lane * per + k;
+      if (sidx < c.nseg) {
+        double v;
+        late |= !read_sum(&seg[sidx], tag, c.max_spins, v);
+        sh.segsum[sidx] = v;
+      }
+    }
+    // every sum to the largest reference, in segment order per lane
+    const double top = wave_max_f64(rf);
+    double part = 0.0;
+    for (int k = 0; k < per; ++k) {
+      const int sidx = lane * per + k;
+      const double ro = __shfl(rf, min(sidx, c.nseg - 1) / per_slice, 64);
+      if (sidx < c.nseg) {
+        const double w = sh.segsum[sidx] * exp_f64(ro - top, sh.tab);
+        sh.segsum[sidx] = w;
+        part += w;
+      }
+    }
+    if (__any(late) && lane == 0) sh.timeout = 1;
+    const double incl = wave_incl_scan(part, lane);
+    sh.lane_excl[lane] = incl - part;
+    if (lane == 63) sh.total = incl;
+    if (lane == 0) sh.frame = top;
+  }
+  __syncthreads();
+  return sh.frame;
+}
+
 // A draw from P_u alone (at a leaf, or from P_u without the rejected tokens
 // once every deterministic child is rejected) locates its chunk of the
 // vocabulary from the statistics partials of row u: chunk k holds mass
@@ -1176,8 +1313,9 @@ accept_sample_kernel(StatsArgs sa, int nstat, const int32_t* __restrict__ row_of
         cval[j] = true;
         clog[j] = ((which ? q_logits : p_logits) + (int64_t)(o + pu) * ld)[x];
       }
-      // (draft rows only of nodes with children: the others are not streamed)
-      if (!sh.bad && (!which || sh.kid_start[i + 1] > sh.kid_start[i]) &&
+      // (rows of nodes with children only, and with the LM head every target
+      // row: the others are not streamed)
+      if (!sh.bad && ((!which && sa.leafp) || sh.kid_start[i + 1] > sh.kid_start[i]) &&
           !merged_ref_sum(ws, which * R + o + i, sh.tab, sh.lse[which][i]))
         sh.timeout = 1;
     }
@@ -1249,6 +1387,13 @@ accept_sample_kernel(StatsArgs sa, int nstat, const int32_t* __restrict__ row_of
     c.nrej = topk ? sh.nrej : 0;
     const double act_t = st.act_t;
     const bool act_q = st.act_q != 0;
+    if (action == 1 && !act_q && !sa.leafp && sh.kid_start[u + 1] == sh.kid_start[u]) {
+      // a leaf, whose target row was not streamed: a self-normalised pass
+      c.lse_p = leaf_pass(sh, c, ++pass, ws.sref + (size_t)b * 2 * kMaxSlices);
+      if (sh.timeout) break;
+      final_token = walk_draw(sh, c, 0.0, false, sh.coin[1][u] * sh.total);
+      break;
+    }
     if (action == 1 && !act_q) {                     // a draw from P_u alone
       if ((tid >> 6) == 0) locate_chunk(sh, ws, c, o + u, sh.coin[1][u]);
       __syncthreads();
@@ -1461,7 +1606,8 @@ hipError_t launch_accept(const LaunchCtx& cx, int R, const int32_t* parents, con
   // With the LM head's partials, the target rows are merged, not streamed.
   hipError_t e;
   int nstat = 0;
-  StatsArgs stats_args{p_logits, q_logits, ld, vocab, R, 0, 0, 1.0 / (double)temperature};
+  StatsArgs stats_args{p_logits, q_logits, ld, vocab, R, 0, 0, head ? 1 : 0,
+                       1.0 / (double)temperature};
   if (!greedy) {
     // the rows to stream (and the walk's exchange area cleared)
     const int64_t nseg_all = (int64_t)cx.B * 2 * segs_for(vocab);
