@@ -733,10 +733,16 @@ SPEC_DEVICE double walk_pass(WalkShared& sh, const WalkCtx& c, int pass, double 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   double* seg = c.seg + (pass & 1) * c.nseg;
   const int tag = pass_tag(pass);
-  if (need_q)
+  if (need_q) {
+    // Residual passes are the walks' critical path; raised priority lets
+    // their exponentials go first on SIMDs shared with leaf passes and the
+    // last statistics items.
+    __builtin_amdgcn_s_setprio(2);
     pass_segments<true>(sh, c, seg, t, tag);
-  else
+    __builtin_amdgcn_s_setprio(0);
+  } else {
     pass_segments<false>(sh, c, seg, t, tag);
+  }
   if (wave == 0) {
     const int per = (c.rd_n + 63) / 64;
     double part = 0.0;
