@@ -359,10 +359,15 @@ spec_status spec_accept_topk(const spec_batch *batch, const int32_t *parents_d,
  *   head->weight_d   bf16 [vocab][hidden_size]: one row per vocabulary entry
  *   head->hidden_size  a multiple of 64 in 64 .. 65536, with
  *                    vocab * hidden_size and R * hidden_size below 2^31
- *   head->logits_d   fp32 [R][logits_ld] output, written in full; required
- *                    at temperature > 0 (the residual and bonus draws read
- *                    back the rows they need), optional at temperature 0
- *                    (NULL: the logits are never written)
+ *   head->logits_d   fp32 [R][logits_ld] output.  Required at temperature > 0,
+ *                    where the first `vocab` entries of the rows of nodes
+ *                    that have children are written (the residual passes and
+ *                    draws at those nodes read them back) and every other
+ *                    row is left untouched: a walk that ends at a leaf finds
+ *                    the 256-entry vocabulary tile of its bonus draw from the
+ *                    head's partial statistics and recomputes that tile's
+ *                    logits alone.  Optional at temperature 0: written in
+ *                    full when given, never written when NULL
  *   q_logits_d       as spec_accept_sample (same logits_ld)
  *   workspace >= spec_lm_head_accept_workspace_bytes(batch, vocab) bytes
  *                    (no init needed; 16-byte aligned)

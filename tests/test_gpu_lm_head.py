@@ -5,7 +5,10 @@ operands; the library accumulates in fp32, so:
 
 * logits: every entry within the worst-case fp32 accumulation bound
   gamma_H * sum_k |h_k w_k| of its oracle value, and an rms error below 1e-5
-  of the logits' own (``parity.check_head_logits``);
+  of the logits' own (``parity.check_head_logits``).  At temperature > 0
+  only the rows of nodes with children are stored (a leaf's draw recomputes
+  the one tile it needs), and the other rows of the buffer are left as they
+  were;
 * child probabilities: |d log P| <= 2 max_v |d z_v| / T (the logit and the
   row's log-sum-exp each move by at most the row's largest logit error),
   with that largest error measured against the oracle on the same rows;
@@ -62,6 +65,11 @@ def _head_case(name, H, requests=None, temperature=1.0, seed=0, topk=False, stor
     return w, vs, hidden, weight, requests, rows, z, bound
 
 
+def _stored(w, rows):
+    """Positions (into rows) of the rows whose logits the head stores at T > 0."""
+    return [i for i, r in enumerate(rows) if w.nonleaf[r]]
+
+
 def _z_by_request(w, requests, rows, z):
     pos = {r: i for i, r in enumerate(rows)}
     out = {}
@@ -72,16 +80,19 @@ def _z_by_request(w, requests, rows, z):
 
 
 def _check_sampled(w, vs, requests, rows, z, bound, temperature, seed, topk):
-    got = vs.head_logits[torch.as_tensor(rows, device="cuda"), :w.V].double().cpu().numpy()
-    err = check_head_logits(got, z, bound, f"{w.name} rows {len(rows)}")
+    keep = _stored(w, rows)
+    srows = [rows[i] for i in keep]
+    got = vs.head_logits[torch.as_tensor(srows, device="cuda"), :w.V].double().cpu().numpy()
+    err = check_head_logits(got, z[keep], bound[keep], f"{w.name} stored rows {len(srows)}")
     zb = _z_by_request(w, requests, rows, z)
     ref = oracle_head_accept(w, zb, temperature, seed, 0, requests, topk=topk)
-    pos = {r: i for i, r in enumerate(rows)}
+    spos = {r: i for i, r in enumerate(srows)}
     T = float(np.float32(temperature))
     tol = {}
     for b in requests:
+        # child probabilities read their parents' rows: the stored ones
         o, e = request_slice(w, b)
-        tol[b] = 2.0 * max(err[pos[r]] for r in range(o, e)) / T + 1e-6
+        tol[b] = 2.0 * max((err[spos[r]] for r in range(o, e) if r in spos), default=0.0) / T + 1e-6
     check_accept(w, vs, temperature, seed, 0, requests=requests, topk=topk, ref=ref,
                  flag_eps=FLAG_EPS, prob_rtol=tol, max_flagged=2)
 
@@ -116,10 +127,27 @@ def _check_greedy(w, vs, requests, rows, z, bound):
     assert near <= 1
 
 
-def _check_consistent(lib, w, vs, temperature, seed, topk):
-    """The plain acceptance on the stored head logits gives the same walk."""
+def _leaf_rows_filled(w, vs, hidden, weight):
+    """The head's logits buffer with the rows it does not store at T > 0 (the
+    leaves) filled from an fp32 product of the same bf16 operands."""
+    z = vs.head_logits.clone()
+    leaves = torch.from_numpy(np.nonzero(~np.asarray(w.nonleaf))[0]).to("cuda")
+    if len(leaves):
+        h = hidden[leaves].float().t().contiguous()              # [H][leaves]
+        z[leaves, :w.V] = (weight.float() @ h).t().contiguous()
+    return z
+
+
+def _check_consistent(lib, w, vs, temperature, seed, topk, hidden=None, weight=None):
+    """The plain acceptance on the head's logits gives the same walk (at T > 0
+    with the leaf rows, which the head does not store, computed in fp32: a
+    walk ending at a leaf then draws from logits summed in another order, so
+    only a draw within that rounding of a boundary could differ)."""
     dev = "cuda"
     batch = vs.batch
+    logits = vs.head_logits
+    if temperature > 0:
+        logits = _leaf_rows_filled(w, vs, hidden, weight)
     S = vs.acc.path.shape[1]
     out = lib.AcceptOut(torch.empty(w.B, dtype=torch.int32, device=dev),
                         torch.empty((w.B, S), dtype=torch.int32, device=dev),
@@ -129,11 +157,11 @@ def _check_consistent(lib, w, vs, temperature, seed, topk):
                         flags=torch.empty(w.B, dtype=torch.int32, device=dev))
     ws = torch.empty(lib.spec_accept_workspace_bytes(batch, w.V), dtype=torch.uint8, device=dev)
     if topk:
-        lib.spec_accept_topk(batch, vs.parents, vs.tokens, vs.head_logits, w.V, temperature, seed,
+        lib.spec_accept_topk(batch, vs.parents, vs.tokens, logits, w.V, temperature, seed,
                              0, out, ws, logits_ld=vs.head_ld)
     else:
         q = w.q_logits if temperature > 0 else None
-        lib.spec_accept_sample(batch, vs.parents, vs.tokens, vs.head_logits, q, w.V, temperature,
+        lib.spec_accept_sample(batch, vs.parents, vs.tokens, logits, q, w.V, temperature,
                                seed, 0, out, ws, logits_ld=vs.head_ld)
     torch.cuda.synchronize()
     for name in ("accept_len", "path", "tokens", "accept_mask", "flags"):
@@ -145,7 +173,7 @@ def _check_consistent(lib, w, vs, temperature, seed, topk):
     assert np.array_equal(fin, np.isfinite(cp1))
     rel = np.abs(cp0[fin] - cp1[fin]) / np.maximum(np.abs(cp0[fin]), 1e-30)
     assert rel.max(initial=0) <= 4e-6, rel.max(initial=0)
-    log(f"[parity] head vs plain acceptance on the stored logits: child_p rel "
+    log(f"[parity] head vs plain acceptance on the head's logits: child_p rel "
         f"{rel.max(initial=0):.3g}")
 
 
@@ -172,13 +200,14 @@ def test_head_parity_small(lib, case, mode):
         _check_greedy(w, vs, req, rows, z, bound)
     else:
         _check_sampled(w, vs, req, rows, z, bound, T, 3, mode == "topk")
-    _check_consistent(lib, w, vs, T, 3, mode == "topk")
+    _check_consistent(lib, w, vs, T, 3, mode == "topk", hidden, weight)
 
 
 @pytest.mark.parametrize("mode", ["sample", "greedy"])
 def test_head_ragged_vocab_padded_rows(lib, mode):
     """vocab 4001 in rows of 4004 floats: the head writes only the first 4001
-    of each stored row (the padding keeps its NaN), and the last vocabulary
+    of each stored row (the padding keeps its NaN; at T > 0 the rows of
+    leaves are not stored and keep theirs too), and the last vocabulary
     tile's entries past 4001 never reach the statistics."""
     from oracle import accept as OA
     V, LD = 4001, 4004
@@ -206,7 +235,11 @@ def test_head_ragged_vocab_padded_rows(lib, mode):
     torch.cuda.synchronize()
     assert torch.isnan(logits[:, V:]).all(), "padding was written"
     z, bound = oracle_head_logits(hidden, weight, list(range(R)))
-    check_head_logits(logits[:, :V].double().cpu().numpy(), z, bound, "ragged vocab")
+    keep = list(range(R)) if T == 0 else _stored(w, list(range(R)))
+    if T > 0:
+        leaves = torch.from_numpy(np.nonzero(~np.asarray(w.nonleaf))[0]).to(dev)
+        assert torch.isnan(logits[leaves]).all(), "a leaf row was stored"
+    check_head_logits(logits[keep, :V].double().cpu().numpy(), z[keep], bound[keep], "ragged vocab")
     alen = out.accept_len.cpu().numpy()
     toks = out.tokens.cpu().numpy()
     path = out.path.cpu().numpy()
@@ -246,7 +279,7 @@ def test_head_full_size_sampled(lib):
     rows = _rows_of(w, req)
     z, bound = oracle_head_logits(hidden, weight, rows)
     _check_sampled(w, vs, req, rows, z, bound, 1.0, 0, False)
-    _check_consistent(lib, w, vs, 1.0, 0, False)
+    _check_consistent(lib, w, vs, 1.0, 0, False, hidden, weight)
     del vs, hidden, weight
     torch.cuda.empty_cache()
 
@@ -254,14 +287,16 @@ def test_head_full_size_sampled(lib):
 @pytest.mark.parametrize("T", [1.0, 0.0])
 def test_head_single_row_single_tile(lib, T):
     """One request with only its root (R = 1): one row tile holding a single
-    row, a vocabulary of 200 (one partial tile) and H = 64 (one K slice)."""
+    row, a vocabulary of 200 (one partial tile) and H = 64 (one K slice); at
+    T > 0 the bonus draw recomputes that tile."""
     w = make("dynamic", B=1, L=[5], V=200, Hq=2, Hkv=1, tree=("given", [np.array([-1])]),
              given_tokens=np.array([7]))
     hidden, weight = W.heads.head_inputs(w, H=64)
     vs = run_step(w, temperature=T, seed=1, step=0, commit=False, head=(hidden, weight),
                   store_head_logits=True)
     z, bound = oracle_head_logits(hidden, weight, [0])
-    check_head_logits(vs.head_logits[:1, :200].double().cpu().numpy(), z, bound, "single row")
+    if T == 0:     # (at T > 0 the root is a leaf: its logits are not stored)
+        check_head_logits(vs.head_logits[:1, :200].double().cpu().numpy(), z, bound, "single row")
     from oracle import accept as OA
     r = OA.accept_request(w.parents, w.tokens, z, None, T, 1, 0, 0)
     assert int(vs.acc.accept_len[0]) == 0 == r["accept_len"]
@@ -283,7 +318,7 @@ def test_head_full_size_specinfer_wide(lib):
     rows = _rows_of(w, req)
     z, bound = oracle_head_logits(hidden, weight, rows)
     _check_sampled(w, vs, req, rows, z, bound, 1.0, 2, False)
-    _check_consistent(lib, w, vs, 1.0, 2, False)
+    _check_consistent(lib, w, vs, 1.0, 2, False, hidden, weight)
     del vs, hidden, weight
     torch.cuda.empty_cache()
 
@@ -297,4 +332,4 @@ def test_head_extreme_temperatures(lib, T):
     name, H = kw.pop("name"), kw.pop("H")
     w, vs, hidden, weight, req, rows, z, bound = _head_case(name, H, temperature=T, seed=5, **kw)
     _check_sampled(w, vs, req, rows, z, bound, T, 5, False)
-    _check_consistent(lib, w, vs, T, 5, False)
+    _check_consistent(lib, w, vs, T, 5, False, hidden, weight)

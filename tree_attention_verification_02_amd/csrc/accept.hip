@@ -554,6 +554,8 @@ struct WalkShared {
   double chunk_base, chunk_target;   // P-only draw: mass before the drawn chunk, the target
   double frame;                      // leaf pass: the reference its sums were rescaled to
   int chunk;                         // P-only draw: the chunk holding the target (-1: none)
+  int tile;                          // LM-head leaf draw: the 256-entry tile holding the target
+  double tile_target;                //   and the target less the mass before that tile
   int found_seg;
   int pick;
   int bad;
@@ -1167,6 +1169,95 @@ SPEC_DEVICE void locate_chunk(WalkShared& sh, const AcceptWs& ws, const WalkCtx&
   }
 }
 
+// The bonus draw at a leaf on the LM-head path, whose logits were not
+// stored (only rows with children are).  locate_chunk finds the 16K chunk
+// from the merged partials; the head's partials of that chunk's 64 tiles of
+// 256 entries, s_k exp(ref_k - lse), find the tile; the tile's logits are
+// recomputed from the hidden row and the weight rows (bf16 products summed
+// in fp32, as the head does; each slice a share, exchanged with the pass
+// tag); slice 0 then draws inside the tile with the walk's weights.  A
+// target within rounding of the end of the chunk or tile falls back to the
+// last tile or entry with positive weight, as the other draws do.  Returns
+// the token (slice 0), -1 in the other slices or on a timeout.
+SPEC_DEVICE int head_leaf_draw(WalkShared& sh, const WalkCtx& c, const AcceptWs& ws,
+                               const HeadTiles& ht, int row, int b, int tag, double r) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (wave == 0) locate_chunk(sh, ws, c, row, r);
+  __syncthreads();
+  if (wave == 0) {
+    const int ck = sh.chunk < 0 ? 0 : sh.chunk;       // (no mass at all: not reached)
+    const int t = ck * kTilesPerChunk + lane;
+    double m = 0.0;
+    if (t < ht.ntile) {
+      const int64_t i = (int64_t)row * ht.ntile + t;
+      m = ht.s[i] * exp_f64(ht.ref[i] - c.lse_p, sh.tab);
+    }
+    const double incl = wave_incl_scan(m, lane);
+    const double target = sh.chunk_target - sh.chunk_base;
+    const uint64_t hit = __ballot(t < ht.ntile && incl > target && m > 0.0);
+    const uint64_t pos = __ballot(m > 0.0);
+    const int tk = hit ? __ffsll((long long)hit) - 1 : pos ? 63 - __clzll((long long)pos) : 0;
+    if (lane == tk) {
+      sh.tile = ck * kTilesPerChunk + tk;
+      sh.tile_target = target - (incl - m);
+    }
+  }
+  __syncthreads();
+  const int v0 = sh.tile * kHeadTileV;
+  const int nv = min(kHeadTileV, c.vocab - v0);
+  // this slice's share of the tile: G threads per logit, G a power of two
+  const int per = (nv + c.S - 1) / c.S;
+  const int j0 = c.slice * per, j1 = min(nv, j0 + per);
+  int G = 1;
+  while (G < 64 && 2 * G * per <= kWalkThreads) G *= 2;
+  const int jl = tid / G, part = tid % G;
+  const int j = j0 + jl;
+  const bool mine = jl < per && j < j1;
+  float z = 0.0f;
+  if (mine) {
+    const uint4* wr = reinterpret_cast<const uint4*>(ht.weight + (int64_t)(v0 + j) * ht.H);
+    const uint4* hr = reinterpret_cast<const uint4*>(ht.hidden + (int64_t)row * ht.H);
+    for (int k = part; k < ht.H / 8; k += G) {
+      const uint4 wv = wr[k], hv = hr[k];
+      const uint32_t wa[4] = {wv.x, wv.y, wv.z, wv.w}, ha[4] = {hv.x, hv.y, hv.z, hv.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        z = fmaf(__uint_as_float(wa[e] << 16), __uint_as_float(ha[e] << 16), z);
+        z = fmaf(__uint_as_float(wa[e] & 0xffff0000u), __uint_as_float(ha[e] & 0xffff0000u), z);
+      }
+    }
+  }
+  for (int o = G / 2; o > 0; o >>= 1) z += __shfl_xor(z, o, 64);
+  double* slot = ht.leafz + (int64_t)b * kHeadTileV;
+  if (mine && part == 0) publish_sum(slot + j, (double)z, tag);   // a float: exact in 44 bits
+  if (c.slice != 0) return -1;
+  double zd = 0.0;
+  if (tid < nv && !read_sum(slot + tid, tag, c.max_spins, zd)) sh.timeout = 1;
+  __syncthreads();
+  if (sh.timeout) return -1;
+  const double w = tid < nv ? walk_weight((float)zd, 0.0f, c.invT, c.lse_p, 0.0, 0.0, false, sh.tab)
+                            : 0.0;
+  const double incl = wave_incl_scan(w, lane);
+  if (lane == 63) sh.wave_tot[wave] = incl;
+  if (tid == 0) sh.pick = 0x7fffffff;
+  __syncthreads();
+  double base = 0.0;
+  for (int k = 0; k < wave; ++k) base += sh.wave_tot[k];
+  if (tid < nv && w > 0.0 && base + incl > sh.tile_target) atomicMin(&sh.pick, v0 + tid);
+  __syncthreads();
+  int res = sh.pick;
+  if (res == 0x7fffffff) {
+    // rounding past the tile's last cumulative weight: its last positive entry
+    __syncthreads();
+    if (tid == 0) sh.pick = -1;
+    __syncthreads();
+    if (tid < nv && w > 0.0) atomicMax(&sh.pick, v0 + tid);
+    __syncthreads();
+    res = sh.pick;
+  }
+  return res;
+}
+
 // Per-request walk state, kept in LDS and advanced by thread 0.
 struct WalkState {
   int u;            // current node (local row)
@@ -1262,7 +1353,7 @@ accept_sample_kernel(StatsArgs sa, int nstat, const int32_t* __restrict__ row_of
                      const int32_t* __restrict__ tokens, const float* __restrict__ p_logits,
                      const float* __restrict__ q_logits, int64_t ld, int vocab,
                      float temperature, uint64_t seed, uint64_t step, AcceptWs ws, WalkOut out,
-                     int max_spins) {
+                     int max_spins, HeadTiles ht) {
   __shared__ WalkShared sh;
   __shared__ WalkState st;
   if ((int)blockIdx.x < nstat) {
@@ -1398,6 +1489,11 @@ accept_sample_kernel(StatsArgs sa, int nstat, const int32_t* __restrict__ row_of
       c.lse_p = leaf_pass(sh, c, ++pass, ws.sref + (size_t)b * 2 * kMaxSlices);
       if (sh.timeout) break;
       final_token = walk_draw(sh, c, 0.0, false, sh.coin[1][u] * sh.total);
+      break;
+    }
+    if (action == 1 && !act_q && ht.hidden && sh.kid_start[u + 1] == sh.kid_start[u]) {
+      // a leaf on the LM-head path: its logits were not stored
+      final_token = head_leaf_draw(sh, c, ws, ht, o + u, b, pass_tag(++pass), sh.coin[1][u]);
       break;
     }
     if (action == 1 && !act_q) {                     // a draw from P_u alone
@@ -1652,9 +1748,11 @@ hipError_t launch_accept(const LaunchCtx& cx, int R, const int32_t* parents, con
   const int max_spins = walk.max_spins >= 0 ? walk.max_spins : kWalkMaxSpins;
   // nstat statistics items, then B * S <= capacity walk workgroups, which
   // take tickets (see the kernel).
+  HeadTiles ht{};
+  if (head) ht = *head;     // ht.hidden == nullptr: no LM head (every leaf draw reads its row)
   hipLaunchKernelGGL(accept_sample_kernel, dim3(nstat + cx.B * S), dim3(kWalkThreads), 0,
                      cx.stream, stats_args, nstat, cx.row_offsets_d, cx.B, R, S, parents, tokens,
-                     p_logits, q_logits, ld, vocab, temperature, seed, step, ws, out, max_spins);
+                     p_logits, q_logits, ld, vocab, temperature, seed, step, ws, out, max_spins, ht);
   return hipGetLastError();
 }
 

@@ -382,10 +382,14 @@ spec_status spec_lm_head_accept(const spec_batch* batch, const int32_t* parents_
   if (!workspace_d || workspace_bytes < need)
     return fail(SPEC_ERR_WORKSPACE, "LM head workspace %zu bytes < required %zu", workspace_bytes, need);
   if (!aligned16(workspace_d)) return fail(SPEC_ERR_SHAPE, "workspace must be 16-byte aligned");
-  const spec::HeadTiles tiles = spec::head_tiles((char*)workspace_d + acc_bytes, R, vocab);
+  spec::HeadTiles tiles = spec::head_tiles((char*)workspace_d + acc_bytes, R, vocab);
+  tiles.hidden = (const uint16_t*)head->hidden_d;
+  tiles.weight = (const uint16_t*)head->weight_d;
+  tiles.H = H;
   hipError_t e = spec::launch_lm_head(R, (const uint16_t*)head->hidden_d, H,
                                       (const uint16_t*)head->weight_d, vocab, temperature,
-                                      head->logits_d, logits_ld, tiles, stream);
+                                      head->logits_d, logits_ld, tiles, batch->batch,
+                                      batch->row_offsets_d, parents_d, stream);
   if (e != hipSuccess) return launched(e, "spec_lm_head_accept (head)");
   return launched(spec::launch_accept(ctx(batch, stream), R, parents_d, tokens_d, head->logits_d,
                                       (temperature > 0.0f && !topk) ? q_logits_d : nullptr,

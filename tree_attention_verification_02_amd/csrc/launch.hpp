@@ -79,12 +79,18 @@ struct HeadTiles {
   double* s;
   float* m;       // [R][ntile]  temperature 0 (aliases ref / s)
   int32_t* am;
+  uint8_t* kids;  // [R] 1 where the row has children: at T > 0 only those logits are stored
+  double* leafz;  // [B][kHeadTileV] a leaf's tile logits as the walk recomputes them (tagged)
+  const uint16_t* hidden;   // the head's operands, for that recomputation
+  const uint16_t* weight;
+  int H;
 };
 int head_vocab_tiles(int vocab);
 size_t head_tiles_bytes(int R, int vocab);
 HeadTiles head_tiles(void* base, int R, int vocab);
 hipError_t launch_lm_head(int R, const uint16_t* hidden, int H, const uint16_t* weight, int vocab,
                           float temperature, float* logits, int64_t ld, const HeadTiles& tiles,
+                          int B, const int32_t* row_offsets, const int32_t* parents,
                           hipStream_t stream);
 
 // Acceptance.  At temperature > 0, q_logits == nullptr selects deterministic

@@ -13,8 +13,11 @@
 //    statistics pass writes, so the walk merges either alike.  The terms are
 //    fp32 exponentials of the fp32 logits (the logits already carry the fp32
 //    accumulation error; the sums lose about 1e-7 more), added in fp64
-//    across lanes.  The logits are stored (fp32): the residual and bonus
-//    draws read back the few rows they need.
+//    across lanes.  The logits of the rows that have children are stored
+//    (fp32): the residual passes and draws at those nodes read them back.  A
+//    leaf's logits are needed only if the walk ends there, for one draw,
+//    which finds its 256-entry tile from these partials and recomputes that
+//    tile's logits alone; so leaf rows are not stored.
 //  * temperature 0: the tile's largest logit and its first index.  Nothing
 //    else is needed downstream, so the logits need not be stored.
 //
@@ -63,6 +66,7 @@ struct HeadArgs {
   int R, H, V;
   int nvt, nrt;             // vocabulary tiles, row tiles
   float* logits;            // [R][ld] or null
+  const uint8_t* store;     // [R] rows whose logits are stored (null: every row)
   int64_t ld;
   int greedy;
   double inv_t;
@@ -238,6 +242,10 @@ __global__ void __launch_bounds__(WAVES * 64, 1) lm_head_kernel(HeadArgs a) {
     // region, 16-byte chunk c (4 logits) of row rr sits at slot c ^ rr of
     // the row's 512 bytes: the writes (16 rows at one chunk) and the row
     // reads (16 chunks of one row) both touch all 64 banks once.
+    // which of the tile's rows are stored, read once into LDS
+    __shared__ unsigned char s_keep[kBN];
+    for (int i = tid; i < kBN; i += WAVES * 64)
+      s_keep[i] = (r0 + i < a.R) && (!a.store || a.store[r0 + i]);
     __syncthreads();                                 // every wave is done with the ring
     char* reg = (wave < G::HW ? st0 : st1) + (wave % G::HW) * 16384;
     static_assert(G::HW * 16384 <= G::STAGE, "staging regions fit one ring slot");
@@ -258,7 +266,7 @@ __global__ void __launch_bounds__(WAVES * 64, 1) lm_head_kernel(HeadArgs a) {
         const int rr = 2 * t + half;
         const f32x4 x = *reinterpret_cast<const f32x4*>(reg + rr * 512 + ((l31 ^ rr) << 4));
         const int r = r0 + wr * JT * 32 + 32 * j + rr;
-        if (r >= a.R) continue;
+        if (!s_keep[r - r0]) continue;
         float* dst = a.logits + (int64_t)r * a.ld + vcol;
         if (vcol + 3 < a.V) {
           // streaming hint: the walk reads back only a few rows, so the
@@ -362,6 +370,24 @@ __global__ void __launch_bounds__(WAVES * 64, 1) lm_head_kernel(HeadArgs a) {
   }
 }
 
+// Which rows have children (one workgroup per request, whose rows are
+// contiguous and at most kMaxRows), and the request's slot of recomputed
+// leaf logits cleared to tag 0.  Parents outside 0 .. row-1 mark nothing
+// (the acceptance reports such a tree as invalid and reads no logits).
+__global__ void __launch_bounds__(kHeadTileV)
+head_rows_kernel(const int32_t* __restrict__ row_offsets, const int32_t* __restrict__ parents,
+                 uint8_t* kids, double* leafz) {
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const int o = row_offsets[b], n = row_offsets[b + 1] - o;
+  for (int i = tid; i < n; i += kHeadTileV) kids[o + i] = 0;
+  leafz[(int64_t)b * kHeadTileV + tid] = 0.0;
+  __syncthreads();
+  for (int i = tid; i < n; i += kHeadTileV) {
+    const int p = parents[o + i];
+    if (i > 0 && p >= 0 && p < i) kids[o + p] = 1;
+  }
+}
+
 constexpr int kBK = 64;
 constexpr int kStages = 2;
 constexpr int kWaves = 8;
@@ -372,8 +398,10 @@ int head_vocab_tiles(int vocab) { return (vocab + kBM - 1) / kBM; }
 
 size_t head_tiles_bytes(int R, int vocab) {
   const size_t n = (size_t)R * head_vocab_tiles(vocab);
-  // (ref, s) doubles for sampling; (max, argmax) share the same space at T = 0
-  return 2 * ((n * sizeof(double) + 255) & ~(size_t)255);
+  // (ref, s) doubles for sampling; (max, argmax) share the same space at T = 0;
+  // then the children marks and the leaf-logit slots (B <= R requests)
+  return 2 * ((n * sizeof(double) + 255) & ~(size_t)255) + (((size_t)R + 255) & ~(size_t)255) +
+         (size_t)R * kHeadTileV * sizeof(double);
 }
 
 HeadTiles head_tiles(void* base, int R, int vocab) {
@@ -386,11 +414,17 @@ HeadTiles head_tiles(void* base, int R, int vocab) {
   t.s = (double*)(p + half);
   t.m = (float*)p;            // greedy: the reference / sum arrays are unused
   t.am = (int32_t*)(p + half);
+  t.kids = (uint8_t*)(p + 2 * half);
+  t.leafz = (double*)(p + 2 * half + (((size_t)R + 255) & ~(size_t)255));
+  t.hidden = nullptr;
+  t.weight = nullptr;
+  t.H = 0;
   return t;
 }
 
 hipError_t launch_lm_head(int R, const uint16_t* hidden, int H, const uint16_t* weight, int vocab,
                           float temperature, float* logits, int64_t ld, const HeadTiles& tiles,
+                          int B, const int32_t* row_offsets, const int32_t* parents,
                           hipStream_t stream) {
   HeadArgs a;
   a.hidden = hidden;
@@ -401,8 +435,14 @@ hipError_t launch_lm_head(int R, const uint16_t* hidden, int H, const uint16_t* 
   a.nvt = head_vocab_tiles(vocab);
   a.nrt = (R + kBN - 1) / kBN;
   a.logits = logits;
+  a.store = nullptr;
   a.ld = ld;
   a.greedy = temperature == 0.0f;
+  if (!a.greedy) {
+    hipLaunchKernelGGL(head_rows_kernel, dim3((unsigned)B), dim3(kHeadTileV), 0, stream, row_offsets,
+                       parents, tiles.kids, tiles.leafz);
+    a.store = tiles.kids;
+  }
   a.inv_t = a.greedy ? 0.0 : 1.0 / (double)temperature;
   a.tiles = tiles;
   const int groups = (a.nvt + 7) / 8;

@@ -36,8 +36,9 @@ class VerifyStep:
         (deterministic children: spec_accept_topk, draft rows unused).
         ``head``: optional (hidden [R][H], weight [V][H]) bf16 tensors; the
         target logits then come from the LM head (spec_lm_head_accept) instead
-        of ``w.p_logits``, and are kept in ``head_logits`` (always at
-        temperature > 0; at 0 only with ``store_head_logits``)."""
+        of ``w.p_logits``, and are kept in ``head_logits`` (at temperature > 0
+        the rows of nodes with children; at 0 every row, only with
+        ``store_head_logits``)."""
         if acceptance not in ("sample", "topk"):
             raise ValueError(f"acceptance must be 'sample' or 'topk', not {acceptance!r}")
         self.acceptance = acceptance
