@@ -306,6 +306,37 @@ def test_head_single_row_single_tile(lib, T):
         log("[parity] single-row bonus draw near a boundary: compared up to it")
 
 
+@pytest.mark.parametrize("T", [1.0, 0.3])
+def test_head_leaf_draws_recompute_their_tile(lib, T):
+    """Every walk ends at a leaf: 24 requests of a single row each (the root
+    is the leaf), a vocabulary of 40000 (3 statistics chunks, 157 tiles, the
+    last one partial).  No logits are stored; every bonus draw finds its tile
+    from the head's partials and recomputes it, shared among the request's
+    walk workgroups.  Tokens against the oracle's draws on the oracle logits
+    (a draw within 1e-7 of the mass of a boundary is reported, not failed)."""
+    from oracle import accept as OA
+    B, V = 24, 40000
+    trees = [np.array([-1])] * B
+    w = make("dynamic", B=B, L=[9] * B, V=V, Hq=2, Hkv=1, tree=("given", trees),
+             given_tokens=np.arange(B, dtype=np.int32))
+    hidden, weight = W.heads.head_inputs(w, H=320)
+    vs = run_step(w, temperature=T, seed=6, step=2, commit=False, head=(hidden, weight))
+    z, bound = oracle_head_logits(hidden, weight, list(range(w.R)))
+    alen = vs.acc.accept_len.cpu().numpy()
+    path = vs.acc.path.cpu().numpy()
+    toks = vs.acc.tokens.cpu().numpy()
+    flagged = 0
+    for b in range(B):
+        r = OA.accept_request(w.parents[b:b + 1], w.tokens[b:b + 1], z[b:b + 1], None, T, 6, 2, b)
+        f, same = r["result"].check_outputs(alen[b], path[b], toks[b], flag_eps=FLAG_EPS,
+                                            what=f"request {b}")
+        flagged += f
+        assert same or f, b
+    log(f"[parity] head leaf draws, T={T}: {B} requests, {flagged} near a boundary, tokens "
+        f"{toks[:, 0].tolist()}")
+    assert len(set(toks[:, 0].tolist())) > B // 2       # draws spread over the vocabulary
+
+
 def test_head_full_size_specinfer_wide(lib):
     """The SpecInfer batch at full size with the 70B-class width H = Hq * D =
     8192: 368 rows (the second row tile holds 112), vocabulary 128256; the last
