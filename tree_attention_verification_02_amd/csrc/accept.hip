@@ -33,7 +33,10 @@
 //    sums go to global memory carrying their pass tag, and every slice reads
 //    all of them (bounded polls), sums them in the same order and replays
 //    the same scalar decisions, so no further broadcast is needed; slice 0
-//    rescans the drawn segment and writes the outputs.
+//    rescans the drawn segment and writes the outputs.  With the LM head's
+//    partials, a leaf's logits were never stored: its bonus draw finds the
+//    256-entry tile from the head's tile partials and the slices recompute
+//    that tile's logits from the hidden row and the weight rows.
 //  * accept_argmax (T = 0): the first argmax of every target-row chunk;
 //    accept_finalize merges them per row.
 //  * accept_greedy: temperature 0, one workgroup per request.
