@@ -267,15 +267,14 @@ def test_head_greedy_without_logits(lib):
 
 
 def test_head_full_size_sampled(lib):
-    """The batched dynamic workload at full size (64 requests, 1024 rows,
-    vocabulary 128256, H = 4096), the launch the benchmark times: logits and
-    acceptance of three requests (first, middle, last -- the last row tile)
-    against the oracle, and every request against the plain acceptance on
-    the stored logits."""
+    """The batched dynamic workload at full size (64 requests, 1024 rows in
+    four row tiles, vocabulary 128256, H = 4096), the launch the benchmark
+    times: stored logits and acceptance of every request against the oracle,
+    and every request against the plain acceptance on the head's logits."""
     w = make("dynamic")
     hidden, weight = W.heads.head_inputs(w)
     vs = run_step(w, temperature=1.0, seed=0, step=0, commit=False, head=(hidden, weight))
-    req = [0, w.B // 2, w.B - 1]
+    req = list(range(w.B))
     rows = _rows_of(w, req)
     z, bound = oracle_head_logits(hidden, weight, rows)
     _check_sampled(w, vs, req, rows, z, bound, 1.0, 0, False)
@@ -339,13 +338,13 @@ def test_head_leaf_draws_recompute_their_tile(lib, T):
 
 def test_head_full_size_specinfer_wide(lib):
     """The SpecInfer batch at full size with the 70B-class width H = Hq * D =
-    8192: 368 rows (the second row tile holds 112), vocabulary 128256; the last
-    request against the oracle, every request against the plain acceptance."""
+    8192: 368 rows (the second row tile holds 112), vocabulary 128256; every
+    request against the oracle and against the plain acceptance."""
     w = make("specinfer")
     hidden, weight = W.heads.head_inputs(w)
     assert hidden.shape[1] == 8192
     vs = run_step(w, temperature=1.0, seed=2, step=0, commit=False, head=(hidden, weight))
-    req = [w.B - 1]
+    req = list(range(w.B))
     rows = _rows_of(w, req)
     z, bound = oracle_head_logits(hidden, weight, rows)
     _check_sampled(w, vs, req, rows, z, bound, 1.0, 2, False)
