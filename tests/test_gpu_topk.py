@@ -133,6 +133,10 @@ SMALL = {
     "specinfer-small": ("specinfer", dict(B=3, L=700, Hq=16, Hkv=2, V=6000)),
     "dynamic-small": ("dynamic", dict(B=6, L=("uniform", 30, 700), V=5000)),
     "toy": ("toy", dict()),
+    # 48 requests: at 32 and more the walks go first in the grid and wait for
+    # their rows' partials while the statistics stream behind them
+    "dynamic-48-walks-first": ("dynamic", dict(B=48, L=("uniform", 30, 300), V=20000, Hq=4,
+                                               Hkv=1)),
 }
 
 
