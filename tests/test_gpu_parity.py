@@ -63,6 +63,26 @@ def test_small_sampling(lib, case):
             assert bits_equal(w.k_cache[b, :, :L], snap[b, :, :L])
 
 
+# Batches of 8 requests and more run with the walks first in the grid: each
+# walk takes a node's statistics when it reaches the node, while the
+# statistics of deeper rows still stream.  Chains make a walk wait at every
+# level; wide trees make it pass over residuals between the waits.
+WALKS_FIRST = {
+    "chain8-batch12": ("chain8", dict(B=12, L=100, V=3000, Hq=4, Hkv=4)),
+    "medusa-batch8": ("medusa", dict(B=8, L=64, V=2000, Hq=4, Hkv=4, tree=("cartesian", (2, 3, 2)))),
+    "dynamic-batch20": ("dynamic", dict(B=20, L=("uniform", 8, 200), V=5000, Hq=4, Hkv=1)),
+}
+
+
+@pytest.mark.parametrize("case", list(WALKS_FIRST))
+@pytest.mark.parametrize("T,seed,step", [(1.0, 0, 0), (0.3, 4, 1), (2.0, 9, 3)])
+def test_walks_first_batches(lib, case, T, seed, step):
+    base, kw = WALKS_FIRST[case]
+    w = make(base, **kw)
+    vs = run_step(w, temperature=T, seed=seed, step=step, commit=False)
+    check_accept(w, vs, T, seed, step)
+
+
 @pytest.mark.parametrize("case", ["chain8-small", "medusa-small", "dynamic-small", "toy"])
 def test_small_greedy(lib, case):
     w = make(BASE[case], **SMALL[case])

@@ -170,10 +170,11 @@ SPEC_DEVICE int find_request(const int* off, int B, int r) {   // off[b] <= r < 
 __global__ void __launch_bounds__(kPrepThreads)
 accept_prep_kernel(const int32_t* __restrict__ row_offsets, int B, int R,
                    const int32_t* __restrict__ parents, AcceptWs ws, int vocab, int list_p,
-                   int list_q) {
+                   int list_q, int wfirst) {
   __shared__ int s_off[kPrepMaxBatch + 1];
   __shared__ unsigned char s_kids[kPrepMaxRows];
   __shared__ int s_wave[kPrepThreads / 64];
+  __shared__ int s_key[kMaxRows + 1];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   if (blockIdx.x > 0) {
     const int64_t nseg_all = (int64_t)B * 2 * ((vocab + kSeg - 1) / kSeg);
@@ -190,8 +191,48 @@ accept_prep_kernel(const int32_t* __restrict__ row_offsets, int B, int R,
     }
     return;
   }
+  const int m = (list_q ? 1 : 0) + (list_p ? 1 : 0);   // entries per listed node (walks first)
   if (!list_p && !list_q) {
     if (tid == 0) ws.sync[2] = ws.sync[3] = 0;
+  } else if (wfirst && (R > kPrepMaxRows || B > kPrepMaxBatch)) {
+    for (int r = tid; r < R; r += kPrepThreads) {
+      int j = 0;
+      if (list_q) ws.order[m * r + j++] = R + r;
+      if (list_p) ws.order[m * r + j] = r;
+    }
+    if (tid == 0) ws.sync[2] = m * R;
+  } else if (wfirst) {
+    // Walks first: one list, the draft then the target row of each node that
+    // has children, nodes ordered by their index inside their request (all
+    // roots, then every request's row 1, ...).  Rows are in tree order (a
+    // parent before its children), so the statistics a walk needs next
+    // arrive about when it gets there.  A counting sort over the 256 local
+    // indices; the order inside one index is immaterial.
+    for (int i = tid; i <= B; i += kPrepThreads) s_off[i] = row_offsets[i];
+    for (int r = tid; r < R; r += kPrepThreads) s_kids[r] = 0;
+    for (int i = tid; i <= kMaxRows; i += kPrepThreads) s_key[i] = 0;
+    __syncthreads();
+    for (int r = tid; r < R; r += kPrepThreads) {
+      const int b = find_request(s_off, B, r);
+      const int u = r - s_off[b], pu = parents[r];
+      if (u > 0 && pu >= 0 && pu < u) s_kids[s_off[b] + pu] = 1;
+    }
+    __syncthreads();
+    for (int r = tid; r < R; r += kPrepThreads)
+      if (s_kids[r]) atomicAdd(&s_key[r - s_off[find_request(s_off, B, r)] + 1], 1);
+    __syncthreads();
+    if (tid == 0) {                                      // exclusive prefix over the indices
+      for (int i = 1; i <= kMaxRows; ++i) s_key[i] += s_key[i - 1];
+      ws.sync[2] = m * s_key[kMaxRows];
+    }
+    __syncthreads();
+    for (int r = tid; r < R; r += kPrepThreads)
+      if (s_kids[r]) {
+        const int pos = atomicAdd(&s_key[r - s_off[find_request(s_off, B, r)]], 1);
+        int j = 0;
+        if (list_q) ws.order[m * pos + j++] = R + r;
+        if (list_p) ws.order[m * pos + j] = r;
+      }
   } else if (R > kPrepMaxRows || B > kPrepMaxBatch) {
     for (int r = tid; r < R; r += kPrepThreads) {
       ws.order[r] = R + r;
@@ -349,9 +390,9 @@ SPEC_DEVICE void sample_stats_item(const StatsArgs& a, const AcceptWs& ws, int i
   // entries past that list end at once before the live ones, not between
   // the last statistics and the walk workgroups.
   int rr;
-  if (a.wfirst) {                                    // listed target rows, in row order
-    if (e >= ws.sync[3]) return;
-    rr = ws.order[a.R + e];
+  if (a.wfirst) {                                    // one list (walks first)
+    if (e >= ws.sync[2]) return;
+    rr = ws.order[e];
   } else if (e < a.nq) {
     if (e >= ws.sync[2]) return;                     // past the listed draft rows
     rr = ws.order[e];
@@ -470,8 +511,10 @@ SPEC_DEVICE unsigned long long load_partial(const double* p) {
   return __hip_atomic_load(reinterpret_cast<unsigned long long*>(const_cast<double*>(p)),
                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-// False if some partial never showed its tag (the polls gave up).
-SPEC_DEVICE bool merged_ref_sum(const AcceptWs& ws, int rr, const double* tab, double& lse) {
+// False if some partial never showed its tag (the polls gave up; with
+// max_spins = 0: not all published yet).
+SPEC_DEVICE bool merged_ref_sum(const AcceptWs& ws, int rr, const double* tab, double& lse,
+                               int max_spins = kWalkMaxSpins) {
   const int nch = ws.nch;
   const double* pr = ws.part_ref + (int64_t)rr * nch;
   const double* ps = ws.part_s + (int64_t)rr * nch;
@@ -488,7 +531,7 @@ SPEC_DEVICE bool merged_ref_sum(const AcceptWs& ws, int rr, const double* tab, d
     for (int j = 0; j < 8; ++j) {
       if (c0 + j >= nch) break;
       int spins = 0;
-      while (((r8[j] & s8[j]) & 0xffull) == 0 && ++spins <= kWalkMaxSpins) {
+      while (((r8[j] & s8[j]) & 0xffull) == 0 && ++spins <= max_spins) {
         __builtin_amdgcn_s_sleep(1);
         r8[j] = load_partial(pr + c0 + j);
         s8[j] = load_partial(ps + c0 + j);
@@ -561,6 +604,7 @@ struct WalkShared {
   double chunk_base, chunk_target;   // P-only draw: mass before the drawn chunk, the target
   double frame;                      // leaf pass: the reference its sums were rescaled to
   int chunk;                         // P-only draw: the chunk holding the target (-1: none)
+  unsigned char ready[kMaxRows];     // walks first: node's row statistics merged (lazily)
   int tile;                          // LM-head leaf draw: the 256-entry tile holding the target
   double tile_target;                //   and the target less the mass before that tile
   int found_seg;
@@ -1265,13 +1309,50 @@ SPEC_DEVICE int head_leaf_draw(WalkShared& sh, const WalkCtx& c, const AcceptWs&
   return res;
 }
 
+// The statistics of one node, merged when the walk reaches it (walks that
+// go first in the grid, while the statistics still stream): the
+// log-sum-exps of its rows from their chunk partials (polled until
+// published), then P_u(x_c), Q_u(x_c) of its children, with the arithmetic
+// of the all-rows form (the children's logits load while the partials are
+// polled).  Block-wide; sets sh.timeout if a partial never arrives.  (Also
+// merging, in the same round trip, every other row whose partials were
+// already in measured slower: the extra loads lengthen each step.)
+SPEC_DEVICE void node_stats(WalkShared& sh, const AcceptWs& ws, int R, int o, int u,
+                            const float* p_logits, const float* q_logits, int64_t ld, int vocab,
+                            double invT, bool topk) {
+  const int tid = threadIdx.x;
+  const int k0 = sh.kid_start[u], nk = sh.kid_start[u + 1] - k0;
+  float lp = 0.0f, lq = 0.0f;
+  bool cv = false;
+  int ch = -1;
+  if (tid < nk) {
+    ch = sh.kid_list[k0 + tid];
+    const int x = sh.tok[ch];
+    if (x >= 0 && x < vocab) {
+      cv = true;
+      lp = (p_logits + (int64_t)(o + u) * ld)[x];
+      if (!topk) lq = (q_logits + (int64_t)(o + u) * ld)[x];
+    }
+  }
+  if (tid < (topk ? 1 : 2) && !merged_ref_sum(ws, tid * R + o + u, sh.tab, sh.lse[tid][u]))
+    sh.timeout = 1;
+  __syncthreads();
+  if (tid < nk) {
+    sh.cp[ch] = cv ? exp_f64((double)lp * invT - sh.lse[0][u], sh.tab) : 0.0;
+    if (!topk) sh.cq[ch] = cv ? exp_f64((double)lq * invT - sh.lse[1][u], sh.tab) : 0.0;
+  }
+  if (tid == 0) sh.ready[u] = 1;
+  __syncthreads();
+}
+
 // Per-request walk state, kept in LDS and advanced by thread 0.
 struct WalkState {
   int u;            // current node (local row)
   int kidx;         // next child of u to test (index into kid_list)
   double t, N;      // residual R = max(0, P_u - t Q_u) / N
   double pass_t;    // t of the weights the last pass left (-1: none at u)
-  int action;       // 0: pass, 1: pass then draw, 2: draw from the last pass, 3: stop
+  int action;       // 0: pass, 1: pass then draw, 2: draw from the last pass, 3: stop,
+                    // 4: merge the statistics of node u (walks first)
   double act_t;     // t of the pass to run
   int act_q;        // whether the pass needs the draft row
 };
@@ -1279,7 +1360,8 @@ struct WalkState {
 // Thread 0: run sibling tests and moves until a vocabulary pass (or a draw)
 // is needed.  Coins (sh.coin): purpose 0 for the accept test of child c,
 // purpose 1 for the draw at the node where the walk stops.
-SPEC_DEVICE void walk_decide(WalkShared& sh, WalkState& st, int path_stride, bool topk) {
+SPEC_DEVICE void walk_decide(WalkShared& sh, WalkState& st, int path_stride, bool topk,
+                             bool lazy) {
   while (true) {
     const int u = st.u;
     const int k0 = sh.kid_start[u], k1 = sh.kid_start[u + 1];
@@ -1327,6 +1409,10 @@ SPEC_DEVICE void walk_decide(WalkShared& sh, WalkState& st, int path_stride, boo
       st.N = 1.0;
       st.pass_t = -1.0;
       sh.nrej = 0;
+      if (lazy && !sh.ready[ch] && sh.kid_start[ch + 1] > sh.kid_start[ch]) {
+        st.action = 4;                   // merge the new node's statistics first
+        return;
+      }
       continue;
     }
     if (topk) {                          // reject: drop x from the residual
@@ -1354,6 +1440,7 @@ SPEC_DEVICE void walk_decide(WalkShared& sh, WalkState& st, int path_stride, boo
 // dispatched as the statistics drain and load their trees meanwhile; each
 // then polls the partials of its rows until they are published (a bounded
 // wait: a request whose partials never arrive reports a timeout).
+template <bool kLazy>
 __global__ void __launch_bounds__(kWalkThreads, 4)
 accept_sample_kernel(StatsArgs sa, int nstat, const int32_t* __restrict__ row_offsets, int B,
                      int R, int S, const int32_t* __restrict__ parents,
@@ -1363,8 +1450,8 @@ accept_sample_kernel(StatsArgs sa, int nstat, const int32_t* __restrict__ row_of
                      int max_spins, HeadTiles ht) {
   __shared__ WalkShared sh;
   __shared__ WalkState st;
-  if (sa.wfirst ? (int)blockIdx.x >= B * S : (int)blockIdx.x < nstat) {
-    sample_stats_item(sa, ws, (int)blockIdx.x - (sa.wfirst ? B * S : 0), sh.tab, sh.red_m,
+  if (kLazy ? (int)blockIdx.x >= B * S : (int)blockIdx.x < nstat) {
+    sample_stats_item(sa, ws, (int)blockIdx.x - (kLazy ? B * S : 0), sh.tab, sh.red_m,
                       sh.wave_tot);
     return;
   }
@@ -1374,7 +1461,7 @@ accept_sample_kernel(StatsArgs sa, int nstat, const int32_t* __restrict__ row_of
   // workgroups fit on the device at once (no cooperative launch needed).
   __shared__ int s_ticket;
   if (threadIdx.x == 0)
-    s_ticket = sa.wfirst ? (int)blockIdx.x                  // every walk workgroup resident
+    s_ticket = kLazy ? (int)blockIdx.x                      // every walk workgroup resident
                : (S == 1) ? (int)blockIdx.x - nstat
                           : __hip_atomic_fetch_add(ws.sync, 1, __ATOMIC_RELAXED,
                                                    __HIP_MEMORY_SCOPE_AGENT);
@@ -1394,55 +1481,68 @@ accept_sample_kernel(StatsArgs sa, int nstat, const int32_t* __restrict__ row_of
   }
   load_tree(sh, parents, tokens, o, n, sh.tab);
   // This request's row statistics: each row's log-sum-exp from its chunk
-  // partials (in chunk order), then each child's P_u(x_c), Q_u(x_c) in fp64.
-  // Every slice computes them; slice 0 writes the fp32 outputs (NaN at roots
-  // and at rows whose parent is invalid; Q is NaN everywhere without draft
-  // rows).  Thread k takes row k's partials and child k's logit; all of
-  // them are loaded at once (one memory round trip), the child logits are
-  // held in registers until the parents' log-sum-exps are in LDS.
+  // partials (in chunk order), then each child's P_u(x_c), Q_u(x_c) in fp64;
+  // `write`: slice 0 writes the fp32 outputs (NaN at roots and at rows whose
+  // parent is invalid; Q is NaN everywhere without draft rows).  Thread k
+  // takes row k's partials and child k's logit; all of them are loaded at
+  // once (one memory round trip), the child logits are held in registers
+  // until the parents' log-sum-exps are in LDS.  Walks that go first in the
+  // grid merge node by node as they reach them instead (node_stats) and run
+  // this at their end, for the outputs.
   const bool topk = q_logits == nullptr;
   const double invT = 1.0 / (double)temperature;
-  constexpr int kRowsPerThread = 2 * kMaxRows / kWalkThreads;
-  float clog[kRowsPerThread];
-  bool cval[kRowsPerThread];
+  constexpr bool lazy = kLazy;   // walks first in the grid (then sa.wfirst too)
+  auto all_rows = [&](bool write) {
+    constexpr int kRowsPerThread = 2 * kMaxRows / kWalkThreads;
+    float clog[kRowsPerThread];
+    bool cval[kRowsPerThread];
 #pragma unroll
-  for (int j = 0; j < kRowsPerThread; ++j) {
-    const int k = tid + j * kWalkThreads;
-    const int which = k >= n ? 1 : 0;
-    const int i = k - which * n;
-    cval[j] = false;
-    clog[j] = 0.0f;
-    if (k < 2 * n && !(which && topk)) {
-      const int pu = sh.par[i];
-      const int x = sh.tok[i];
-      if (i > 0 && pu >= 0 && pu < i && x >= 0 && x < vocab) {
-        cval[j] = true;
-        clog[j] = ((which ? q_logits : p_logits) + (int64_t)(o + pu) * ld)[x];
+    for (int j = 0; j < kRowsPerThread; ++j) {
+      const int k = tid + j * kWalkThreads;
+      const int which = k >= n ? 1 : 0;
+      const int i = k - which * n;
+      cval[j] = false;
+      clog[j] = 0.0f;
+      if (k < 2 * n && !(which && topk)) {
+        const int pu = sh.par[i];
+        const int x = sh.tok[i];
+        if (i > 0 && pu >= 0 && pu < i && x >= 0 && x < vocab) {
+          cval[j] = true;
+          clog[j] = ((which ? q_logits : p_logits) + (int64_t)(o + pu) * ld)[x];
+        }
+        // (rows of nodes with children only, and with the LM head every target
+        // row: the others are not streamed)
+        if (!sh.bad && ((!which && sa.leafp) || sh.kid_start[i + 1] > sh.kid_start[i]) &&
+            !merged_ref_sum(ws, which * R + o + i, sh.tab, sh.lse[which][i]))
+          sh.timeout = 1;
       }
-      // (rows of nodes with children only, and with the LM head every target
-      // row: the others are not streamed)
-      if (!sh.bad && ((!which && sa.leafp) || sh.kid_start[i + 1] > sh.kid_start[i]) &&
-          !merged_ref_sum(ws, which * R + o + i, sh.tab, sh.lse[which][i]))
-        sh.timeout = 1;
     }
-  }
-  __syncthreads();
+    __syncthreads();
 #pragma unroll
-  for (int j = 0; j < kRowsPerThread; ++j) {
-    const int k = tid + j * kWalkThreads;
-    if (k >= 2 * n) continue;
-    const int which = k >= n ? 1 : 0;
-    const int i = k - which * n;
-    float* dst = which ? out.child_q : out.child_p;
-    const int pu = sh.par[i];
-    double val = __longlong_as_double(0x7ff8000000000000LL);
-    if (!sh.bad && i > 0 && pu >= 0 && pu < i && !(which && topk)) {   // (NaN: invalid tree)
-      val = cval[j] ? exp_f64((double)clog[j] * invT - sh.lse[which][pu], sh.tab) : 0.0;
-      (which ? sh.cq : sh.cp)[i] = val;
+    for (int j = 0; j < kRowsPerThread; ++j) {
+      const int k = tid + j * kWalkThreads;
+      if (k >= 2 * n) continue;
+      const int which = k >= n ? 1 : 0;
+      const int i = k - which * n;
+      float* dst = which ? out.child_q : out.child_p;
+      const int pu = sh.par[i];
+      double val = __longlong_as_double(0x7ff8000000000000LL);
+      if (!sh.bad && i > 0 && pu >= 0 && pu < i && !(which && topk)) {   // (NaN: invalid tree)
+        val = cval[j] ? exp_f64((double)clog[j] * invT - sh.lse[which][pu], sh.tab) : 0.0;
+        (which ? sh.cq : sh.cp)[i] = val;
+      }
+      if (dst && write) dst[o + i] = (float)val;
     }
-    if (dst && slice == 0) dst[o + i] = (float)val;
+    __syncthreads();
+  };
+  if (!lazy || sh.bad) {
+    all_rows(slice == 0);
+  } else if constexpr (lazy) {
+    if (tid < n) sh.ready[tid] = 0;
+    __syncthreads();
+    if (sh.kid_start[1] > sh.kid_start[0])
+      node_stats(sh, ws, R, o, 0, p_logits, q_logits, ld, vocab, invT, topk);
   }
-  __syncthreads();
   if (sh.bad) {
     if (slice == 0) write_abandoned(out, b, o, n, kFlagBadTree);
     return;
@@ -1480,10 +1580,15 @@ accept_sample_kernel(StatsArgs sa, int nstat, const int32_t* __restrict__ row_of
   int final_token = -1;
   while (true) {
     if (tid == 0)
-      walk_decide(sh, st, out.path_stride, topk);
+      walk_decide(sh, st, out.path_stride, topk, lazy);
     __syncthreads();
     const int action = st.action;
     if (action == 3) break;
+    if (lazy && action == 4) {
+      node_stats(sh, ws, R, o, st.u, p_logits, q_logits, ld, vocab, invT, topk);
+      if (sh.timeout) break;
+      continue;
+    }
     const int u = st.u;
     c.p = p_logits + (int64_t)(o + u) * ld;
     c.q = topk ? nullptr : q_logits + (int64_t)(o + u) * ld;
@@ -1552,6 +1657,7 @@ accept_sample_kernel(StatsArgs sa, int nstat, const int32_t* __restrict__ row_of
   // gave up at one (then the request reports the timeout).
   if (slice != 0) return;
   __syncthreads();
+  if (lazy && !sh.timeout) all_rows(true);     // every child's probabilities, for the outputs
   if (sh.timeout) {
     write_abandoned(out, b, o, n, sh.flags | kFlagSyncTimeout);
     return;
@@ -1682,10 +1788,13 @@ static hipError_t walk_capacity(int dev, int* capacity) {
   hipError_t e;
   if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess)
     return e;
-  if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, accept_sample_kernel, kWalkThreads,
-                                                        0)) != hipSuccess)
+  int per_cu_lazy = 0;
+  if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, accept_sample_kernel<false>,
+                                                        kWalkThreads, 0)) != hipSuccess ||
+      (e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu_lazy, accept_sample_kernel<true>,
+                                                        kWalkThreads, 0)) != hipSuccess)
     return e;
-  *capacity = cus * per_cu;
+  *capacity = cus * std::min(per_cu, per_cu_lazy);
   if (dev >= 0 && dev < kMaxDevices) cached[dev].store(*capacity, std::memory_order_relaxed);
   return hipSuccess;
 }
@@ -1700,7 +1809,7 @@ int walk_slices(int B, int vocab, int capacity_blocks) {
   return S;
 }
 
-constexpr int kWalkFirstMinBatch = 32;   // requests from which top-k walks go first in the grid
+constexpr int kWalkFirstMinBatch = 8;    // requests from which the walks go first in the grid
 
 hipError_t launch_accept(const LaunchCtx& cx, int R, const int32_t* parents, const int32_t* tokens,
                          const float* p_logits, const float* q_logits, int64_t ld, int vocab,
@@ -1721,26 +1830,45 @@ hipError_t launch_accept(const LaunchCtx& cx, int R, const int32_t* parents, con
   int nstat = 0;
   StatsArgs stats_args{p_logits, q_logits, ld, vocab, R, 0, 0, head ? 1 : 0, 0,
                        1.0 / (double)temperature};
+  if (!greedy && (!head || q_logits)) {
+    stats_args.np = head ? 0 : R;
+    stats_args.nq = q_logits ? R : 0;
+    nstat = (stats_args.np + stats_args.nq) * nch;
+  }
+  int S = 1;
   if (!greedy) {
+    int dev = 0;
+    if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
+    int capacity = 0;
+    if ((e = walk_capacity(dev, &capacity)) != hipSuccess) return e;
+    S = walk_slices(cx.B, vocab, capacity);
+    // Walks first in the grid (batches of kWalkFirstMinBatch requests or
+    // more): the walk workgroups load their trees and take each node's
+    // statistics as they reach it (node_stats), while the statistics stream
+    // behind them in the order walks need them (every root first), so the
+    // walks' set-ups and root decisions overlap the streaming.  They hold at
+    // most half of the device, so every walk workgroup is resident at once
+    // (no tickets) and the statistics keep the other half.
+    if (nstat > 0 && !head && cx.B >= kWalkFirstMinBatch && cx.B <= capacity / 2 &&
+        walk.max_slices <= 0) {
+      stats_args.wfirst = 1;
+      S = walk_slices(cx.B, vocab, capacity / 2);
+    }
+    if (walk.max_slices > 0) S = walk.max_slices < S ? walk.max_slices : S;
     // the rows to stream (and the walk's exchange area cleared)
     const int64_t nseg_all = (int64_t)cx.B * 2 * segs_for(vocab);
     const int clear_blocks =
         (int)std::max<int64_t>(1, std::min<int64_t>(256, (nseg_all + kPrepThreads - 1) / kPrepThreads));
     hipLaunchKernelGGL(accept_prep_kernel, dim3(1 + clear_blocks), dim3(kPrepThreads), 0,
                        cx.stream, cx.row_offsets_d, cx.B, R, parents, ws, vocab, head ? 0 : 1,
-                       q_logits ? 1 : 0);
+                       q_logits ? 1 : 0, stats_args.wfirst);
   }
   if (head)
     hipLaunchKernelGGL(accept_head_merge_kernel, dim3((R * nch + 3) / 4), dim3(256), 0,
                        cx.stream, cx.B, R, *head, greedy ? 1 : 0, ws, vocab);
-  if (greedy && !head) {
+  if (greedy && !head)
     hipLaunchKernelGGL(accept_argmax_kernel, dim3(R * nch), dim3(kStatThreads), 0, cx.stream,
                        p_logits, ld, vocab, ws);
-  } else if (!greedy && (!head || q_logits)) {
-    stats_args.np = head ? 0 : R;
-    stats_args.nq = q_logits ? R : 0;
-    nstat = (stats_args.np + stats_args.nq) * nch;
-  }
   if ((e = hipGetLastError()) != hipSuccess) return e;
   WalkOut out{accept_len, path, tokens_out, accept_mask, flags, path_stride, child_p, child_q};
   if (temperature == 0.0f) {
@@ -1750,34 +1878,21 @@ hipError_t launch_accept(const LaunchCtx& cx, int R, const int32_t* parents, con
                        cx.row_offsets_d, parents, tokens, ws, out);
     return hipGetLastError();
   }
-  int dev = 0;
-  if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
-  int capacity = 0;
-  if ((e = walk_capacity(dev, &capacity)) != hipSuccess) return e;
-  int S = walk_slices(cx.B, vocab, capacity);
-  // Deterministic children stream only the target rows, and their walks make
-  // no pass before the final draw: in large batches the walks then go first
-  // in the grid, load their trees and wait for their rows' partials while
-  // the statistics stream behind them, so the many walk set-ups overlap the
-  // streaming (64 requests: acceptance -6% in an interleaved A/B; 8
-  // requests: +2%, the walks' slots slow the streaming more than their few
-  // set-ups gain; with draft rows it measured no better).  The walks hold
-  // at most half of the device, so every walk workgroup is resident at once
-  // (no tickets) and the statistics keep the other half.
-  if (nstat > 0 && !q_logits && cx.B >= kWalkFirstMinBatch && cx.B <= capacity / 2 &&
-      walk.max_slices <= 0) {
-    stats_args.wfirst = 1;
-    S = walk_slices(cx.B, vocab, capacity / 2);
-  }
-  if (walk.max_slices > 0) S = walk.max_slices < S ? walk.max_slices : S;
   const int max_spins = walk.max_spins >= 0 ? walk.max_spins : kWalkMaxSpins;
-  // nstat statistics items, then B * S <= capacity walk workgroups, which
-  // take tickets (see the kernel).
+  // nstat statistics items and B * S walk workgroups: the walks after the
+  // statistics, taking tickets (see the kernel), or first in the grid.
   HeadTiles ht{};
   if (head) ht = *head;     // ht.hidden == nullptr: no LM head (every leaf draw reads its row)
-  hipLaunchKernelGGL(accept_sample_kernel, dim3(nstat + cx.B * S), dim3(kWalkThreads), 0,
-                     cx.stream, stats_args, nstat, cx.row_offsets_d, cx.B, R, S, parents, tokens,
-                     p_logits, q_logits, ld, vocab, temperature, seed, step, ws, out, max_spins, ht);
+  if (stats_args.wfirst)
+    hipLaunchKernelGGL(accept_sample_kernel<true>, dim3(nstat + cx.B * S), dim3(kWalkThreads), 0,
+                       cx.stream, stats_args, nstat, cx.row_offsets_d, cx.B, R, S, parents,
+                       tokens, p_logits, q_logits, ld, vocab, temperature, seed, step, ws, out,
+                       max_spins, ht);
+  else
+    hipLaunchKernelGGL(accept_sample_kernel<false>, dim3(nstat + cx.B * S), dim3(kWalkThreads), 0,
+                       cx.stream, stats_args, nstat, cx.row_offsets_d, cx.B, R, S, parents,
+                       tokens, p_logits, q_logits, ld, vocab, temperature, seed, step, ws, out,
+                       max_spins, ht);
   return hipGetLastError();
 }
 
