@@ -404,15 +404,20 @@ SPEC_DEVICE void sample_stats_item(const StatsArgs& a, const AcceptWs& ws, int i
   }
   load_exp_table(s_tab);
   const int which = rr >= a.R ? 1 : 0;
-  const float4* row4 = reinterpret_cast<const float4*>((which ? a.q_logits : a.p_logits) +
-                                                       (int64_t)(rr - which * a.R) * a.ld);
+  const f32x4* row4 = reinterpret_cast<const f32x4*>((which ? a.q_logits : a.p_logits) +
+                                                     (int64_t)(rr - which * a.R) * a.ld);
   const int v4 = (a.vocab + 3) >> 2;
   const int f_begin = chunk * (kStatThreads * kStatF4);
   // the whole chunk in flight: clamped (in-bounds) loads, masked to -inf
-  // (only the row's last chunk can reach past it)
+  // (only the row's last chunk can reach past it).  Non-temporal: the
+  // stream should not displace what the walks re-read between passes
+  // (acceptance -1 to -6% in an interleaved A/B).
   float4 x[kStatF4];
 #pragma unroll
-  for (int k = 0; k < kStatF4; ++k) x[k] = row4[min(f_begin + k * kStatThreads + tid, v4 - 1)];
+  for (int k = 0; k < kStatF4; ++k) {
+    const f32x4 v = __builtin_nontemporal_load(row4 + min(f_begin + k * kStatThreads + tid, v4 - 1));
+    x[k] = make_float4(v[0], v[1], v[2], v[3]);
+  }
   if ((chunk + 1) * kStatChunkLen > a.vocab) {
 #pragma unroll
     for (int k = 0; k < kStatF4; ++k) {
