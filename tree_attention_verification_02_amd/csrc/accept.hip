@@ -221,10 +221,19 @@ accept_prep_kernel(const int32_t* __restrict__ row_offsets, int B, int R,
     for (int r = tid; r < R; r += kPrepThreads)
       if (s_kids[r]) atomicAdd(&s_key[r - s_off[find_request(s_off, B, r)] + 1], 1);
     __syncthreads();
-    if (tid == 0) {                                      // exclusive prefix over the indices
-      for (int i = 1; i <= kMaxRows; ++i) s_key[i] += s_key[i - 1];
-      ws.sync[2] = m * s_key[kMaxRows];
+    // exclusive prefix over the 256 indices: s_key[i] = nodes at indices < i
+    int cnt = (tid < kMaxRows) ? s_key[tid + 1] : 0;
+    int incl = cnt;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int x = __shfl_up(incl, d, 64);
+      if (lane >= d) incl += x;
     }
+    if (lane == 63) s_wave[wave] = incl;
+    __syncthreads();
+    for (int w = 0; w < wave; ++w) incl += s_wave[w];
+    if (tid < kMaxRows) s_key[tid + 1] = incl;
+    if (tid == kMaxRows - 1) ws.sync[2] = m * incl;
     __syncthreads();
     for (int r = tid; r < R; r += kPrepThreads)
       if (s_kids[r]) {
