@@ -1348,7 +1348,10 @@ SPEC_DEVICE void node_stats(WalkShared& sh, const AcceptWs& ws, int R, int o, in
       if (!topk) lq = (q_logits + (int64_t)(o + u) * ld)[x];
     }
   }
-  if (tid < (topk ? 1 : 2) && !merged_ref_sum(ws, tid * R + o + u, sh.tab, sh.lse[tid][u]))
+  // (a leaf reaches here only with the LM head's partials, for its draw: its
+  // target row alone)
+  if (tid < ((topk || nk == 0) ? 1 : 2) &&
+      !merged_ref_sum(ws, tid * R + o + u, sh.tab, sh.lse[tid][u]))
     sh.timeout = 1;
   __syncthreads();
   if (tid < nk) {
@@ -1375,7 +1378,7 @@ struct WalkState {
 // is needed.  Coins (sh.coin): purpose 0 for the accept test of child c,
 // purpose 1 for the draw at the node where the walk stops.
 SPEC_DEVICE void walk_decide(WalkShared& sh, WalkState& st, int path_stride, bool topk,
-                             bool lazy) {
+                             bool lazy, bool leafp) {
   while (true) {
     const int u = st.u;
     const int k0 = sh.kid_start[u], k1 = sh.kid_start[u + 1];
@@ -1423,7 +1426,7 @@ SPEC_DEVICE void walk_decide(WalkShared& sh, WalkState& st, int path_stride, boo
       st.N = 1.0;
       st.pass_t = -1.0;
       sh.nrej = 0;
-      if (lazy && !sh.ready[ch] && sh.kid_start[ch + 1] > sh.kid_start[ch]) {
+      if (lazy && !sh.ready[ch] && (leafp || sh.kid_start[ch + 1] > sh.kid_start[ch])) {
         st.action = 4;                   // merge the new node's statistics first
         return;
       }
@@ -1554,7 +1557,7 @@ accept_sample_kernel(StatsArgs sa, int nstat, const int32_t* __restrict__ row_of
   } else if constexpr (lazy) {
     if (tid < n) sh.ready[tid] = 0;
     __syncthreads();
-    if (sh.kid_start[1] > sh.kid_start[0])
+    if (sa.leafp || sh.kid_start[1] > sh.kid_start[0])
       node_stats(sh, ws, R, o, 0, p_logits, q_logits, ld, vocab, invT, topk);
   }
   if (sh.bad) {
@@ -1594,7 +1597,7 @@ accept_sample_kernel(StatsArgs sa, int nstat, const int32_t* __restrict__ row_of
   int final_token = -1;
   while (true) {
     if (tid == 0)
-      walk_decide(sh, st, out.path_stride, topk, lazy);
+      walk_decide(sh, st, out.path_stride, topk, lazy, sa.leafp != 0);
     __syncthreads();
     const int action = st.action;
     if (action == 3) break;
@@ -1863,7 +1866,7 @@ hipError_t launch_accept(const LaunchCtx& cx, int R, const int32_t* parents, con
     // walks' set-ups and root decisions overlap the streaming.  They hold at
     // most half of the device, so every walk workgroup is resident at once
     // (no tickets) and the statistics keep the other half.
-    if (nstat > 0 && !head && cx.B >= kWalkFirstMinBatch && cx.B <= capacity / 2 &&
+    if (nstat > 0 && cx.B >= kWalkFirstMinBatch && cx.B <= capacity / 2 &&
         walk.max_slices <= 0) {
       stats_args.wfirst = 1;
       S = walk_slices(cx.B, vocab, capacity / 2);
