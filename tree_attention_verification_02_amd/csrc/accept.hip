@@ -1452,11 +1452,15 @@ SPEC_DEVICE void walk_decide(WalkShared& sh, WalkState& st, int path_stride, boo
   }
 }
 
-// Statistics and walk in one launch: blocks [0, nstat) are statistics items
-// (sample_stats_item), the B * S after them the walk's workgroups, which are
-// dispatched as the statistics drain and load their trees meanwhile; each
-// then polls the partials of its rows until they are published (a bounded
-// wait: a request whose partials never arrive reports a timeout).
+// Statistics and walk in one launch.  kLazy = false: blocks [0, nstat) are
+// statistics items (sample_stats_item), the B * S after them the walk's
+// workgroups, which are dispatched as the statistics drain, take tickets and
+// load their trees meanwhile; each then polls the partials of all its rows
+// until they are published.  kLazy = true (walks first): blocks [0, B * S)
+// are the walk's workgroups, all resident at once, each merging a node's
+// partials when its walk reaches the node (node_stats); the statistics items
+// follow in the order the walks need them.  Every wait is bounded: a request
+// whose partials never arrive reports a timeout.
 template <bool kLazy>
 __global__ void __launch_bounds__(kWalkThreads, 4)
 accept_sample_kernel(StatsArgs sa, int nstat, const int32_t* __restrict__ row_offsets, int B,
@@ -1476,6 +1480,8 @@ accept_sample_kernel(StatsArgs sa, int nstat, const int32_t* __restrict__ row_of
   // the lowest unfinished request then always has all its slices running
   // or next in line, so the per-request barriers make progress whenever S
   // workgroups fit on the device at once (no cooperative launch needed).
+  // With the walks first, every walk workgroup is resident from the start
+  // (B * S <= half the device), so the block id serves.
   __shared__ int s_ticket;
   if (threadIdx.x == 0)
     s_ticket = kLazy ? (int)blockIdx.x                      // every walk workgroup resident
