@@ -359,7 +359,7 @@ struct StatsArgs {
   int vocab, R, np;   // np: target rows listed (R, or 0 when the LM head made their partials)
   int nq;             // draft-row entries in the grid (R, or 0 without draft rows)
   int leafp;          // 1: target partials of leaf rows exist too (the LM head's)
-  int wfirst;         // 1: the walk workgroups come first in the grid (target rows only)
+  int wfirst;         // 1: the walk workgroups come first in the grid (one stream list)
   double invT;
 };
 
