@@ -803,7 +803,7 @@ __global__ void __launch_bounds__(W * 64, 1) attn_bf16_kernel(AttnArgs a) {
           *reinterpret_cast<uint2*>((uint16_t*)a.out + obase + d0) = pk;
         }
       }
-  } else {
+  } else if (a.out_f32) {
     const int r_in_block = g * kRowsPerWave + col;
     float* pp = a.part + (item * ROWS + r_in_block) * D;
 #pragma unroll
@@ -818,6 +818,45 @@ __global__ void __launch_bounds__(W * 64, 1) attn_bf16_kernel(AttnArgs a) {
       float* ml = a.part_ml + (item * ROWS + r_in_block) * 2;
       ml[0] = m_run;
       ml[1] = l_run;
+    }
+  } else {
+    // bf16 output: the partial is stored normalised, y = O / l in fp16 (a
+    // convex combination of V rows, |y| <= max |V|; 2^-11 relative, finer
+    // than the bf16 output), half the bytes of the fp32 form.  A row whose
+    // largest |y| reaches 2^15 is stored as y * 2^-e instead (e < 128), and
+    // e travels in the low 7 bits of its l, which is then stored negated.
+    const int r_in_block = g * kRowsPerWave + col;
+    const float inv = (l_run > 0.0f) ? 1.0f / l_run : 0.0f;
+    float mx = 0.0f;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, fabsf(acc[db][i]));
+    mx = row_pair_max(mx * inv);
+    int e = 0;
+    if (mx >= 32768.0f && mx <= 3.4e38f) {
+      int k;
+      frexpf(mx, &k);                                // mx < 2^k, k <= 128
+      e = k - 15;
+    }
+    const float sc = e ? ldexpf(inv, -e) : inv;
+    _Float16* ph = reinterpret_cast<_Float16*>(a.part) + (item * ROWS + r_in_block) * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int ai = 0; ai < 4; ++ai) {
+        const int d0 = db * 32 + half * 4 + 8 * ai;
+        const _Float16 h0 = (_Float16)(acc[db][4 * ai] * sc), h1 = (_Float16)(acc[db][4 * ai + 1] * sc);
+        const _Float16 h2 = (_Float16)(acc[db][4 * ai + 2] * sc), h3 = (_Float16)(acc[db][4 * ai + 3] * sc);
+        uint2 pk;
+        pk.x = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+        pk.y = (uint32_t)__builtin_bit_cast(uint16_t, h2) | ((uint32_t)__builtin_bit_cast(uint16_t, h3) << 16);
+        *reinterpret_cast<uint2*>(ph + d0) = pk;
+      }
+    if (half == 0) {
+      float* ml = a.part_ml + (item * ROWS + r_in_block) * 2;
+      ml[0] = m_run;
+      ml[1] = e ? -__uint_as_float((__float_as_uint(l_run) & ~127u) | (uint32_t)e) : l_run;
     }
   }
 }
@@ -842,12 +881,13 @@ struct CombineArgs {
 };
 
 // Merge split partials.  One workgroup per 32 query rows of one (request, KV
-// head, row block); each thread merges one float4 column of a row over the
-// splits in one pass with a running maximum (coalesced 512-byte rows of
-// partials; weights exp2(m_s - m)).  The grid covers only chunks that can
+// head, row block); each thread merges one 4-wide column of a row over the
+// splits in one pass with a running maximum (coalesced rows of partials:
+// fp32 O for fp32 output, normalised fp16 O / l for bf16 output; weights
+// exp2(m_s - m)).  The grid covers only chunks that can
 // hold rows (and, when the requests are listed, only units with partials),
 // so few workgroups start just to find nothing to do.
-template <int D, int W>
+template <int D, int W, bool kHalf>
 __global__ void __launch_bounds__(256) attn_combine_kernel(CombineArgs a) {
   constexpr int C4 = D / 4;                        // float4 per row
   constexpr int RPI = 256 / C4;                    // rows per pass of the block
@@ -899,7 +939,24 @@ __global__ void __launch_bounds__(256) attn_combine_kernel(CombineArgs a) {
     for (int rp = 0; rp < NP; ++rp) {
       const int64_t pr = base + min(rp * RPI + rsub, rows - 1);
       const float2 v = ml[pr];
-      const float4 pv = *reinterpret_cast<const float4*>(a.part + pr * D + c4 * 4);
+      float4 pv;
+      float lw = v.y, yscale = 1.0f;
+      if (kHalf) {
+        // normalised fp16 partial y = O / l (times 2^-e when l is stored negated)
+        const uint2 hv = *reinterpret_cast<const uint2*>(
+            reinterpret_cast<const _Float16*>(a.part) + pr * D + c4 * 4);
+        pv = make_float4((float)__builtin_bit_cast(_Float16, (uint16_t)(hv.x & 0xffffu)),
+                         (float)__builtin_bit_cast(_Float16, (uint16_t)(hv.x >> 16)),
+                         (float)__builtin_bit_cast(_Float16, (uint16_t)(hv.y & 0xffffu)),
+                         (float)__builtin_bit_cast(_Float16, (uint16_t)(hv.y >> 16)));
+        if (lw < 0.0f) {
+          lw = -lw;
+          yscale = ldexpf(1.0f, (int)(__float_as_uint(lw) & 127u));
+        }
+        yscale *= lw;
+      } else {
+        pv = *reinterpret_cast<const float4*>(a.part + pr * D + c4 * 4);
+      }
       if (v.x > mx[rp]) {                            // new maximum: rescale what is summed
         const float sc = (mx[rp] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mx[rp] - v.x);
         accv[rp].x *= sc; accv[rp].y *= sc; accv[rp].z *= sc; accv[rp].w *= sc;
@@ -907,9 +964,10 @@ __global__ void __launch_bounds__(256) attn_combine_kernel(CombineArgs a) {
         mx[rp] = v.x;
       }
       const float wgt = (v.x == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(v.x - mx[rp]);
-      l[rp] += v.y * wgt;
-      accv[rp].x += pv.x * wgt; accv[rp].y += pv.y * wgt;
-      accv[rp].z += pv.z * wgt; accv[rp].w += pv.w * wgt;
+      l[rp] += lw * wgt;
+      const float yw = yscale * wgt;                 // fp32 partials: O itself (yscale 1)
+      accv[rp].x += pv.x * yw; accv[rp].y += pv.y * yw;
+      accv[rp].z += pv.z * yw; accv[rp].w += pv.w * yw;
     }
   }
 #pragma unroll
@@ -1192,20 +1250,36 @@ hipError_t launch_attention_bf16(const LaunchCtx& cx, const AttnPlan& plan, cons
   const dim3 cgrid((unsigned)cwg);
   if (addr.d == 128 && W == kWaves) {
     hipLaunchKernelGGL((attn_bf16_kernel<128, kWaves>), grid, dim3(W * 64), 0, cx.stream, a);
-    if (plan.partial_items)
-      hipLaunchKernelGGL((attn_combine_kernel<128, kWaves>), cgrid, dim3(256), 0, cx.stream, ca);
+    if (plan.partial_items) {
+      if (out_f32)
+        hipLaunchKernelGGL((attn_combine_kernel<128, kWaves, false>), cgrid, dim3(256), 0, cx.stream, ca);
+      else
+        hipLaunchKernelGGL((attn_combine_kernel<128, kWaves, true>), cgrid, dim3(256), 0, cx.stream, ca);
+    }
   } else if (addr.d == 128) {
     hipLaunchKernelGGL((attn_bf16_kernel<128, kWideWaves>), grid, dim3(W * 64), 0, cx.stream, a);
-    if (plan.partial_items)
-      hipLaunchKernelGGL((attn_combine_kernel<128, kWideWaves>), cgrid, dim3(256), 0, cx.stream, ca);
+    if (plan.partial_items) {
+      if (out_f32)
+        hipLaunchKernelGGL((attn_combine_kernel<128, kWideWaves, false>), cgrid, dim3(256), 0, cx.stream, ca);
+      else
+        hipLaunchKernelGGL((attn_combine_kernel<128, kWideWaves, true>), cgrid, dim3(256), 0, cx.stream, ca);
+    }
   } else if (W == kWaves) {
     hipLaunchKernelGGL((attn_bf16_kernel<64, kWaves>), grid, dim3(W * 64), 0, cx.stream, a);
-    if (plan.partial_items)
-      hipLaunchKernelGGL((attn_combine_kernel<64, kWaves>), cgrid, dim3(256), 0, cx.stream, ca);
+    if (plan.partial_items) {
+      if (out_f32)
+        hipLaunchKernelGGL((attn_combine_kernel<64, kWaves, false>), cgrid, dim3(256), 0, cx.stream, ca);
+      else
+        hipLaunchKernelGGL((attn_combine_kernel<64, kWaves, true>), cgrid, dim3(256), 0, cx.stream, ca);
+    }
   } else {
     hipLaunchKernelGGL((attn_bf16_kernel<64, kWideWaves>), grid, dim3(W * 64), 0, cx.stream, a);
-    if (plan.partial_items)
-      hipLaunchKernelGGL((attn_combine_kernel<64, kWideWaves>), cgrid, dim3(256), 0, cx.stream, ca);
+    if (plan.partial_items) {
+      if (out_f32)
+        hipLaunchKernelGGL((attn_combine_kernel<64, kWideWaves, false>), cgrid, dim3(256), 0, cx.stream, ca);
+      else
+        hipLaunchKernelGGL((attn_combine_kernel<64, kWideWaves, true>), cgrid, dim3(256), 0, cx.stream, ca);
+    }
   }
   return hipGetLastError();
 }
